@@ -1,0 +1,24 @@
+"""Head-aware token-sparse decode attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in the HIP library ``libhas.so`` (C ABI in
+``include/has.h``); this package is a thin ctypes binding with the same
+names.  PyTorch tensors are used only as device buffers and for the current
+HIP stream.
+"""
+from .binding import (  # noqa: F401
+    HAS_BF16,
+    HAS_F32,
+    DecodeDims,
+    HasError,
+    aoh_label,
+    aoh_label_workspace,
+    kdom_pack,
+    kdom_row_elems,
+    last_error,
+    library_path,
+    shared_index_decode,
+    shared_index_workspace,
+    sparse_decode_step,
+    sparse_decode_workspace,
+    status_string,
+)

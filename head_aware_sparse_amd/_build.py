@@ -1,0 +1,53 @@
+"""Builds the in-tree shared libraries with hipcc for gfx950.
+
+libhas.so    the product: C ABI of include/has.h (HIP kernels + host code)
+libsynth.so  the seeded input generator (host + device fill), test/bench input
+"""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "head_aware_sparse_amd")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+COMMON = ["-O3", "-fPIC", "-shared", "-std=c++17", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+HAS_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("api.cpp", "decode.hip", "label.hip")]
+HAS_LIB = os.path.join(PKG, "libhas.so")
+SYNTH_SOURCES = [os.path.join(ROOT, "synth", "csrc", "synth.hip")]
+SYNTH_LIB = os.path.join(ROOT, "synth", "libsynth.so")
+
+
+def _run(cmd):
+    print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(ln for ln in r.stdout.splitlines() if "packed-fp32-ops" not in ln)
+    if r.returncode != 0:
+        sys.stderr.write(out + "\n")
+        raise RuntimeError(f"build failed: {cmd[-1]}")
+    if out.strip():
+        print(out)
+
+
+def build_has():
+    cmd = [HIPCC, *COMMON, "-I", os.path.join(ROOT, "include"), "-x", "hip", *HAS_SOURCES,
+           "-o", HAS_LIB + ".tmp"]
+    # api.cpp carries no device code, but compiling it as HIP keeps one toolchain.
+    _run(cmd)
+    os.replace(HAS_LIB + ".tmp", HAS_LIB)
+
+
+def build_synth():
+    _run([HIPCC, *COMMON, "-ffp-contract=off", *SYNTH_SOURCES, "-o", SYNTH_LIB + ".tmp"])
+    os.replace(SYNTH_LIB + ".tmp", SYNTH_LIB)
+
+
+def build_all():
+    build_synth()
+    build_has()
+
+
+if __name__ == "__main__":
+    build_all()

@@ -1,0 +1,218 @@
+"""ctypes binding of libhas.so: argument marshalling only.
+
+Every function takes PyTorch tensors that already live on the GPU, checks
+their dtype, shape and contiguity, and passes raw device pointers and the
+current HIP stream to the C entry point of the same name.  The library
+itself validates again and returns a status; a non-OK status raises
+HasError with the library's message.  If the library is not built the
+import of any entry point fails loudly: there is no fallback path.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libhas.so")
+_lib = None
+
+HAS_F32, HAS_BF16 = 0, 1
+HAS_ROPE_ROTATE_HALF, HAS_ROPE_INTERLEAVED = 0, 1
+_FIELDS = ["n_layers", "batch", "n_q_heads", "n_kv_heads", "d_head", "ctx_len", "n_fac", "n_sink",
+           "window", "n_dom", "kv_dtype", "rope_layout"]
+
+
+class DecodeDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in _FIELDS]
+
+    def __repr__(self):
+        return "DecodeDims(" + ", ".join(f"{n}={getattr(self, n)}" for n in _FIELDS) + ")"
+
+
+class HasError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        DP = ctypes.POINTER(DecodeDims)
+        L.has_status_string.argtypes = [I]
+        L.has_status_string.restype = ctypes.c_char_p
+        L.has_last_error.argtypes = []
+        L.has_last_error.restype = ctypes.c_char_p
+        L.kdom_row_elems.argtypes = [DP]
+        L.kdom_row_elems.restype = I
+        L.kdom_pack.argtypes = [DP, P, P, P, P]
+        L.kdom_pack.restype = I
+        L.sparse_decode_workspace.argtypes = [DP]
+        L.sparse_decode_workspace.restype = S
+        L.sparse_decode_step.argtypes = [DP, P, P, P, P, P, P, P, P, P, S, P]
+        L.sparse_decode_step.restype = I
+        L.shared_index_workspace.argtypes = [DP]
+        L.shared_index_workspace.restype = S
+        L.shared_index_decode.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.shared_index_decode.restype = I
+        L.aoh_label_workspace.argtypes = [I, I, I, I, I]
+        L.aoh_label_workspace.restype = S
+        L.aoh_label.argtypes = [I, I, I, I, I, I, P, P, I, ctypes.c_float, P, P, P, P, S, P]
+        L.aoh_label.restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(s):
+    return lib().has_status_string(int(s)).decode()
+
+
+def last_error():
+    return lib().has_last_error().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise HasError(status, last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _kv_torch_dtype(dims):
+    import torch
+    return torch.bfloat16 if dims.kv_dtype == HAS_BF16 else torch.float32
+
+
+def kdom_row_elems(dims):
+    r = lib().kdom_row_elems(ctypes.byref(dims))
+    if r < 0:
+        raise HasError(1, last_error())
+    return r
+
+
+def sparse_decode_workspace(dims):
+    return int(lib().sparse_decode_workspace(ctypes.byref(dims)))
+
+
+def shared_index_workspace(dims):
+    return int(lib().shared_index_workspace(ctypes.byref(dims)))
+
+
+def aoh_label_workspace(n_layers, n_q_heads, n_kv_heads, d_model, d_head):
+    return int(lib().aoh_label_workspace(n_layers, n_q_heads, n_kv_heads, d_model, d_head))
+
+
+def _workspace(nbytes, ws, like):
+    import torch
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+    _dev(ws, "ws", torch.uint8)
+    return ws
+
+
+def kdom_pack(dims, k_cache, i_dom, k_dom, stream=None):
+    import torch
+    L, B, Hkv, T, d = dims.n_layers, dims.batch, dims.n_kv_heads, dims.ctx_len, dims.d_head
+    dt = _kv_torch_dtype(dims)
+    _dev(k_cache, "k_cache", dt, (L, B, Hkv, T, d))
+    _dev(i_dom, "i_dom", torch.int32, (L, Hkv, dims.n_dom))
+    _dev(k_dom, "k_dom", dt, (L, B, Hkv, T, kdom_row_elems(dims)))
+    _check(lib().kdom_pack(ctypes.byref(dims), _ptr(k_cache), _ptr(i_dom), _ptr(k_dom), _stream(stream)))
+
+
+def sparse_decode_step(dims, q, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out=None, ws=None,
+                       stream=None):
+    import torch
+    L, B, Hq, Hkv, T, d = (dims.n_layers, dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.ctx_len,
+                           dims.d_head)
+    dt = _kv_torch_dtype(dims)
+    _dev(q, "q", dt, (L, B, Hq, d))
+    _dev(k_cache, "k_cache", dt, (L, B, Hkv, T, d))
+    _dev(v_cache, "v_cache", dt, (L, B, Hkv, T, d))
+    _dev(k_dom, "k_dom", dt, (L, B, Hkv, T, kdom_row_elems(dims)))
+    _dev(i_dom, "i_dom", torch.int32, (L, Hkv, dims.n_dom))
+    _dev(labels, "labels", torch.uint8, (L, Hkv))
+    _dev(out, "out", torch.float32, (L, B, Hq, d))
+    _dev(idx_out, "idx_out", torch.int32, (L, B, Hkv, dims.n_fac))
+    nbytes = sparse_decode_workspace(dims)
+    ws = _workspace(nbytes, ws, q)
+    _check(lib().sparse_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_dom),
+                                    _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+    return ws
+
+
+def shared_index_decode(dims, q, k_cache, v_cache, k_dom, i_dom, out, q_index=None, labels=None,
+                        idx_out=None, ws=None, stream=None):
+    import torch
+    N, B, Hq, Hkv, T, d = (dims.n_layers, dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.ctx_len,
+                           dims.d_head)
+    dt = _kv_torch_dtype(dims)
+    _dev(q, "q", dt, (N, B, Hq, d))
+    _dev(q_index, "q_index", dt, (B, Hq, d))
+    _dev(k_cache, "k_cache", dt, (B, Hkv, T, d))
+    _dev(v_cache, "v_cache", dt, (B, Hkv, T, d))
+    _dev(k_dom, "k_dom", dt, (B, Hkv, T, kdom_row_elems(dims)))
+    _dev(i_dom, "i_dom", torch.int32, (Hkv, dims.n_dom))
+    _dev(labels, "labels", torch.uint8, (N, Hkv))
+    _dev(out, "out", torch.float32, (N, B, Hq, d))
+    _dev(idx_out, "idx_out", torch.int32, (B, Hkv, dims.n_fac))
+    nbytes = shared_index_workspace(dims)
+    ws = _workspace(nbytes, ws, q)
+    _check(lib().shared_index_decode(ctypes.byref(dims), _ptr(q), _ptr(q_index), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(k_dom), _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _ptr(ws),
+                                     ws.numel(), _stream(stream)))
+    return ws
+
+
+def aoh_label(w_q, w_k, n_q_heads, n_kv_heads, d_head, labels, n_retrieval=-1, er_threshold=0.0,
+              er_head=None, er_group=None, ws=None, stream=None):
+    import torch
+    if w_q.dtype == torch.bfloat16:
+        wdt = HAS_BF16
+    elif w_q.dtype == torch.float32:
+        wdt = HAS_F32
+    else:
+        raise ValueError("weights must be bfloat16 or float32")
+    L, rows, d_model = w_q.shape
+    _dev(w_q, "w_q", w_q.dtype, (L, n_q_heads * d_head, d_model))
+    _dev(w_k, "w_k", w_q.dtype, (L, n_kv_heads * d_head, d_model))
+    _dev(labels, "labels", torch.uint8, (L, n_kv_heads))
+    _dev(er_head, "er_head", torch.float32, (L, n_q_heads))
+    _dev(er_group, "er_group", torch.float32, (L, n_kv_heads))
+    nbytes = aoh_label_workspace(L, n_q_heads, n_kv_heads, d_model, d_head)
+    ws = _workspace(nbytes, ws, w_q)
+    _check(lib().aoh_label(L, n_q_heads, n_kv_heads, d_model, d_head, wdt, _ptr(w_q), _ptr(w_k), int(n_retrieval),
+                           float(er_threshold), _ptr(er_head), _ptr(er_group), _ptr(labels), _ptr(ws), ws.numel(),
+                           _stream(stream)))
+    return ws

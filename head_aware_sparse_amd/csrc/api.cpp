@@ -1,0 +1,321 @@
+// C ABI of libhas.so: host-side validation, workspace carving and launch
+// sequencing.  Every check runs before the first HIP call, so an invalid
+// argument returns without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/has.h"
+#include "internal.h"
+#include "label.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+has_status fail(has_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+has_status ok() {
+  g_err[0] = '\0';
+  return HAS_OK;
+}
+
+has_status hip_fail(hipError_t e, const char* what) {
+  return fail(HAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int pow2_floor(long long v) {
+  int p = 1;
+  while ((long long)p * 2 <= v && p < (1 << 30)) p *= 2;
+  return p;
+}
+
+int clampi(long long v, int lo, int hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); }
+
+int esize(int dt) { return dt == HAS_BF16 ? 2 : 4; }
+
+int kdom_elems(int n_dom, int dt) {
+  const int bytes = 2 * n_dom * esize(dt);
+  int vecs = 1;
+  while (vecs * 16 < bytes) vecs *= 2;
+  return vecs * 16 / esize(dt);
+}
+
+// Validates a decode shape.  clsa selects the shared-index limits.
+has_status check_dims(const has_decode_dims* d, bool clsa) {
+  if (!d) return fail(HAS_ERR_INVALID_ARG, "dims is NULL");
+  if (d->n_layers < 1 || d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(HAS_ERR_INVALID_ARG, "n_layers, batch, n_q_heads and n_kv_heads must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(HAS_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", d->n_q_heads,
+                d->n_kv_heads);
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(HAS_ERR_UNSUPPORTED, "group size %d not in {1,2,4,8}", G);
+  if (d->d_head < 2 || (d->d_head & 1)) return fail(HAS_ERR_INVALID_ARG, "d_head must be even and >= 2");
+  if (d->d_head != 64 && d->d_head != 128) return fail(HAS_ERR_UNSUPPORTED, "d_head %d not in {64,128}", d->d_head);
+  if (d->ctx_len < 1) return fail(HAS_ERR_INVALID_ARG, "ctx_len must be >= 1");
+  if (d->ctx_len > has::kMaxTipChunks * 4096)
+    return fail(HAS_ERR_UNSUPPORTED, "ctx_len %d above %d", d->ctx_len, has::kMaxTipChunks * 4096);
+  if (d->n_fac < 1 || d->n_fac > d->ctx_len)
+    return fail(HAS_ERR_INVALID_ARG, "n_fac %d outside [1, ctx_len=%d]", d->n_fac, d->ctx_len);
+  if (d->n_sink < 0 || d->window < 0) return fail(HAS_ERR_INVALID_ARG, "n_sink and window must be >= 0");
+  if ((long long)d->n_sink + d->window < 1) return fail(HAS_ERR_INVALID_ARG, "n_sink + window must be >= 1");
+  if (d->n_dom < 1 || d->n_dom > d->d_head / 2)
+    return fail(HAS_ERR_INVALID_ARG, "n_dom %d outside [1, d_head/2]", d->n_dom);
+  if (d->kv_dtype != HAS_F32 && d->kv_dtype != HAS_BF16) return fail(HAS_ERR_INVALID_ARG, "bad kv_dtype");
+  if (d->rope_layout != HAS_ROPE_ROTATE_HALF && d->rope_layout != HAS_ROPE_INTERLEAVED)
+    return fail(HAS_ERR_INVALID_ARG, "bad rope_layout");
+  if ((long long)d->n_layers * d->n_kv_heads > has::kMaxPairs)
+    return fail(HAS_ERR_UNSUPPORTED, "n_layers * n_kv_heads above %d", has::kMaxPairs);
+  (void)clsa;
+  return HAS_OK;
+}
+
+struct Layout {
+  has::Geo g;
+  size_t off_plan, off_hist, off_info, off_cand, off_ngt, off_off, off_thr, off_scores, off_idx, off_part;
+  size_t bytes;
+};
+
+Layout make_layout(const has_decode_dims* d, bool clsa) {
+  Layout L{};
+  has::Geo& g = L.g;
+  g.Lq = d->n_layers;
+  g.Lkv = clsa ? 1 : d->n_layers;
+  g.B = d->batch;
+  g.Hq = d->n_q_heads;
+  g.Hkv = d->n_kv_heads;
+  g.G = g.Hq / g.Hkv;
+  g.d = d->d_head;
+  g.T = d->ctx_len;
+  g.n_fac = d->n_fac;
+  g.n_sink = d->n_sink;
+  g.window = d->window;
+  g.n_dom = d->n_dom;
+  g.R = kdom_elems(d->n_dom, d->kv_dtype);
+  g.bf16 = d->kv_dtype == HAS_BF16;
+  g.clsa = clsa ? 1 : 0;
+  g.interleaved = d->rope_layout == HAS_ROPE_INTERLEAVED;
+  const long long n_idx = (long long)(clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
+  const long long n_att = (long long)g.Lq * g.Hkv * g.B;
+  // Score chunks: aim for ~1024 units over the worst-case item count.
+  g.ct = clampi(pow2_floor((long long)g.T * n_idx / 1024), 256, 4096);
+  while ((g.T + g.ct - 1) / g.ct > has::kMaxTipChunks && g.ct < 4096) g.ct *= 2;
+  g.nch_t = (g.T + g.ct - 1) / g.ct;
+  g.cf = clampi(pow2_floor((long long)g.n_fac * n_att / 2048), 128, has::kMaxChunkRows);
+  g.nch_f = (g.n_fac + g.cf - 1) / g.cf;
+  g.s_end = g.n_sink < g.T ? g.n_sink : g.T;
+  g.w_start = (g.T - g.window) > g.s_end ? (g.T - g.window) : g.s_end;
+  g.n_srows = g.s_end + (g.T - g.w_start);
+  g.cs = clampi(pow2_floor((long long)g.n_srows * n_att / 2048), 128, has::kMaxChunkRows);
+  g.nch_s = (g.n_srows + g.cs - 1) / g.cs;
+  g.nparts = g.nch_f > g.nch_s ? g.nch_f : g.nch_s;
+  g.cand_cap = g.T < has::kCandLds ? g.T : has::kCandLds;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.off_plan = take(sizeof(int) * (4 + 3 * has::kMaxPairs));
+  L.off_hist = take((size_t)n_idx * has::kHistBins * 4);
+  L.off_info = take((size_t)n_idx * 16);
+  L.off_cand = take((size_t)n_idx * g.cand_cap * 8);
+  L.off_ngt = take((size_t)n_idx * g.nch_t * 4);
+  L.off_off = take((size_t)n_idx * g.nch_t * 4);
+  L.off_thr = take((size_t)n_idx * 8);
+  L.off_scores = take((size_t)n_idx * g.T * 4);
+  L.off_idx = take((size_t)n_idx * g.n_fac * 4);
+  L.off_part = take((size_t)n_att * g.nparts * g.G * (g.d + 4) * 4);
+  L.bytes = o;
+  return L;
+}
+
+void carve(Layout& L, void* ws) {
+  char* b = (char*)ws;
+  has::Geo& g = L.g;
+  g.plan = (int*)(b + L.off_plan);
+  g.hist = (uint32_t*)(b + L.off_hist);
+  g.info = (uint32_t*)(b + L.off_info);
+  g.cand = (uint2*)(b + L.off_cand);
+  g.ngt = (uint32_t*)(b + L.off_ngt);
+  g.off = (uint32_t*)(b + L.off_off);
+  g.thr = (uint2*)(b + L.off_thr);
+  g.scores = (float*)(b + L.off_scores);
+  g.idx = (int32_t*)(b + L.off_idx);
+  g.part = (float*)(b + L.off_part);
+}
+
+has_status persistent_grid(int& grid) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  grid = cus * 8;
+  return HAS_OK;
+}
+
+#define REQUIRE_PTR(p, name)                                                              \
+  do {                                                                                    \
+    if (!(p)) return fail(HAS_ERR_INVALID_ARG, "%s is NULL", name);                       \
+    if (!aligned16(p)) return fail(HAS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define OPTIONAL_PTR(p, name)                                                             \
+  do {                                                                                    \
+    if ((p) && !aligned16(p)) return fail(HAS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, const void* q_index,
+                      const void* k_cache, const void* v_cache, const void* k_dom, const int32_t* i_dom,
+                      const uint8_t* labels, float* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  has_status s = check_dims(dims, clsa);
+  if (s != HAS_OK) return s;
+  REQUIRE_PTR(q, "q");
+  OPTIONAL_PTR(q_index, "q_index");
+  REQUIRE_PTR(k_cache, "k_cache");
+  REQUIRE_PTR(v_cache, "v_cache");
+  REQUIRE_PTR(k_dom, "k_dom");
+  REQUIRE_PTR(i_dom, "i_dom");
+  if (!clsa) REQUIRE_PTR(labels, "labels");
+  OPTIONAL_PTR(labels, "labels");
+  REQUIRE_PTR(out, "out");
+  OPTIONAL_PTR(idx_out, "idx_out");
+  Layout L = make_layout(dims, clsa);
+  if (!ws) return fail(HAS_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned16(ws)) return fail(HAS_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  if (ws_bytes < L.bytes) return fail(HAS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, L.bytes);
+  carve(L, ws);
+  has::Geo& g = L.g;
+  g.q = q;
+  g.q_index = q_index;
+  g.k = k_cache;
+  g.v = v_cache;
+  g.kdom = k_dom;
+  g.i_dom = i_dom;
+  g.labels = labels;
+  g.out = out;
+  g.idx_out = idx_out;
+  s = persistent_grid(g.grid);
+  if (s != HAS_OK) return s;
+  hipError_t e = has::launch_decode(g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, clsa ? "shared_index_decode launch" : "sparse_decode_step launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* has_status_string(has_status s) {
+  switch (s) {
+    case HAS_OK: return "HAS_OK";
+    case HAS_ERR_INVALID_ARG: return "HAS_ERR_INVALID_ARG";
+    case HAS_ERR_UNSUPPORTED: return "HAS_ERR_UNSUPPORTED";
+    case HAS_ERR_WORKSPACE: return "HAS_ERR_WORKSPACE";
+    case HAS_ERR_HIP: return "HAS_ERR_HIP";
+    default: return "HAS_ERR_UNKNOWN";
+  }
+}
+
+const char* has_last_error(void) { return g_err; }
+
+int kdom_row_elems(const has_decode_dims* dims) {
+  if (check_dims(dims, false) != HAS_OK) return -1;
+  return kdom_elems(dims->n_dom, dims->kv_dtype);
+}
+
+has_status kdom_pack(const has_decode_dims* dims, const void* k_cache, const int32_t* i_dom, void* k_dom,
+                     void* stream) {
+  has_status s = check_dims(dims, false);
+  if (s != HAS_OK) return s;
+  REQUIRE_PTR(k_cache, "k_cache");
+  REQUIRE_PTR(i_dom, "i_dom");
+  REQUIRE_PTR(k_dom, "k_dom");
+  Layout L = make_layout(dims, false);
+  L.g.k = k_cache;
+  L.g.i_dom = i_dom;
+  hipError_t e = has::launch_kdom_pack(L.g, k_dom, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kdom_pack launch");
+  return ok();
+}
+
+size_t sparse_decode_workspace(const has_decode_dims* dims) {
+  if (check_dims(dims, false) != HAS_OK) return 0;
+  return make_layout(dims, false).bytes;
+}
+
+has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const void* k_cache,
+                              const void* v_cache, const void* k_dom, const int32_t* i_dom,
+                              const uint8_t* labels, float* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return run_decode(dims, false, q, nullptr, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out, ws,
+                    ws_bytes, stream);
+}
+
+size_t shared_index_workspace(const has_decode_dims* dims) {
+  if (check_dims(dims, true) != HAS_OK) return 0;
+  return make_layout(dims, true).bytes;
+}
+
+has_status shared_index_decode(const has_decode_dims* dims, const void* q, const void* q_index,
+                               const void* k_cache, const void* v_cache, const void* k_dom, const int32_t* i_dom,
+                               const uint8_t* labels, float* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return run_decode(dims, true, q, q_index, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out, ws, ws_bytes,
+                    stream);
+}
+
+size_t aoh_label_workspace(int n_layers, int n_q_heads, int n_kv_heads, int d_model, int d_head) {
+  return has::label_workspace_bytes(n_layers, n_q_heads, n_kv_heads, d_model, d_head);
+}
+
+has_status aoh_label(int n_layers, int n_q_heads, int n_kv_heads, int d_model, int d_head, has_dtype wdt,
+                     const void* w_q, const void* w_k, int n_retrieval, float er_threshold, float* er_head,
+                     float* er_group, uint8_t* labels, void* ws, size_t ws_bytes, void* stream) {
+  if (n_layers < 1 || n_q_heads < 1 || n_kv_heads < 1 || d_model < 1 || d_head < 1)
+    return fail(HAS_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (n_q_heads % n_kv_heads)
+    return fail(HAS_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", n_q_heads, n_kv_heads);
+  if (wdt != HAS_F32 && wdt != HAS_BF16) return fail(HAS_ERR_INVALID_ARG, "bad wdt");
+  if (d_head != 64 && d_head != 128) return fail(HAS_ERR_UNSUPPORTED, "d_head %d not in {64,128}", d_head);
+  if (d_model < d_head || d_model % 64)
+    return fail(HAS_ERR_UNSUPPORTED, "d_model %d must be a multiple of 64 and >= d_head", d_model);
+  if ((long long)n_layers * n_kv_heads > has::kMaxPairs || (long long)n_layers * n_q_heads > 65535)
+    return fail(HAS_ERR_UNSUPPORTED, "too many heads");
+  if (n_retrieval > n_layers * n_kv_heads)
+    return fail(HAS_ERR_INVALID_ARG, "n_retrieval %d above n_layers*n_kv_heads", n_retrieval);
+  if (n_retrieval < 0 && !(er_threshold == er_threshold))
+    return fail(HAS_ERR_INVALID_ARG, "er_threshold is NaN");
+  REQUIRE_PTR(w_q, "w_q");
+  REQUIRE_PTR(w_k, "w_k");
+  OPTIONAL_PTR(er_head, "er_head");
+  OPTIONAL_PTR(er_group, "er_group");
+  REQUIRE_PTR(labels, "labels");
+  const size_t need = has::label_workspace_bytes(n_layers, n_q_heads, n_kv_heads, d_model, d_head);
+  if (!ws) return fail(HAS_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned16(ws)) return fail(HAS_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  if (ws_bytes < need) return fail(HAS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, need);
+  has::LabelArgs a{n_layers, n_q_heads, n_kv_heads, d_model, d_head, wdt == HAS_BF16, w_q, w_k,
+                   n_retrieval, er_threshold, er_head, er_group, labels, ws};
+  hipError_t e = has::launch_label(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "aoh_label launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,785 @@
+// Decode-step kernels for gfx950: TIP scoring over the dominant-chunk key
+// copy, exact radix top-N_fac selection, and split-K attention over gathered
+// (retrieval) or contiguous sink+window (streaming) rows.
+//
+// Method: "FASA: Frequency-aware Sparse Attention" §2.B (TIP, then FAC over
+// the selected tokens at their original positions), §2.C (FASA-C: the cache
+// stays in device memory and only a sparse subset of it is read);
+// "Resumen Técnico: Autonomía de Cabezales (AoH)" §4 (streaming heads: sink
+// + recent window); the CLSA article, "Cómo funciona CLSA" (one index reused
+// by every layer sharing the cache).
+//
+// Launch sequence (all on the caller's stream, no host synchronisation):
+//   plan      labels -> work lists; clears histograms and counters
+//   tip       scores s_t (fp32) + per-item histogram of the top 11 key bits
+//   select_a  per chunk: count above the threshold bin, collect candidates
+//   select_b  per item: exact threshold (key*, token*) by radix refinement
+//   select_c  per chunk: ordered compaction -> ascending token indices
+//   attn      per (item, chunk of rows): scores, softmax partial, P.V
+//   merge     log-sum-exp merge of the chunk partials -> out
+// Work is split into units (item x chunk) processed by a persistent grid;
+// unit counts depend on the labels and are read from device memory.
+#include "internal.h"
+
+namespace has {
+namespace {
+
+constexpr int NT = 256;  // threads per workgroup for every kernel here
+constexpr int NWAVE = NT / 64;
+
+// ------------------------------------------------------------------ helpers
+// Order-preserving map of an fp32 score to uint32 (larger key = larger
+// score); -0 is folded onto +0 so equal scores have equal keys.
+__device__ __forceinline__ uint32_t f2key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N consecutive lanes; every lane of the group
+// receives the total.  quad_perm swaps, then half-row and row mirrors.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ int mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Exclusive prefix over the workgroup (NT threads) and the total.
+__device__ int block_excl_scan(int v, int* s_w, int& total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < NWAVE; ++w) {
+    const int t = s_w[w];
+    base += (w < wave) ? t : 0;
+    tot += t;
+  }
+  total = tot;
+  return base + x - v;
+}
+
+// 16-byte vectors of the cache element type.
+template <typename E>
+struct Vec;
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void cvt(const uint4& r, float* o) {
+    o[0] = __uint_as_float(r.x); o[1] = __uint_as_float(r.y);
+    o[2] = __uint_as_float(r.z); o[3] = __uint_as_float(r.w);
+  }
+  __device__ __forceinline__ static float one(const float* p, size_t i) { return p[i]; }
+};
+template <>
+struct Vec<uint16_t> {  // bf16 bits
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void cvt(const uint4& r, float* o) {
+    o[0] = __uint_as_float(r.x << 16); o[1] = __uint_as_float(r.x & 0xFFFF0000u);
+    o[2] = __uint_as_float(r.y << 16); o[3] = __uint_as_float(r.y & 0xFFFF0000u);
+    o[4] = __uint_as_float(r.z << 16); o[5] = __uint_as_float(r.z & 0xFFFF0000u);
+    o[6] = __uint_as_float(r.w << 16); o[7] = __uint_as_float(r.w & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ static float one(const uint16_t* p, size_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ int label_at(const Geo& g, int pair) {
+  return g.labels ? (g.labels[pair] != 0) : 1;
+}
+
+__device__ __forceinline__ const int* idx_pairs(const Geo& g) { return g.plan + 4; }
+__device__ __forceinline__ const int* att_ret_pairs(const Geo& g) { return g.plan + 4 + kMaxPairs; }
+__device__ __forceinline__ const int* att_str_pairs(const Geo& g) { return g.plan + 4 + 2 * kMaxPairs; }
+
+// Finds, over s_hist[0..nbins) read from the top bin down, the bin where the
+// running count first reaches `need` (1 <= need <= total).  Returns the bin
+// and the count strictly above it, identical in every thread.
+__device__ void find_bin_top(const uint32_t* s_hist, int nbins, uint32_t need, int* s_w,
+                             uint32_t* s_res, int& bin, uint32_t& above) {
+  const int per = nbins / NT;  // nbins is a multiple of NT
+  const int tid = threadIdx.x;
+  const int hi = nbins - tid * per;  // this thread owns bins [hi - per, hi)
+  uint32_t seg = 0;
+  for (int i = 1; i <= per; ++i) seg += s_hist[hi - i];
+  int total;
+  const uint32_t before = (uint32_t)block_excl_scan((int)seg, s_w, total);
+  if (before < need && need <= before + seg) {
+    uint32_t run = before;
+    for (int i = 1; i <= per; ++i) {
+      const uint32_t c = s_hist[hi - i];
+      if (run + c >= need) {
+        s_res[0] = (uint32_t)(hi - i);
+        s_res[1] = run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  bin = (int)s_res[0];
+  above = s_res[1];
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ plan
+__global__ __launch_bounds__(NT) void plan_kernel(Geo g) {
+  __shared__ int s_w[NWAVE];
+  const int P = g.Lq * g.Hkv;
+  const int tid = threadIdx.x;
+  const int per = (P + NT - 1) / NT;
+  const int p0 = min(P, tid * per), p1 = min(P, p0 + per);
+  int cnt = 0;
+  for (int p = p0; p < p1; ++p) cnt += label_at(g, p);
+  int n_ret;
+  const int excl = block_excl_scan(cnt, s_w, n_ret);
+  const int n_idx_pairs = g.clsa ? g.Hkv : n_ret;
+  if (blockIdx.x == 0) {
+    int* lists = g.plan + 4;
+    int r = excl, s = p0 - excl;
+    for (int p = p0; p < p1; ++p) {
+      if (label_at(g, p)) {
+        if (!g.clsa) lists[r] = p;
+        lists[kMaxPairs + r++] = p;
+      } else {
+        lists[2 * kMaxPairs + s++] = p;
+      }
+    }
+    if (g.clsa)
+      for (int gi = tid; gi < g.Hkv; gi += NT) lists[gi] = gi;
+    if (tid == 0) {
+      g.plan[0] = n_idx_pairs;
+      g.plan[1] = n_ret;
+      g.plan[2] = P - n_ret;
+      g.plan[3] = 0;
+    }
+  }
+  // Clear the histograms and counters of every index item.
+  const size_t n_items = (size_t)n_idx_pairs * g.B;
+  const size_t gtid = (size_t)blockIdx.x * NT + tid, gstride = (size_t)gridDim.x * NT;
+  uint4* h4 = reinterpret_cast<uint4*>(g.hist);
+  const size_t nh4 = n_items * kHistBins / 4;
+  for (size_t i = gtid; i < nh4; i += gstride) h4[i] = make_uint4(0, 0, 0, 0);
+  uint4* i4 = reinterpret_cast<uint4*>(g.info);
+  for (size_t i = gtid; i < n_items; i += gstride) i4[i] = make_uint4(0, 0, 0, 0);
+  // Streaming groups report -1 indices.
+  if (g.idx_out && !g.clsa) {
+    const size_t tot = (size_t)g.Lq * g.B * g.Hkv * g.n_fac;
+    for (size_t i = gtid; i < tot; i += gstride) {
+      const size_t item = i / (size_t)g.n_fac;
+      const int gi = (int)(item % g.Hkv);
+      const int l = (int)(item / ((size_t)g.Hkv * g.B));
+      if (!label_at(g, l * g.Hkv + gi)) g.idx_out[i] = -1;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ TIP
+// One unit = (index item, chunk of ct tokens).  A wave scores 64 tokens per
+// step: lane L loads 16 bytes of row (L / V) of each of V consecutive
+// 64/V-token slabs, the V lanes of a row reduce their partial dot products,
+// and lane L keeps the score of token (L % V) * 64/V + L / V, so each wave
+// writes 64 consecutive scores.
+template <typename E, int V>
+__global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
+  constexpr int EPV = Vec<E>::N;
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ float s_q[V * EPV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_units = plan_idx_pairs(g.plan) * g.B * g.nch_t;
+  for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0;
+  const int R = V * EPV;
+  const int hd = g.d / 2;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int item = u / g.nch_t, ch = u - item * g.nch_t;
+    const int pidx = item / g.B, b = item - pidx * g.B;
+    const int pair = idx_pairs(g)[pidx];
+    const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
+    const E* qg;
+    if (g.clsa)
+      qg = (const E*)(g.q_index ? g.q_index : g.q) + ((size_t)b * g.Hq + gi * g.G) * g.d;
+    else
+      qg = (const E*)g.q + (((size_t)l * g.B + b) * g.Hq + gi * g.G) * g.d;
+    const int32_t* dom = g.i_dom + (size_t)pair * g.n_dom;
+    __syncthreads();
+    for (int c = tid; c < R; c += NT) {
+      float v = 0.f;
+      if (c < 2 * g.n_dom) {
+        const int f = dom[c >> 1], cc = c & 1;
+        const int chn = g.interleaved ? 2 * f + cc : f + cc * hd;
+        float s = 0.f;
+        for (int h = 0; h < g.G; ++h) s += Vec<E>::one(qg, (size_t)h * g.d + chn);
+        v = s / (float)g.G;
+      }
+      s_q[c] = v;
+    }
+    __syncthreads();
+    float qr[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
+    const size_t slice = ((size_t)l * g.B + b) * g.Hkv + gi;
+    const E* kd = (const E*)g.kdom + slice * (size_t)g.T * R;
+    float* sc = g.scores + (size_t)item * g.T;
+    const int t0 = ch * g.ct, t1 = min(g.T, t0 + g.ct);
+    for (int base = t0 + wave * 64; base < t1; base += NT) {
+      uint4 raw[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int tok = base + i * (64 / V) + lane / V;
+        raw[i] = tok < t1 ? ld16(kd + (size_t)tok * R + (lane % V) * EPV) : make_uint4(0, 0, 0, 0);
+      }
+      float mine = 0.f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        float kv[EPV];
+        Vec<E>::cvt(raw[i], kv);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) s += qr[e] * kv[e];
+        s = group_sum<V>(s);
+        if ((lane % V) == i) mine = s;
+      }
+      const int tok = base + (lane % V) * (64 / V) + lane / V;
+      if (tok < t1) {
+        sc[tok] = mine;
+        atomicAdd(&s_hist[f2key(mine) >> 21], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t* gh = g.hist + (size_t)item * kHistBins;
+    for (int i = tid; i < kHistBins; i += NT) {
+      const uint32_t c = s_hist[i];
+      if (c) {
+        atomicAdd(&gh[i], c);
+        s_hist[i] = 0;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ select
+// select_a: threshold bin b1 of the item (from its histogram), tokens above
+// it counted per chunk, tokens inside it appended to the candidate list.
+__global__ __launch_bounds__(NT) void select_a_kernel(Geo g) {
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint2 s_cand[4096];
+  __shared__ int s_w[NWAVE];
+  __shared__ uint32_t s_res[2];
+  __shared__ int s_n;
+  __shared__ uint32_t s_base;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n_units = plan_idx_pairs(g.plan) * g.B * g.nch_t;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int item = u / g.nch_t, ch = u - item * g.nch_t;
+    __syncthreads();
+    const uint32_t* gh = g.hist + (size_t)item * kHistBins;
+    for (int i = tid; i < kHistBins; i += NT) s_hist[i] = gh[i];
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    int b1;
+    uint32_t above1;
+    find_bin_top(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, b1, above1);
+    if (ch == 0 && tid == 0) {
+      g.info[(size_t)item * 4 + 0] = (uint32_t)b1;
+      g.info[(size_t)item * 4 + 1] = above1;
+    }
+    const float* sc = g.scores + (size_t)item * g.T;
+    const int t0 = ch * g.ct, t1 = min(g.T, t0 + g.ct);
+    int ngt = 0;
+    for (int base = t0; base < t1; base += NT) {
+      const int tok = base + tid;
+      const bool valid = tok < t1;
+      const uint32_t key = valid ? f2key(sc[tok]) : 0u;
+      const int bin = (int)(key >> 21);
+      ngt += (valid && bin > b1) ? 1 : 0;
+      const bool eq = valid && bin == b1;
+      const uint64_t m = __ballot(eq);
+      if (m) {
+        int wbase = 0;
+        if (lane == 0) wbase = atomicAdd(&s_n, __popcll(m));
+        wbase = __shfl(wbase, 0);
+        if (eq) s_cand[wbase + mbcnt(m)] = make_uint2(key, (uint32_t)tok);
+      }
+    }
+    int tot;
+    block_excl_scan(ngt, s_w, tot);
+    __syncthreads();
+    const int n = s_n;
+    if (tid == 0) {
+      s_base = atomicAdd(&g.info[(size_t)item * 4 + 2], (uint32_t)n);
+      g.ngt[(size_t)item * g.nch_t + ch] = (uint32_t)tot;
+    }
+    __syncthreads();
+    const uint32_t cbase = s_base;
+    uint2* cd = g.cand + (size_t)item * g.cand_cap;
+    for (int i = tid; i < n; i += NT)
+      if (cbase + (uint32_t)i < (uint32_t)g.cand_cap) cd[cbase + i] = s_cand[i];
+  }
+}
+
+// Candidates of one item: from LDS when they fit, else re-derived from the
+// item's scores (every token whose first digit is b1).
+struct CandSource {
+  const uint2* lds;
+  int n;
+  const float* sc;
+  int T;
+  uint32_t b1;
+  template <class F>
+  __device__ __forceinline__ void for_each(F f) const {
+    if (lds) {
+      for (int i = threadIdx.x; i < n; i += NT) f(lds[i].x, lds[i].y);
+    } else {
+      for (int t = threadIdx.x; t < T; t += NT) {
+        const uint32_t key = f2key(sc[t]);
+        if ((key >> 21) == b1) f(key, (uint32_t)t);
+      }
+    }
+  }
+};
+
+template <class Pred, class Dig>
+__device__ void histogram(const CandSource& src, uint32_t* s_hist, int nbins, Pred pred, Dig dig) {
+  for (int i = threadIdx.x; i < nbins; i += NT) s_hist[i] = 0;
+  __syncthreads();
+  src.for_each([&](uint32_t key, uint32_t tok) {
+    if (pred(key, tok)) atomicAdd(&s_hist[dig(key, tok)], 1u);
+  });
+  __syncthreads();
+}
+
+// select_b: exact threshold.  Ordering is (score desc, token asc); the
+// n_fac-th element (key*, token*) is found digit by digit: key bits 20..10
+// and 9..0 among the candidates, then token bits 29..20, 19..10, 9..0 among
+// candidates equal to key* (ascending).  Then per-chunk output offsets.
+__global__ __launch_bounds__(NT) void select_b_kernel(Geo g) {
+  __shared__ uint2 s_c[kCandLds];
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_chunk[kMaxTipChunks];
+  __shared__ int s_w[NWAVE];
+  __shared__ uint32_t s_res[2];
+  const int tid = threadIdx.x;
+  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    __syncthreads();
+    const uint32_t b1 = g.info[(size_t)item * 4 + 0];
+    const uint32_t above1 = g.info[(size_t)item * 4 + 1];
+    const uint32_t count = g.info[(size_t)item * 4 + 2];
+    const bool in_lds = count <= (uint32_t)min(g.cand_cap, kCandLds);
+    CandSource src{nullptr, 0, g.scores + (size_t)item * g.T, g.T, b1};
+    if (in_lds) {
+      const uint2* cd = g.cand + (size_t)item * g.cand_cap;
+      for (int i = tid; i < (int)count; i += NT) s_c[i] = cd[i];
+      src.lds = s_c;
+      src.n = (int)count;
+    }
+    __syncthreads();
+    uint32_t need = (uint32_t)g.n_fac - above1;
+    int bin;
+    uint32_t above;
+    // key bits 20..10
+    histogram(src, s_hist, 2048, [](uint32_t, uint32_t) { return true; },
+              [](uint32_t k, uint32_t) { return (k >> 10) & 0x7FFu; });
+    find_bin_top(s_hist, 2048, need, s_w, s_res, bin, above);
+    need -= above;
+    const uint32_t pre22 = (b1 << 11) | (uint32_t)bin;
+    // key bits 9..0
+    histogram(src, s_hist, 1024, [=](uint32_t k, uint32_t) { return (k >> 10) == pre22; },
+              [](uint32_t k, uint32_t) { return k & 0x3FFu; });
+    find_bin_top(s_hist, 1024, need, s_w, s_res, bin, above);
+    need -= above;
+    const uint32_t kstar = (pre22 << 10) | (uint32_t)bin;
+    // the need-th smallest token among key == kstar, 10 bits at a time
+    uint32_t tpre = 0;
+    for (int shift = 20; shift >= 0; shift -= 10) {
+      const uint32_t hmask = (shift == 20) ? 0u : (0xFFFFFFFFu << (shift + 10));
+      histogram(src, s_hist, 1024,
+                [=](uint32_t k, uint32_t t) { return k == kstar && (t & hmask) == tpre; },
+                [=](uint32_t, uint32_t t) { return 1023u - ((t >> shift) & 0x3FFu); });
+      find_bin_top(s_hist, 1024, need, s_w, s_res, bin, above);
+      need -= above;
+      tpre |= (1023u - (uint32_t)bin) << shift;
+    }
+    const uint32_t tstar = tpre;
+    // per-chunk counts of selected candidates
+    for (int c = tid; c < g.nch_t; c += NT) s_chunk[c] = 0;
+    __syncthreads();
+    const int ct = g.ct;
+    src.for_each([&](uint32_t k, uint32_t t) {
+      if (k > kstar || (k == kstar && t <= tstar)) atomicAdd(&s_chunk[t / ct], 1u);
+    });
+    __syncthreads();
+    // exclusive prefix over chunks of (tokens above b1 + selected candidates)
+    const uint32_t* ngt = g.ngt + (size_t)item * g.nch_t;
+    uint32_t* off = g.off + (size_t)item * g.nch_t;
+    const int per = (g.nch_t + NT - 1) / NT;
+    const int c0 = min(g.nch_t, tid * per), c1 = min(g.nch_t, c0 + per);
+    int seg = 0;
+    for (int c = c0; c < c1; ++c) seg += (int)(ngt[c] + s_chunk[c]);
+    int tot;
+    int run = block_excl_scan(seg, s_w, tot);
+    for (int c = c0; c < c1; ++c) {
+      off[c] = (uint32_t)run;
+      run += (int)(ngt[c] + s_chunk[c]);
+    }
+    if (tid == 0) g.thr[item] = make_uint2(kstar, tstar);
+  }
+}
+
+// select_c: ordered compaction of the selected tokens of one chunk.
+__global__ __launch_bounds__(NT) void select_c_kernel(Geo g) {
+  __shared__ int s_w[NWAVE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_units = plan_idx_pairs(g.plan) * g.B * g.nch_t;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int item = u / g.nch_t, ch = u - item * g.nch_t;
+    const int pidx = item / g.B, b = item - pidx * g.B;
+    const int pair = idx_pairs(g)[pidx];
+    const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
+    const uint2 th = g.thr[item];
+    const uint32_t run0 = g.off[(size_t)item * g.nch_t + ch];
+    const float* sc = g.scores + (size_t)item * g.T;
+    int32_t* ix = g.idx + (size_t)item * g.n_fac;
+    int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
+    const int t0 = ch * g.ct, t1 = min(g.T, t0 + g.ct);
+    uint32_t run = run0;
+    for (int base = t0; base < t1; base += NT) {
+      const int tok = base + tid;
+      bool sel = false;
+      if (tok < t1) {
+        const uint32_t k = f2key(sc[tok]);
+        sel = k > th.x || (k == th.x && (uint32_t)tok <= th.y);
+      }
+      const uint64_t m = __ballot(sel);
+      __syncthreads();
+      if (lane == 0) s_w[wave] = __popcll(m);
+      __syncthreads();
+      uint32_t wb = 0, tt = 0;
+      for (int w = 0; w < NWAVE; ++w) {
+        wb += (w < wave) ? (uint32_t)s_w[w] : 0u;
+        tt += (uint32_t)s_w[w];
+      }
+      const uint32_t pos = run + wb + (uint32_t)mbcnt(m);
+      if (sel && pos < (uint32_t)g.n_fac) {
+        ix[pos] = tok;
+        if (ox) ox[pos] = tok;
+      }
+      run += tt;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// One unit = (attention item, chunk of <= kMaxChunkRows rows).  The group's G
+// query heads share every loaded row: lanes of a row (LPR of them, 16 bytes
+// each) form the dot products, then p = exp2(z - m) per head, then P.V.
+// Output: per head acc[d] = sum p v, m (log2 domain), l = sum p.
+template <typename E, int D, int G>
+__global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
+  constexpr int CPL = Vec<E>::N;
+  constexpr int LPR = D / CPL;
+  constexpr int RPW = 64 / LPR;
+  constexpr int RPB = RPW * NWAVE;
+  constexpr float kScale = (D == 128 ? 0.08838834764831845f : 0.125f) * 1.4426950408889634f;
+  __shared__ float s_z[G][kMaxChunkRows];
+  __shared__ int s_rows[kMaxChunkRows];
+  __shared__ float s_red[NWAVE][G][D];
+  __shared__ float s_ml[G][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = lane % LPR, rsub = lane / LPR;
+  const int n_ret = g.plan[1], n_str = g.plan[2];
+  const int n_fac_units = n_ret * g.B * g.nch_f;
+  const int n_units = n_fac_units + n_str * g.B * g.nch_s;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const bool fac = u < n_fac_units;
+    const int uu = fac ? u : u - n_fac_units;
+    const int nchunk = fac ? g.nch_f : g.nch_s;
+    const int item = uu / nchunk, chunk = uu - item * nchunk;
+    const int pa = item / g.B, b = item - pa * g.B;
+    const int pair = fac ? att_ret_pairs(g)[pa] : att_str_pairs(g)[pa];
+    const int lq = pair / g.Hkv, gi = pair - lq * g.Hkv;
+    const int lkv = g.clsa ? 0 : lq;
+    const size_t kvs = ((size_t)lkv * g.B + b) * g.Hkv + gi;
+    const E* kb = (const E*)g.k + kvs * (size_t)g.T * D;
+    const E* vb = (const E*)g.v + kvs * (size_t)g.T * D;
+    __syncthreads();
+    int nrows;
+    if (fac) {
+      const int iitem = g.clsa ? gi * g.B + b : pa * g.B + b;
+      const int32_t* ix = g.idx + (size_t)iitem * g.n_fac + (size_t)chunk * g.cf;
+      nrows = min(g.cf, g.n_fac - chunk * g.cf);
+      // indices come from select_c and are always in [0, T); the clamp only
+      // keeps a corrupted workspace from turning into out-of-range reads
+      for (int r = tid; r < nrows; r += NT) s_rows[r] = min(max(ix[r], 0), g.T - 1);
+    } else {
+      nrows = min(g.cs, g.n_srows - chunk * g.cs);
+      for (int r = tid; r < nrows; r += NT) {
+        const int v = chunk * g.cs + r;
+        s_rows[r] = v < g.s_end ? v : g.w_start + (v - g.s_end);
+      }
+    }
+    float qr[G][CPL];
+    const E* qp = (const E*)g.q + (((size_t)lq * g.B + b) * g.Hq + (size_t)gi * G) * D + slot * CPL;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      Vec<E>::cvt(ld16(qp + (size_t)h * D), qr[h]);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) qr[h][c] *= kScale;
+    }
+    __syncthreads();
+    // pass 1: logits (log2 domain) into s_z
+    for (int r0 = wave * RPW; r0 < nrows; r0 += 2 * RPB) {
+      uint4 raw[2];
+      int rr[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        rr[j] = r0 + j * RPB + rsub;
+        raw[j] = rr[j] < nrows ? ld16(kb + (size_t)s_rows[rr[j]] * D + slot * CPL)
+                               : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float kf[CPL];
+        Vec<E>::cvt(raw[j], kf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float s = 0.f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) s += qr[h][c] * kf[c];
+          s = group_sum<LPR>(s);
+          if (slot == h && rr[j] < nrows) s_z[h][rr[j]] = s;
+        }
+      }
+    }
+    __syncthreads();
+    for (int h = wave; h < G; h += NWAVE) {
+      float m = -INFINITY;
+      for (int r = lane; r < nrows; r += 64) m = fmaxf(m, s_z[h][r]);
+      m = wave_max(m);
+      float l = 0.f;
+      for (int r = lane; r < nrows; r += 64) {
+        const float p = exp2f(s_z[h][r] - m);
+        s_z[h][r] = p;
+        l += p;
+      }
+      l = wave_sum(l);
+      if (lane == 0) {
+        s_ml[h][0] = m;
+        s_ml[h][1] = l;
+      }
+    }
+    __syncthreads();
+    // pass 2: acc += p v
+    float acc[G][CPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[h][c] = 0.f;
+    for (int r0 = wave * RPW; r0 < nrows; r0 += 2 * RPB) {
+      uint4 raw[2];
+      int rr[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        rr[j] = r0 + j * RPB + rsub;
+        raw[j] = rr[j] < nrows ? ld16(vb + (size_t)s_rows[rr[j]] * D + slot * CPL)
+                               : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (rr[j] < nrows) {
+          float vf[CPL];
+          Vec<E>::cvt(raw[j], vf);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float p = s_z[h][rr[j]];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[h][c] += p * vf[c];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[h][c] += __shfl_xor(acc[h][c], o);
+    if (rsub == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) s_red[wave][h][slot * CPL + c] = acc[h][c];
+    }
+    __syncthreads();
+    const size_t a = ((size_t)lq * g.B + b) * g.Hkv + gi;
+    float* pp = g.part + ((a * g.nparts + chunk) * G) * (size_t)(D + 4);
+    for (int e = tid; e < G * D; e += NT) {
+      const int h = e / D, c = e - h * D;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) s += s_red[w][h][c];
+      pp[(size_t)h * (D + 4) + c] = s;
+    }
+    if (tid < G) {
+      pp[(size_t)tid * (D + 4) + D] = s_ml[tid][0];
+      pp[(size_t)tid * (D + 4) + D + 1] = s_ml[tid][1];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ merge
+__global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
+  const size_t total = (size_t)g.Lq * g.B * g.Hkv * g.G * g.d;
+  const int dd = g.d + 4;
+  for (size_t e = (size_t)blockIdx.x * NT + threadIdx.x; e < total; e += (size_t)gridDim.x * NT) {
+    const int c = (int)(e % g.d);
+    const size_t r = e / g.d;
+    const int h = (int)(r % g.G);
+    const size_t a = r / g.G;
+    const int gi = (int)(a % g.Hkv);
+    const size_t lb = a / g.Hkv;
+    const int b = (int)(lb % g.B);
+    const int lq = (int)(lb / g.B);
+    const int np = label_at(g, lq * g.Hkv + gi) ? g.nch_f : g.nch_s;
+    const float* pp = g.part + (a * g.nparts * g.G + h) * (size_t)dd;
+    const size_t stride = (size_t)g.G * dd;
+    float M = -INFINITY;
+    for (int s = 0; s < np; ++s) M = fmaxf(M, pp[s * stride + g.d]);
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < np; ++s) {
+      const float w = exp2f(pp[s * stride + g.d] - M);
+      L += w * pp[s * stride + g.d + 1];
+      O += w * pp[s * stride + c];
+    }
+    g.out[(((size_t)lq * g.B + b) * g.Hq + (size_t)gi * g.G + h) * g.d + c] = O / L;
+  }
+}
+
+// ------------------------------------------------------------------ kdom_pack
+template <typename E>
+__global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd) {
+  const int s = blockIdx.y;  // (l, b, gi) slice
+  const int gi = s % g.Hkv;
+  const int l = s / (g.Hkv * g.B);
+  const int32_t* dom = g.i_dom + ((size_t)l * g.Hkv + gi) * g.n_dom;
+  const E* k = (const E*)g.k + (size_t)s * g.T * g.d;
+  E* o = kd + (size_t)s * g.T * g.R;
+  const uint32_t per = (uint32_t)g.T * (uint32_t)g.R;
+  const int hd = g.d / 2;
+  for (uint32_t i = blockIdx.x * NT + threadIdx.x; i < per; i += gridDim.x * NT) {
+    const uint32_t t = i / (uint32_t)g.R;
+    const int e = (int)(i - t * (uint32_t)g.R);
+    E v = E(0);
+    if (e < 2 * g.n_dom) {
+      const int f = dom[e >> 1], cc = e & 1;
+      const int chn = g.interleaved ? 2 * f + cc : f + cc * hd;
+      v = k[(size_t)t * g.d + chn];
+    }
+    o[i] = v;
+  }
+}
+
+template <typename E, int D>
+hipError_t launch_attn_g(const Geo& g, int grid, hipStream_t s) {
+  switch (g.G) {
+    case 1: attn_kernel<E, D, 1><<<grid, NT, 0, s>>>(g); break;
+    case 2: attn_kernel<E, D, 2><<<grid, NT, 0, s>>>(g); break;
+    case 4: attn_kernel<E, D, 4><<<grid, NT, 0, s>>>(g); break;
+    case 8: attn_kernel<E, D, 8><<<grid, NT, 0, s>>>(g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_tip_v(const Geo& g, int grid, hipStream_t s) {
+  const int V = g.R * (int)sizeof(E) / 16;
+  switch (V) {
+    case 1: tip_kernel<E, 1><<<grid, NT, 0, s>>>(g); break;
+    case 2: tip_kernel<E, 2><<<grid, NT, 0, s>>>(g); break;
+    case 4: tip_kernel<E, 4><<<grid, NT, 0, s>>>(g); break;
+    case 8: tip_kernel<E, 8><<<grid, NT, 0, s>>>(g); break;
+    case 16: tip_kernel<E, 16><<<grid, NT, 0, s>>>(g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int clampi(long long v, int lo, int hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); }
+
+}  // namespace
+
+hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s) {
+  const int n_slices = g.Lkv * g.B * g.Hkv;
+  const uint32_t per = (uint32_t)g.T * (uint32_t)g.R;
+  const dim3 grid(clampi(((long long)per + NT - 1) / NT, 1, 2048), n_slices);
+  if (g.bf16)
+    kdom_pack_kernel<uint16_t><<<grid, NT, 0, s>>>(g, (uint16_t*)k_dom);
+  else
+    kdom_pack_kernel<float><<<grid, NT, 0, s>>>(g, (float*)k_dom);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const Geo& g, hipStream_t s) {
+  hipError_t e;
+  const long long n_idx_items = (long long)(g.clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
+  const long long n_att_items = (long long)g.Lq * g.Hkv * g.B;
+  const int grid_plan = clampi((n_idx_items * kHistBins / 4 + NT - 1) / NT, 1, g.grid);
+  plan_kernel<<<grid_plan, NT, 0, s>>>(g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int grid_tip = clampi(n_idx_items * g.nch_t, 1, g.grid);
+  e = g.bf16 ? launch_tip_v<uint16_t>(g, grid_tip, s) : launch_tip_v<float>(g, grid_tip, s);
+  if (e != hipSuccess) return e;
+  select_a_kernel<<<grid_tip, NT, 0, s>>>(g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  select_b_kernel<<<clampi(n_idx_items, 1, g.grid), NT, 0, s>>>(g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  select_c_kernel<<<grid_tip, NT, 0, s>>>(g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long long max_units = n_att_items * (long long)(g.nch_f > g.nch_s ? g.nch_f : g.nch_s);
+  const int grid_attn = clampi(max_units, 1, g.grid);
+  if (g.bf16)
+    e = g.d == 128 ? launch_attn_g<uint16_t, 128>(g, grid_attn, s) : launch_attn_g<uint16_t, 64>(g, grid_attn, s);
+  else
+    e = g.d == 128 ? launch_attn_g<float, 128>(g, grid_attn, s) : launch_attn_g<float, 64>(g, grid_attn, s);
+  if (e != hipSuccess) return e;
+  const long long n_out = n_att_items * g.G * g.d;
+  merge_kernel<<<clampi((n_out + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace has

@@ -1,0 +1,60 @@
+// Internal geometry shared by the host launch code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace has {
+
+constexpr int kHistBins = 2048;      // first radix digit: key bits 31..21
+constexpr int kCandLds = 8192;       // candidates held in LDS by the threshold pass
+constexpr int kMaxChunkRows = 512;   // attention rows per work unit
+constexpr int kMaxTipChunks = 1024;  // score chunks per item
+constexpr int kMaxPairs = 8192;      // (layer, KV group) pairs per call
+
+// One decode call, with the workspace carved.  Passed by value to kernels.
+struct Geo {
+  // shape
+  int Lq, Lkv, B, Hq, Hkv, G, d, T, n_fac, n_sink, window, n_dom;
+  int R;            // k_dom row elements
+  int bf16;         // kv dtype
+  int clsa;         // 1: one index per (b, g) shared by Lq layers over one cache
+  int interleaved;  // rope pairing
+  // chunking
+  int ct, nch_t;    // score/select chunk tokens and count per item
+  int cf, nch_f;    // FAC chunk rows and count per item
+  int cs, nch_s;    // stream chunk rows and count per item
+  int n_srows, s_end, w_start;  // streaming rows: [0, s_end) U [w_start, T)
+  int nparts;       // partial slots per attention item
+  int cand_cap;     // candidate slots per index item
+  int grid;         // persistent grid size
+  // workspace
+  int* plan;         // [4 + 3*kMaxPairs]: n_idx_pairs, n_att_ret, n_att_str, -, lists
+  uint32_t* hist;    // [idx items][kHistBins]
+  uint32_t* info;    // [idx items][4]: b1, count above b1, candidate count, -
+  uint2* cand;       // [idx items][cand_cap] (key, token)
+  uint32_t* ngt;     // [idx items][nch_t] tokens above the first digit bin per chunk
+  uint32_t* off;     // [idx items][nch_t] output offset of each chunk
+  uint2* thr;        // [idx items] (key*, token*) selection threshold
+  float* scores;     // [idx items][T]
+  int32_t* idx;      // [idx items][n_fac]
+  float* part;       // [att items][nparts][G][d + 4]: acc[d], m, l
+  // inputs / outputs
+  const void* q;
+  const void* q_index;
+  const void* k;
+  const void* v;
+  const void* kdom;
+  const int32_t* i_dom;
+  const uint8_t* labels;
+  float* out;
+  int32_t* idx_out;
+};
+
+inline __host__ __device__ int plan_idx_pairs(const int* p) { return p[0]; }
+
+hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s);
+hipError_t launch_decode(const Geo& g, hipStream_t s);
+
+}  // namespace has

@@ -1,0 +1,496 @@
+// AoH labeller kernels for gfx950.
+//
+// Method: "Resumen Técnico: Autonomía de Cabezales (AoH)", Metodología:
+//   §1 M_h = W_K^T W_Q; §2 ER = exp of the entropy of the normalised singular
+//   values of M_h; §3 those singular values (squared) are the eigenvalues of
+//   the d_head x d_head proxy C_h = (W_Q W_Q^T)(W_K W_K^T); §4 rank by ER, the
+//   k lowest are retrieval heads, GQA groups aggregate by the mean.
+//
+// Pipeline (one stream, no host synchronisation):
+//   gram      G = W W^T for every query and key head (matrix cores, bf16 or
+//             fp32 in, fp32 accumulate).  Reads every weight once: the
+//             HBM-bound step.
+//   spectrum  per query head, in fp64 LDS: Cholesky G_K = L L^T, then the
+//             symmetric S = L^T G_Q L (fp64 matrix cores), which is similar
+//             to C_h = G_Q G_K; Householder tridiagonalisation of S.
+//   bisect    eigenvalues of the tridiagonal by Sturm-count bisection (one
+//             thread per eigenvalue), sigma = sqrt(max(lambda, 0)) and ER.
+//   finalize  group mean of ER, global rank with ties to the lower index,
+//             labels.
+#include "internal.h"
+#include "label.h"
+
+namespace has {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NT = 256;
+constexpr int NWAVE = NT / 64;
+
+struct LGeo {
+  int L, Hq, Hkv, dm, d, G;
+  int n_ret;
+  float thr;
+  const void* wq;
+  const void* wk;
+  float* gram;     // [L*Hq + L*Hkv][d][d]: query heads, then key heads
+  double* tscr;    // [L*Hq][d][d] scratch for G_Q L
+  float* tri;      // [L*Hq][2][d]: diagonal, off-diagonal (fp32)
+  float* er_head;  // [L*Hq]
+  float* er_group; // [L*Hkv]
+  uint8_t* labels;
+};
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+struct LabelLayout {
+  size_t gram, tscr, tri, erh, erg, bytes;
+};
+
+LabelLayout label_layout(int L, int Hq, int Hkv, int d) {
+  LabelLayout o{};
+  size_t at = 0;
+  o.gram = at;
+  at = align256(at + (size_t)(L * Hq + L * Hkv) * d * d * 4);
+  o.tscr = at;
+  at = align256(at + (size_t)L * Hq * d * d * 8);
+  o.tri = at;
+  at = align256(at + (size_t)L * Hq * 2 * d * 4);
+  o.erh = at;
+  at = align256(at + (size_t)L * Hq * 4);
+  o.erg = at;
+  at = align256(at + (size_t)L * Hkv * 4);
+  o.bytes = at;
+  return o;
+}
+
+// ------------------------------------------------------------------ gram
+// One workgroup per head: G = W W^T over d_model.  The head's rows are
+// staged through LDS in 128-byte-wide k tiles (double buffered); wave w owns
+// a row band of 32 x 32 output tiles.  MFMA 32x32: output element
+// (8*(r/4) + 4*(lane/32) + r%4, lane%32) sits in register r of lane.
+template <typename E, int D>
+__global__ __launch_bounds__(NT) void gram_kernel(LGeo g) {
+  constexpr bool BF = sizeof(E) == 2;
+  constexpr int KT = 128 / sizeof(E);           // elements per k tile
+  constexpr int LDW = BF ? KT + 8 : KT + 1;     // padded LDS row
+  constexpr int CPR = KT * sizeof(E) / 16;       // 16-byte chunks per row
+  constexpr int CH = D * CPR / NT;               // chunks per thread
+  constexpr int NB = D / 32;
+  constexpr int TPW = NB * NB / NWAVE;
+  __shared__ __attribute__((aligned(16))) E s_w[2][D][LDW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = blockIdx.x;
+  const int nq = g.L * g.Hq;
+  const E* W = m < nq ? (const E*)g.wq + (size_t)m * D * g.dm
+                      : (const E*)g.wk + (size_t)(m - nq) * D * g.dm;
+  uint4 reg[CH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int id = tid + c * NT;
+      const int row = id / CPR, col = (id % CPR) * (16 / (int)sizeof(E));
+      reg[c] = *reinterpret_cast<const uint4*>(W + (size_t)row * g.dm + k0 + col);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int id = tid + c * NT;
+      const int row = id / CPR, col = (id % CPR) * (16 / (int)sizeof(E));
+      if constexpr (BF) {
+        *reinterpret_cast<uint4*>(&s_w[buf][row][col]) = reg[c];
+      } else {
+        s_w[buf][row][col + 0] = __uint_as_float(reg[c].x);
+        s_w[buf][row][col + 1] = __uint_as_float(reg[c].y);
+        s_w[buf][row][col + 2] = __uint_as_float(reg[c].z);
+        s_w[buf][row][col + 3] = __uint_as_float(reg[c].w);
+      }
+    }
+  };
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  const int nk = g.dm / KT;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * KT);
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < KT; ks += 16) {
+        const int kk = ks + (lane >> 5) * 8;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          const int t = wave * TPW + i, rb = t / NB, cb = t % NB;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_w[buf][rb * 32 + (lane & 31)][kk]);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&s_w[buf][cb * 32 + (lane & 31)][kk]);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll 4
+      for (int ks = 0; ks < KT; ks += 2) {
+        const int kk = ks + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          const int t = wave * TPW + i, rb = t / NB, cb = t % NB;
+          const float a = s_w[buf][rb * 32 + (lane & 31)][kk];
+          const float b = s_w[buf][cb * 32 + (lane & 31)][kk];
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i], 0, 0, 0);
+        }
+      }
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+  float* out = g.gram + (size_t)m * D * D;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wave * TPW + i, rb = t / NB, cb = t % NB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      out[(size_t)row * D + cb * 32 + (lane & 31)] = acc[i][r];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ spectrum
+__device__ __forceinline__ double wave_sum_d(double x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// MFMA f64 16x16x4: A element (lane%16, lane/16), B element (lane/16,
+// lane%16); output (4*(lane/16) + r, lane%16) in register r.
+template <int D>
+__global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
+  constexpr int LD = D + 1;
+  constexpr int RB = D / 64;  // 16-row bands per wave
+  constexpr int CB = D / 16;  // 16-col bands
+  __shared__ double s_m[D * LD];
+  __shared__ double s_v[D], s_p[D];
+  __shared__ double s_red[NWAVE];
+  __shared__ float s_d[D], s_e[D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.x;                 // l*Hq + h
+  const int l = head / g.Hq, h = head - l * g.Hq;
+  const int gk = g.L * g.Hq + l * g.Hkv + h / g.G;
+  const float* GQ = g.gram + (size_t)head * D * D;
+  const float* GK = g.gram + (size_t)gk * D * D;
+  double* A = s_m;
+
+  auto block_sum = [&](double x) -> double {
+    x = wave_sum_d(x);
+    if (lane == 0) s_red[wave] = x;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) t += s_red[w];
+    __syncthreads();
+    return t;
+  };
+
+  // 1. G_K -> LDS (fp64); right-looking Cholesky G_K = L L^T, columns whose
+  //    pivot is not positive (rank-deficient key projections) are zeroed.
+  double dmax = 0.0;
+  for (int e = tid; e < D * D; e += NT) {
+    const int i = e / D, j = e - i * D;
+    A[i * LD + j] = (double)GK[e];
+  }
+  __syncthreads();
+  for (int i = 0; i < D; ++i) dmax = fmax(dmax, A[i * LD + i]);
+  const double tol = 1e-12 * dmax;
+  for (int j = 0; j < D; ++j) {
+    const double piv = A[j * LD + j];
+    __syncthreads();
+    const bool zero = !(piv > tol);
+    const double ljj = zero ? 0.0 : sqrt(piv);
+    for (int i = j + tid; i < D; i += NT) A[i * LD + j] = zero ? 0.0 : (i == j ? ljj : A[i * LD + j] / ljj);
+    __syncthreads();
+    const int m = D - j - 1;
+    for (int e = tid; e < m * m; e += NT) {
+      const int ii = e / m, kk = e - ii * m;
+      if (kk <= ii) {
+        const int r = j + 1 + ii, c = j + 1 + kk;
+        A[r * LD + c] -= A[r * LD + j] * A[c * LD + j];
+      }
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < D * D; e += NT) {
+    const int i = e / D, j = e - i * D;
+    if (j > i) A[i * LD + j] = 0.0;
+  }
+  __syncthreads();
+
+  // 2. T = G_Q L (A operand G_Q from global fp32, B operand L from LDS).
+  f64x4 acc[RB][CB];
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int c = 0; c < CB; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int k = 0; k < D; k += 4) {
+    const int kk = k + (lane >> 4);
+    double av[RB];
+#pragma unroll
+    for (int a = 0; a < RB; ++a) av[a] = (double)GQ[(size_t)((wave * RB + a) * 16 + (lane & 15)) * D + kk];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const double bv = A[kk * LD + c * 16 + (lane & 15)];
+#pragma unroll
+      for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
+    }
+  }
+  double* T = g.tscr + (size_t)head * D * D;
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        T[(size_t)((wave * RB + a) * 16 + 4 * (lane >> 4) + r) * D + c * 16 + (lane & 15)] = acc[a][c][r];
+  __threadfence();
+  __syncthreads();
+
+  // 3. S = L^T T (A operand L^T from LDS, B operand T from global).
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int c = 0; c < CB; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int k = 0; k < D; k += 4) {
+    const int kk = k + (lane >> 4);
+    double av[RB];
+#pragma unroll
+    for (int a = 0; a < RB; ++a) av[a] = A[kk * LD + (wave * RB + a) * 16 + (lane & 15)];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const double bv = T[(size_t)kk * D + c * 16 + (lane & 15)];
+#pragma unroll
+      for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        A[((wave * RB + a) * 16 + 4 * (lane >> 4) + r) * LD + c * 16 + (lane & 15)] = acc[a][c][r];
+  __syncthreads();
+  for (int e = tid; e < D * D; e += NT) {
+    const int i = e / D, j = e - i * D;
+    if (j > i) {
+      const double s = 0.5 * (A[i * LD + j] + A[j * LD + i]);
+      A[i * LD + j] = s;
+      A[j * LD + i] = s;
+    }
+  }
+  __syncthreads();
+
+  // 4. Householder tridiagonalisation of S (similarity, eigenvalues kept).
+  for (int k = 0; k < D - 2; ++k) {
+    const int m = D - k - 1, r0 = k + 1;
+    const double x = tid < m ? A[(r0 + tid) * LD + k] : 0.0;
+    const double nrm2 = block_sum(x * x);
+    const double x0 = A[r0 * LD + k];
+    const double alpha = x0 >= 0.0 ? -sqrt(nrm2) : sqrt(nrm2);
+    const double vn2 = nrm2 - x0 * x0 + (x0 - alpha) * (x0 - alpha);
+    if (tid == 0) s_d[k] = (float)A[k * LD + k];
+    if (!(vn2 > 0.0)) {
+      if (tid == 0) s_e[k] = (float)x0;
+      continue;
+    }
+    if (tid == 0) s_e[k] = (float)alpha;
+    const double beta = 2.0 / vn2;
+    if (tid < m) s_v[tid] = tid == 0 ? x0 - alpha : x;
+    __syncthreads();
+    if (tid < m) {
+      const double* row = A + (r0 + tid) * LD + r0;
+      double s = 0.0;
+      for (int j = 0; j < m; ++j) s += row[j] * s_v[j];
+      s_p[tid] = beta * s;
+    }
+    __syncthreads();
+    const double kk = 0.5 * beta * block_sum(tid < m ? s_v[tid] * s_p[tid] : 0.0);
+    if (tid < m) s_p[tid] -= kk * s_v[tid];
+    __syncthreads();
+    for (int i = wave; i < m; i += NWAVE) {
+      const double vi = s_v[i], wi = s_p[i];
+      double* row = A + (r0 + i) * LD + r0;
+      for (int j = lane; j < m; j += 64) row[j] -= vi * s_p[j] + wi * s_v[j];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    s_d[D - 2] = (float)A[(D - 2) * LD + D - 2];
+    s_e[D - 2] = (float)A[(D - 1) * LD + D - 2];
+    s_d[D - 1] = (float)A[(D - 1) * LD + D - 1];
+    s_e[D - 1] = 0.f;
+  }
+  __syncthreads();
+  float* tri = g.tri + (size_t)head * 2 * D;
+  for (int i = tid; i < D; i += NT) {
+    tri[i] = s_d[i];
+    tri[D + i] = s_e[i];
+  }
+}
+
+// ------------------------------------------------------------------ bisect
+// Number of eigenvalues of the tridiagonal below x (Sturm sequence of the
+// LDL^T pivots; an exact zero pivot is nudged negative).
+template <int D>
+__device__ __forceinline__ int sturm_count(const float* d, const float* e2, float x) {
+  int cnt = 0;
+  float q = d[0] - x;
+  cnt += q < 0.f;
+  for (int i = 1; i < D; ++i) {
+    if (fabsf(q) < 1e-30f) q = -1e-30f;
+    q = (d[i] - x) - e2[i - 1] * __builtin_amdgcn_rcpf(q);
+    cnt += q < 0.f;
+  }
+  return cnt;
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void bisect_kernel(LGeo g) {
+  __shared__ float s_d[D], s_e2[D];
+  __shared__ float s_lo[D / 64], s_hi[D / 64];
+  __shared__ double s_sum[D / 64];
+  const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
+  const int head = blockIdx.x;
+  const float* tri = g.tri + (size_t)head * 2 * D;
+  const float dj = tri[j], ej = tri[D + j];
+  s_d[j] = dj;
+  s_e2[j] = ej * ej;
+  const float ejm = j > 0 ? tri[D + j - 1] : 0.f;
+  float lo = dj - fabsf(ej) - fabsf(ejm), hi = dj + fabsf(ej) + fabsf(ejm);
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+  }
+  if (lane == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+  }
+  __syncthreads();
+  for (int w = 0; w < D / 64; ++w) {
+    lo = fminf(lo, s_lo[w]);
+    hi = fmaxf(hi, s_hi[w]);
+  }
+  const float pad = 1e-6f * fmaxf(fabsf(lo), fabsf(hi)) + 1e-30f;
+  float a = lo - pad, b = hi + pad;
+  for (int it = 0; it < 64; ++it) {
+    const float mid = 0.5f * (a + b);
+    if (!(mid > a && mid < b)) break;
+    if (sturm_count<D>(s_d, s_e2, mid) > j) b = mid;
+    else a = mid;
+  }
+  const double lam = fmax(0.5 * ((double)a + (double)b), 0.0);
+  const double sigma = sqrt(lam);
+  double tot = wave_sum_d(sigma);
+  if (lane == 0) s_sum[wave] = tot;
+  __syncthreads();
+  tot = 0.0;
+  for (int w = 0; w < D / 64; ++w) tot += s_sum[w];
+  __syncthreads();
+  const double p = tot > 0.0 ? sigma / tot : 0.0;
+  double hterm = p > 0.0 ? -p * log(p) : 0.0;
+  hterm = wave_sum_d(hterm);
+  if (lane == 0) s_sum[wave] = hterm;
+  __syncthreads();
+  if (j == 0) {
+    double H = 0.0;
+    for (int w = 0; w < D / 64; ++w) H += s_sum[w];
+    g.er_head[head] = (float)exp(H);
+  }
+}
+
+// ------------------------------------------------------------------ finalize
+__global__ __launch_bounds__(NT) void finalize_kernel(LGeo g) {
+  __shared__ float s_eg[kMaxPairs];
+  const int P = g.L * g.Hkv;
+  for (int p = threadIdx.x; p < P; p += NT) {
+    const int l = p / g.Hkv, gi = p - l * g.Hkv;
+    const float* eh = g.er_head + (size_t)l * g.Hq + gi * g.G;
+    float s = 0.f;
+    for (int h = 0; h < g.G; ++h) s += eh[h];
+    s_eg[p] = s / (float)g.G;
+  }
+  __syncthreads();
+  const int p = blockIdx.x * NT + threadIdx.x;
+  if (p >= P) return;
+  const float e = s_eg[p];
+  g.er_group[p] = e;
+  uint8_t lab;
+  if (g.n_ret >= 0) {
+    int rank = 0;
+    for (int q = 0; q < P; ++q) {
+      const float f = s_eg[q];
+      rank += (f < e || (f == e && q < p)) ? 1 : 0;
+    }
+    lab = rank < g.n_ret ? 1 : 0;
+  } else {
+    lab = e < g.thr ? 1 : 0;
+  }
+  g.labels[p] = lab;
+}
+
+}  // namespace
+
+size_t label_workspace_bytes(int L, int Hq, int Hkv, int dm, int d) {
+  (void)dm;
+  if (L < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
+  return label_layout(L, Hq, Hkv, d).bytes;
+}
+
+hipError_t launch_label(const LabelArgs& a, hipStream_t s) {
+  const LabelLayout lo = label_layout(a.L, a.Hq, a.Hkv, a.d);
+  char* ws = (char*)a.ws;
+  LGeo g{};
+  g.L = a.L;
+  g.Hq = a.Hq;
+  g.Hkv = a.Hkv;
+  g.dm = a.dm;
+  g.d = a.d;
+  g.G = a.Hq / a.Hkv;
+  g.n_ret = a.n_retrieval;
+  g.thr = a.threshold;
+  g.wq = a.w_q;
+  g.wk = a.w_k;
+  g.gram = (float*)(ws + lo.gram);
+  g.tscr = (double*)(ws + lo.tscr);
+  g.tri = (float*)(ws + lo.tri);
+  g.er_head = a.er_head ? a.er_head : (float*)(ws + lo.erh);
+  g.er_group = a.er_group ? a.er_group : (float*)(ws + lo.erg);
+  g.labels = a.labels;
+  const int n_mats = a.L * a.Hq + a.L * a.Hkv;
+  const int n_heads = a.L * a.Hq;
+  if (a.d == 128) {
+    if (a.bf16) gram_kernel<uint16_t, 128><<<n_mats, NT, 0, s>>>(g);
+    else gram_kernel<float, 128><<<n_mats, NT, 0, s>>>(g);
+    spectrum_kernel<128><<<n_heads, NT, 0, s>>>(g);
+    bisect_kernel<128><<<n_heads, 128, 0, s>>>(g);
+  } else {
+    if (a.bf16) gram_kernel<uint16_t, 64><<<n_mats, NT, 0, s>>>(g);
+    else gram_kernel<float, 64><<<n_mats, NT, 0, s>>>(g);
+    spectrum_kernel<64><<<n_heads, NT, 0, s>>>(g);
+    bisect_kernel<64><<<n_heads, 64, 0, s>>>(g);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int P = a.L * a.Hkv;
+  finalize_kernel<<<(P + NT - 1) / NT, NT, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace has

@@ -1,0 +1,175 @@
+/* has.h -- head-aware sparse decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libhas.so.  The operations follow three method descriptions:
+ *
+ *   [AoH]  "Resumen Técnico: Autonomía de Cabezales (Autonomy-of-Heads, AoH)"
+ *          (gist.science, paper 2608.06849), Metodología §1-§4.
+ *   [FASA] "FASA: Frequency-aware Sparse Attention" (gist.science, paper
+ *          2602.03152), §2.A-§2.C.
+ *   [CLSA] "El enrutamiento compartido entre capas acelera la atención
+ *          dispersa 7 veces ..." (seventnews.com, on "CLSA: You Only Index
+ *          Once"), section "Cómo funciona CLSA".
+ *
+ * Conventions for every entry point:
+ *   - Every array argument is a DEVICE pointer to contiguous row-major data,
+ *     aligned to 16 bytes, owned by the caller.  The library never allocates
+ *     or frees memory and never synchronises the stream.
+ *   - `stream` is a hipStream_t (NULL = the default stream); all device work
+ *     is enqueued on it, in order, and is asynchronous to the host.
+ *   - `ws`/`ws_bytes` is caller-owned scratch memory of at least the size the
+ *     matching *_workspace() query returns; its contents on entry do not
+ *     matter and are undefined on exit.  Two calls that run concurrently
+ *     must not share a workspace.
+ *   - Arguments are validated on the host before anything is enqueued: an
+ *     error status means nothing was launched and no output was written.
+ *     HAS_ERR_HIP means a HIP call failed while enqueueing; outputs are then
+ *     undefined.  has_last_error() gives a message (thread-local).
+ *   - Array contents are not checked (finite values; i_dom entries distinct
+ *     and in [0, d_head/2); labels in {0, 1}).
+ *   - Threads may call the library concurrently on distinct streams.
+ */
+#ifndef HAS_H_
+#define HAS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int has_status;
+#define HAS_OK 0
+#define HAS_ERR_INVALID_ARG 1 /* a size, pointer or alignment is invalid */
+#define HAS_ERR_UNSUPPORTED 2 /* valid, but outside what the kernels implement */
+#define HAS_ERR_WORKSPACE 3   /* ws is NULL or smaller than the query says */
+#define HAS_ERR_HIP 4         /* a HIP runtime call failed */
+
+typedef enum { HAS_F32 = 0, HAS_BF16 = 1 } has_dtype;
+
+/* Rotary pairing of the d/2 frequency chunks ([FASA] §2.A: RoPE splits a
+ * d-vector into d/2 two-dimensional subspaces).  Chunk f holds channels
+ * (f, f + d/2) in the rotate-half layout and (2f, 2f + 1) in the interleaved
+ * layout. */
+#define HAS_ROPE_ROTATE_HALF 0
+#define HAS_ROPE_INTERLEAVED 1
+
+const char* has_status_string(has_status s);
+const char* has_last_error(void);
+
+/* ------------------------------------------------------------------ AoH --
+ * aoh_label: data-free head labelling from frozen weights ([AoH] §1-§4).
+ *
+ * For query head h of layer l, with KV group g = h / (n_q_heads/n_kv_heads):
+ *   W_Q^h = w_q[l, h*d_head : (h+1)*d_head, :]    (d_head x d_model)
+ *   W_K^g = w_k[l, g*d_head : (g+1)*d_head, :]
+ *   C_h = (W_Q^h W_Q^hT)(W_K^g W_K^gT)           ([AoH] §3, d_head x d_head)
+ * whose eigenvalues are the squared nonzero singular values sigma^2 of the
+ * operator M_h = W_K^T W_Q ([AoH] §1).  Then, with s = sigma / sum(sigma),
+ *   er_head[l, h]  = exp(-sum_k s_k ln s_k)       ([AoH] §2; 0 ln 0 = 0)
+ *   er_group[l, g] = mean of er_head over the group's query heads ([AoH] §4)
+ *   labels[l, g]   = 1 (retrieval) for the n_retrieval lowest er_group over
+ *                    all (l, g), ties to the lower l*n_kv_heads + g; when
+ *                    n_retrieval < 0, labels = (er_group < er_threshold).
+ *                    0 = streaming.
+ *
+ * w_q: [n_layers, n_q_heads*d_head, d_model], w_k: [n_layers,
+ * n_kv_heads*d_head, d_model], both of dtype `wdt` (the layout of a
+ * PyTorch nn.Linear weight).  er_head [n_layers, n_q_heads] f32 and
+ * er_group [n_layers, n_kv_heads] f32 may be NULL; labels
+ * [n_layers, n_kv_heads] uint8 is required.
+ * Supported: d_head in {64, 128}, d_model a multiple of 64, d_model >= d_head,
+ * 0 <= n_retrieval <= n_layers*n_kv_heads (or < 0 for the threshold).
+ * Eigenvalues are computed in fp32 (Gram products on the matrix cores). */
+size_t aoh_label_workspace(int n_layers, int n_q_heads, int n_kv_heads, int d_model, int d_head);
+has_status aoh_label(int n_layers, int n_q_heads, int n_kv_heads, int d_model, int d_head,
+                     has_dtype wdt, const void* w_q, const void* w_k, int n_retrieval,
+                     float er_threshold, float* er_head, float* er_group, uint8_t* labels,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------- decode --
+ * Shape of one decode call.  n_layers layers, `batch` sequences, each with a
+ * cache of ctx_len tokens at positions 0..ctx_len-1 (the current token
+ * included); queries are for position ctx_len-1.
+ *   n_q_heads % n_kv_heads == 0, G = n_q_heads / n_kv_heads in {1,2,4,8}
+ *   d_head in {64, 128}; 1 <= n_dom <= d_head/2
+ *   1 <= n_fac <= ctx_len; n_sink >= 0, window >= 0, n_sink + window >= 1
+ *   n_fac <= 65536, ctx_len <= 2^30
+ */
+typedef struct has_decode_dims {
+  int n_layers;
+  int batch;
+  int n_q_heads;
+  int n_kv_heads;
+  int d_head;
+  int ctx_len;
+  int n_fac;      /* tokens kept per retrieval (layer, sequence, KV group) */
+  int n_sink;     /* streaming heads: first n_sink tokens ... */
+  int window;     /* ... plus the last `window` tokens */
+  int n_dom;      /* |I_dom|, dominant frequency chunks per KV group */
+  int kv_dtype;   /* has_dtype of q, k_cache, v_cache, k_dom */
+  int rope_layout;/* HAS_ROPE_ROTATE_HALF or HAS_ROPE_INTERLEAVED */
+} has_decode_dims;
+
+/* Elements per row of the dominant-key copy: 2*n_dom rounded up to a power
+ * of two count of 16-byte vectors (zero padded). */
+int kdom_row_elems(const has_decode_dims* dims);
+
+/* kdom_pack: builds the dominant-chunk key copy that TIP scoring reads
+ * ([FASA] §2.C: only the dominant key components need to be touched for
+ * scoring).  For every cache row t of slice (l, b, g) and i < n_dom, c in {0,1}:
+ *   k_dom[l,b,g,t, 2i+c] = k_cache[l,b,g,t, chan(i_dom[l,g,i], c)]
+ * with chan() from rope_layout; the padding elements are 0.
+ * k_cache [n_layers,batch,n_kv_heads,ctx_len,d_head] (kv_dtype), i_dom
+ * [n_layers,n_kv_heads,n_dom] int32, k_dom
+ * [n_layers,batch,n_kv_heads,ctx_len,kdom_row_elems] (kv_dtype).
+ * Meant for cache-write time; not part of a decode step. */
+has_status kdom_pack(const has_decode_dims* dims, const void* k_cache, const int32_t* i_dom,
+                     void* k_dom, void* stream);
+
+/* sparse_decode_step: one decode step of head-heterogeneous token-sparse
+ * attention over all n_layers layers.  For every (l, b, g):
+ *   labels[l,g] = 1 (retrieval, [FASA] §2.B):
+ *     qbar = mean of q[l,b,h] over the group's heads h;
+ *     s_t  = sum over f in i_dom[l,g] of the chunk-f part of qbar . k_t
+ *            (TIP, [FASA] §2.B.1), for t < ctx_len, fp32;
+ *     S    = the n_fac tokens with the largest s_t, ties to the lower t;
+ *   labels[l,g] = 0 (streaming, [AoH] §4):
+ *     S    = [0, n_sink) united with [ctx_len - window, ctx_len).
+ *   For each head h of the group (FAC, [FASA] §2.B.2, full d_head):
+ *     out[l,b,h] = sum_{t in S} softmax_t(q[l,b,h].k_t / sqrt(d_head)) v_t.
+ * q [n_layers,batch,n_q_heads,d_head] and the caches
+ * [n_layers,batch,n_kv_heads,ctx_len,d_head] hold post-RoPE values of
+ * kv_dtype; k_dom is kdom_pack's output for the same i_dom; labels
+ * [n_layers,n_kv_heads] uint8; out [n_layers,batch,n_q_heads,d_head] f32.
+ * idx_out [n_layers,batch,n_kv_heads,n_fac] int32 receives S ascending for
+ * retrieval groups and -1 for streaming groups; it may be NULL.
+ * Accumulation is fp32; scores and selection are deterministic. */
+size_t sparse_decode_workspace(const has_decode_dims* dims);
+has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const void* k_cache,
+                              const void* v_cache, const void* k_dom, const int32_t* i_dom,
+                              const uint8_t* labels, float* out, int32_t* idx_out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* shared_index_decode: CLSA mode ([CLSA] "Cómo funciona CLSA").  The
+ * dims->n_layers = N layers share ONE cache.  The index is computed once per
+ * (b, g) by TIP + top-n_fac (as in sparse_decode_step) from the indexer
+ * query q_index [batch,n_q_heads,d_head] (NULL: q[0]) and then reused by all
+ * N layers: for layer n with labels[n,g] = 1 (or labels == NULL),
+ *   out[n,b,h] = FAC over the shared index with the layer's own q[n,b,h];
+ * with labels[n,g] = 0 the layer attends to sink + window of the cache.
+ * q [N,batch,n_q_heads,d_head]; k_cache, v_cache [batch,n_kv_heads,ctx_len,
+ * d_head]; k_dom [batch,n_kv_heads,ctx_len,kdom_row_elems] (kdom_pack with
+ * n_layers = 1); i_dom [n_kv_heads,n_dom]; labels [N,n_kv_heads] or NULL;
+ * out [N,batch,n_q_heads,d_head] f32; idx_out [batch,n_kv_heads,n_fac] or
+ * NULL. */
+size_t shared_index_workspace(const has_decode_dims* dims);
+has_status shared_index_decode(const has_decode_dims* dims, const void* q, const void* q_index,
+                               const void* k_cache, const void* v_cache, const void* k_dom,
+                               const int32_t* i_dom, const uint8_t* labels, float* out,
+                               int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HAS_H_ */

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_aware_sparse_amd as H
+from head_aware_sparse_amd.binding import DecodeDims, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "has.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"aoh_label", "sparse_decode_step", "shared_index_decode", "kdom_pack"} <= set(names)
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _dims(**over):
+    d = DecodeDims(1, 1, 32, 8, 128, 32768, 2048, 4, 1024, 16, H.HAS_BF16, 0)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = 0x10000  # never dereferenced: validation fails first
+
+
+def _decode(d, ws_bytes=1 << 40, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, kd=FAKE, idom=FAKE, lab=FAKE, out=FAKE, idx=None, ws=FAKE)
+    p.update(ptrs)
+    P = ctypes.c_void_p
+    return lib().sparse_decode_step(ctypes.byref(d), P(p["q"]), P(p["k"]), P(p["v"]), P(p["kd"]), P(p["idom"]),
+                                    P(p["lab"]), P(p["out"]), P(p["idx"]), P(p["ws"]), ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n_q_heads=30), 1), (dict(n_q_heads=48, n_kv_heads=3), 2), (dict(d_head=96), 2),
+    (dict(d_head=7), 1), (dict(ctx_len=0), 1), (dict(n_fac=0), 1), (dict(n_fac=40000), 1),
+    (dict(n_sink=0, window=0), 1), (dict(window=-1), 1), (dict(n_dom=0), 1), (dict(n_dom=65), 1),
+    (dict(kv_dtype=5), 1), (dict(rope_layout=3), 1), (dict(n_layers=2000, n_kv_heads=8, n_q_heads=8), 2),
+    (dict(ctx_len=1 << 23, n_fac=10), 2), (dict(batch=0), 1),
+])
+def test_bad_dims_rejected(over, status):
+    assert _decode(_dims(**over)) == status
+    assert H.last_error()
+
+
+def test_bad_pointers_and_workspace():
+    d = _dims()
+    assert _decode(d, q=None) == 1 and "q" in H.last_error()
+    assert _decode(d, kd=FAKE + 4) == 1 and "aligned" in H.last_error()
+    assert _decode(d, lab=None) == 1
+    assert _decode(d, idx=FAKE + 8) == 1
+    assert _decode(d, ws=None) == 3
+    need = H.sparse_decode_workspace(d)
+    assert need > 0
+    assert _decode(d, ws_bytes=need - 1) == 3
+    assert H.sparse_decode_workspace(_dims(d_head=96)) == 0
+
+
+def test_shared_index_allows_null_labels_only_there():
+    d = _dims(n_layers=8)
+    P = ctypes.c_void_p
+    r = lib().shared_index_decode(ctypes.byref(d), P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None,
+                                  P(FAKE), None, None, 1 << 40, None)
+    assert r == 3  # passes argument checks, stops at the NULL workspace
+    assert H.shared_index_workspace(d) > 0
+
+
+def test_label_argument_checks():
+    P = ctypes.c_void_p
+    L = lib()
+    ws = 1 << 40
+    args = lambda **o: dict(dict(L=1, Hq=4, Hkv=4, dm=256, d=64, wdt=0, wq=FAKE, wk=FAKE, k=2, thr=0.0, lab=FAKE,
+                                  ws=FAKE), **o)
+
+    def call(a):
+        return L.aoh_label(a["L"], a["Hq"], a["Hkv"], a["dm"], a["d"], a["wdt"], P(a["wq"]), P(a["wk"]), a["k"],
+                           a["thr"], None, None, P(a["lab"]), P(a["ws"]) if a["ws"] else None, ws, None)
+    assert call(args(Hq=6)) == 1
+    assert call(args(d=96)) == 2
+    assert call(args(dm=100)) == 2
+    assert call(args(k=5)) == 1
+    assert call(args(wq=None)) == 1
+    assert call(args(lab=None)) == 1
+    assert call(args(ws=None)) == 3
+    assert H.aoh_label_workspace(1, 4, 4, 256, 64) > 0
+
+
+def test_status_strings_and_row_elems():
+    assert H.status_string(0) == "HAS_OK" and H.status_string(4) == "HAS_ERR_HIP"
+    assert H.kdom_row_elems(_dims()) == 32
+    assert H.kdom_row_elems(_dims(n_dom=12)) == 32   # 24 bf16 -> padded to 4 vectors
+    assert H.kdom_row_elems(_dims(n_dom=1)) == 8
+    assert H.kdom_row_elems(_dims(n_dom=8, kv_dtype=H.HAS_F32)) == 16

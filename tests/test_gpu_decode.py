@@ -1,0 +1,155 @@
+"""GPU parity of sparse_decode_step (through the C ABI) against the fp64 oracle.
+
+Bars (the required agreement for this path): index sets identical except for
+tokens whose fp64 TIP score lies within 1e-5 relative of the n_fac-th score;
+outputs within 2e-3 absolute + 1e-2 relative (bf16 or fp32 inputs, fp32
+accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+import head_aware_sparse_amd as H
+from synth import recipe as R
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_items(case, items, tag):
+    cfg, hi = case.cfg, case.hi
+    out, idx, _ = case.run()
+    for (l, b, g) in items:
+        ref, ridx, scores = U.oracle_item(cfg, hi, case.labels_np, l, b, g)
+        G = cfg.group
+        U.check_out(out[l, b, g * G:(g + 1) * G], ref, f"{tag} out l{l} b{b} g{g}")
+        if case.labels_np[l, g]:
+            U.check_index_set(idx[l, b, g], scores, cfg.n_fac, f"{tag} idx l{l} b{b} g{g}")
+        else:
+            assert (idx[l, b, g] == -1).all(), f"{tag} streaming idx l{l} b{b} g{g}"
+    return out, idx
+
+
+def _all_items(cfg):
+    return [(l, b, g) for l in range(cfg.n_layers) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
+
+
+def test_c0_tiny_fp32_all_items():
+    cfg = R.get_config("c0")
+    print(f"case c0 {cfg}", flush=True)
+    case = U.DeviceCase(cfg)
+    _check_items(case, _all_items(cfg), "c0")
+
+
+def test_c1_llama_layer_32k_all_items():
+    cfg = R.get_config("c1")
+    print(f"case c1 {cfg}", flush=True)
+    case = U.DeviceCase(cfg)
+    out, idx = _check_items(case, _all_items(cfg), "c1")
+    # the planted needles are selected
+    for (l, g) in R.planted_groups(cfg):
+        assert np.isin(R.needle_positions(cfg, l, 0, g), idx[l, 0, g]).all()
+
+
+def test_c2_batch16_32k_all_items():
+    cfg = R.get_config("c2")
+    print(f"case c2 {cfg}", flush=True)
+    case = U.DeviceCase(cfg)
+    _check_items(case, _all_items(cfg), "c2")
+
+
+@pytest.mark.parametrize("over", [
+    dict(ctx_len=5000, n_fac=777, window=300, n_sink=3),            # ragged chunks everywhere
+    dict(ctx_len=3000, n_fac=3000, window=100),                     # every token selected
+    dict(ctx_len=2500, n_fac=1, window=4000, n_sink=0),             # one token; window covers all
+    dict(ctx_len=1200, n_fac=64, window=0, n_sink=7),               # sink only
+    dict(ctx_len=4096, n_fac=300, n_dom=64),                        # all chunks: exact logits
+    dict(ctx_len=4096, n_fac=300, n_dom=1),                         # one chunk
+], ids=["ragged", "all", "one", "sink-only", "ndom64", "ndom1"])
+def test_edge_shapes_bf16(over):
+    cfg = R.get_config("c1", **over)
+    print(f"case edge {over}", flush=True)
+    case = U.DeviceCase(cfg)
+    _check_items(case, _all_items(cfg), f"edge {over}")
+
+
+@pytest.mark.parametrize("over", [
+    dict(n_q_heads=8, n_kv_heads=8, ctx_len=3000, n_fac=200, batch=2),     # G = 1
+    dict(n_q_heads=16, n_kv_heads=8, ctx_len=3000, n_fac=200, batch=2),    # G = 2
+    dict(n_q_heads=64, n_kv_heads=8, ctx_len=3000, n_fac=200, batch=2),    # G = 8
+    dict(d_head=64, n_dom=8, ctx_len=3000, n_fac=200, batch=2),            # d = 64 bf16
+], ids=["G1", "G2", "G8", "d64"])
+def test_group_and_head_sizes(over):
+    cfg = R.get_config("c1", **over)
+    print(f"case heads {over}", flush=True)
+    case = U.DeviceCase(cfg)
+    _check_items(case, _all_items(cfg), f"heads {over}")
+
+
+def test_fp32_d128():
+    cfg = R.get_config("c1", kv_dtype="f32", ctx_len=3000, n_fac=250, batch=2)
+    print("case f32 d128", flush=True)
+    case = U.DeviceCase(cfg)
+    _check_items(case, _all_items(cfg), "f32 d128")
+
+
+def test_label_extremes():
+    cfg = R.get_config("c1", ctx_len=4000, n_fac=500, batch=2)
+    for name, lab in [("all-retrieval", np.ones((1, 8), np.uint8)), ("all-streaming", np.zeros((1, 8), np.uint8))]:
+        print(f"case labels {name}", flush=True)
+        case = U.DeviceCase(cfg, labels=lab)
+        _check_items(case, _all_items(cfg), name)
+
+
+def test_degenerate_all_scores_equal():
+    """Zero queries: every TIP score is 0, the selection is the first n_fac
+    tokens (ties to the lower index) and attention is uniform over them."""
+    cfg = R.get_config("c1", ctx_len=20000, n_fac=1500, batch=1)
+    print("case zero-q", flush=True)
+    case = U.DeviceCase(cfg, zero_q=True)
+    out, idx = _check_items(case, _all_items(cfg), "zero-q")
+    for (l, g) in R.planted_groups(cfg):
+        assert idx[l, 0, g].tolist() == list(range(cfg.n_fac))
+
+
+def test_deterministic_and_idx_optional():
+    cfg = R.get_config("c1", ctx_len=8192, n_fac=1024, batch=4)
+    print("case determinism", flush=True)
+    case = U.DeviceCase(cfg)
+    o1, i1, ws = case.run()
+    o2, i2, _ = case.run(ws=ws)
+    assert (o1 == o2).all() and (i1 == i2).all()
+    o3, _, _ = case.run(idx=False, ws=ws)
+    assert (o1 == o3).all()
+    # another stream gives the same bits
+    s = torch.cuda.Stream()
+    out = torch.empty_like(torch.from_numpy(o1)).cuda()
+    with torch.cuda.stream(s):
+        H.sparse_decode_step(case.dims, case.q, case.k, case.v, case.k_dom, case.i_dom, case.labels, out, None,
+                             ws=ws, stream=s)
+    s.synchronize()
+    assert (out.cpu().numpy() == o1).all()
+
+
+def test_kdom_pack_matches_channels():
+    cfg = R.get_config("c1", ctx_len=3000, batch=2)
+    case = U.DeviceCase(cfg)
+    kd = case.k_dom.cpu().float().numpy()
+    k = case.k.cpu().float().numpy()
+    d2 = cfg.d_head // 2
+    for (l, b, g) in [(0, 0, 0), (0, 1, 5)]:
+        f = case.hi.i_dom[l, g]
+        want = np.stack([k[l, b, g][:, f], k[l, b, g][:, f + d2]], axis=-1).reshape(cfg.ctx_len, -1)
+        assert (kd[l, b, g][:, :2 * cfg.n_dom] == want).all()
+        assert (kd[l, b, g][:, 2 * cfg.n_dom:] == 0).all()
+
+
+def test_device_fill_equals_host_generator():
+    cfg = R.get_config("c1", ctx_len=4096, batch=2)
+    case = U.DeviceCase(cfg)
+    k = case.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    v = case.v.view(torch.int16).cpu().numpy().view(np.uint16)
+    l, g = R.planted_groups(cfg)[0]
+    for b in range(2):
+        assert (k[l, b, g] == case.hi.rows("k", l, b, g)).all()
+        assert (v[l, b, g] == case.hi.rows("v", l, b, g)).all()
+    assert (k[0, 1, 0] == case.hi.rows("k", 0, 1, 0)).all()
