@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the head-aware sparse decode step on one MI355X.
+
+Default workload: the full 32-layer Llama-3-8B-shaped pipeline at 128K
+context -- one sparse_decode_step over 32 layers x batch 4 x 8 KV groups
+(64 of the 256 (layer, group) pairs retrieval: TIP over 16 of 64 frequency
+chunks + top-4096 + focused attention; the rest sink 4 + window 2048), bf16
+cache of 131072 tokens (68.7 GB resident).  A step is one call of the whole
+decode path (plan, scoring, selection, attention, merge) over that batch.
+The offline AoH labeller that produces the labels (aoh_label over the
+32 x 40 heads) and the cache-write-time dominant-key packing are timed
+separately and reported in the same line.
+
+Prints ONE JSON line.  Inputs are seeded synthetic data (synth package),
+resident in HBM before timing starts.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode-attn steps/s at 32K & 128K ctx; achieved HBM TB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, labels):
+    """Bytes the method must move per step (counted once): dominant key
+    channels of retrieval items, selected K+V rows, sink+window K+V rows,
+    queries and outputs.  Scores, histograms and partials are not counted."""
+    import numpy as np
+    es = 2 if cfg.bf16 else 4
+    d, T = cfg.d_head, cfg.ctx_len
+    row = 2 * d * es
+    s_end = min(cfg.n_sink, T)
+    n_srows = s_end + T - max(T - cfg.window, s_end)
+    if cfg.clsa:
+        n_idx = cfg.batch * cfg.n_kv_heads
+        n_ret_att = int(labels.sum()) * cfg.batch if labels is not None else cfg.n_layers * n_idx
+        n_str_att = cfg.n_layers * n_idx - n_ret_att
+        tip = n_idx * T * 2 * cfg.n_dom * es
+        gather = n_idx * cfg.n_fac * row          # one gather serves every layer
+        stream = (n_srows * row * cfg.batch * cfg.n_kv_heads) if n_str_att else 0
+    else:
+        n_ret = int(np.asarray(labels).sum()) * cfg.batch
+        n_str = cfg.n_layers * cfg.batch * cfg.n_kv_heads - n_ret
+        tip = n_ret * T * 2 * cfg.n_dom * es
+        gather = n_ret * cfg.n_fac * row
+        stream = n_str * n_srows * row
+    qo = cfg.n_layers * cfg.batch * cfg.n_q_heads * d * (es + 4)
+    return {"tip": tip, "gather": gather, "stream": stream, "q_out": qo, "total": tip + gather + stream + qo}
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken from the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}.counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, rec["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec.get("source_sha256"):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(cfg, hi, labels, n_ret_sample, n_str_sample):
+    """fp64 oracle on a bounded sample of the step's items, scaled to the
+    whole step (input generation excluded from the timing)."""
+    import numpy as np
+    from oracle import fasa
+    from synth import recipe as R
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    G = cfg.group
+    ret = [(l, g) for l in range(cfg.n_layers) for g in range(cfg.n_kv_heads) if labels[l, g]]
+    strm = [(l, g) for l in range(cfg.n_layers) for g in range(cfg.n_kv_heads) if not labels[l, g]]
+    rng = np.random.default_rng(7)
+    t_ret, t_str = [], []
+    for pool, n, acc in [(ret, n_ret_sample, t_ret), (strm, n_str_sample, t_str)]:
+        if not pool:
+            continue
+        for i in rng.choice(len(pool), size=min(n, len(pool)), replace=False):
+            l, g = pool[i]
+            b = int(rng.integers(cfg.batch))
+            k = R.storage_to_f64(hi.rows("k", l, b, g), cfg.bf16)
+            v = R.storage_to_f64(hi.rows("v", l, b, g), cfg.bf16)
+            q = R.storage_to_f64(hi.q[l, b, g * G:(g + 1) * G], cfg.bf16)
+            t0 = time.perf_counter()
+            fasa.decode_group(q, k, v, hi.i_dom[l, g], bool(labels[l, g]), cfg.n_fac, cfg.n_sink, cfg.window)
+            acc.append(time.perf_counter() - t0)
+    n_ret_items = len(ret) * cfg.batch
+    n_str_items = len(strm) * cfg.batch
+    step_s = (np.mean(t_ret) if t_ret else 0.0) * n_ret_items + (np.mean(t_str) if t_str else 0.0) * n_str_items
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{len(t_ret)} retrieval + {len(t_str)} streaming (layer, sequence, KV group) items of "
+                       f"the step timed with the fp64 numpy oracle ({sum(t_ret) + sum(t_str):.1f} s of CPU work), "
+                       f"scaled to {n_ret_items} + {n_str_items} items")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-label", action="store_true")
+    ap.add_argument("--cpu-sample", default="24,72", help="retrieval,streaming items timed on the CPU")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the decode path on one GPU only; --gpus above 1 is not supported "
+              "(the per-(layer, sequence, KV group) work items would shard across GPUs with no exchange; "
+              "see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import head_aware_sparse_amd as H
+    from synth import device as sdev
+    from synth import recipe as R
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = R.get_config(args.config)
+    log(f"config {cfg}")
+    t0 = time.time()
+    hi = R.HostInputs(cfg, with_weights=(cfg.d_model > 0 and not args.no_label))
+    dims = H.DecodeDims(cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.d_head, cfg.ctx_len, cfg.n_fac,
+                        cfg.n_sink, cfg.window, cfg.n_dom, H.HAS_BF16 if cfg.bf16 else H.HAS_F32, 0)
+    kd_dims = H.DecodeDims(*[getattr(dims, f) for f, _ in dims._fields_])
+    kd_dims.n_layers = cfg.kv_layers
+    q = sdev.to_device(hi.q, "cuda", cfg.bf16)
+    k = sdev.kv_cache(cfg, "k", hi)
+    v = sdev.kv_cache(cfg, "v", hi)
+    i_dom = torch.from_numpy(hi.i_dom).cuda()
+    kd = torch.empty((cfg.kv_layers, cfg.batch, cfg.n_kv_heads, cfg.ctx_len, H.kdom_row_elems(kd_dims)),
+                     dtype=k.dtype, device="cuda")
+    log(f"inputs resident ({(k.numel() + v.numel()) * k.element_size() / 1e9:.1f} GB cache) in {time.time() - t0:.1f}s")
+
+    # cache-write-time packing of the dominant key channels (timed separately)
+    H.timing_enable(True)
+    for _ in range(3):
+        H.kdom_pack(kd_dims, k, i_dom, kd)
+    torch.cuda.synchronize()
+    kp = H.timing_collect()
+    H.timing_enable(False)
+    kdom_ms = kp["kdom_pack"][0] / kp["kdom_pack"][1]
+
+    # labels: the offline AoH labeller on the model weights (timed separately)
+    label_info = None
+    labels_np = hi.labels
+    if cfg.d_model and not args.no_label:
+        wq = sdev.to_device(hi.w_q, "cuda", cfg.bf16)
+        wk = sdev.to_device(hi.w_k, "cuda", cfg.bf16)
+        lab_d = torch.empty((cfg.n_layers, cfg.n_kv_heads), dtype=torch.uint8, device="cuda")
+        erh = torch.empty((cfg.n_layers, cfg.n_q_heads), dtype=torch.float32, device="cuda")
+        erg = torch.empty((cfg.n_layers, cfg.n_kv_heads), dtype=torch.float32, device="cuda")
+        ws_l = H.aoh_label(wq, wk, cfg.n_q_heads, cfg.n_kv_heads, cfg.d_head, lab_d, cfg.n_retrieval,
+                           er_head=erh, er_group=erg)
+        torch.cuda.synchronize()
+        H.timing_enable(True)
+        n_lab = 3
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(n_lab):
+            H.aoh_label(wq, wk, cfg.n_q_heads, cfg.n_kv_heads, cfg.d_head, lab_d, cfg.n_retrieval, er_head=erh,
+                        er_group=erg, ws=ws_l)
+        ev1.record()
+        torch.cuda.synchronize()
+        lk = H.timing_collect()
+        H.timing_enable(False)
+        labels_np = lab_d.cpu().numpy()
+        w_bytes = (wq.numel() + wk.numel()) * wq.element_size()
+        gram_ms = lk["gram"][0] / lk["gram"][1]
+        gram_flop = 2.0 * (cfg.n_layers * (cfg.n_q_heads + cfg.n_kv_heads)) * cfg.d_head ** 2 * cfg.d_model
+        label_info = {
+            "ms": ev0.elapsed_time(ev1) / n_lab,
+            "kernels_ms": {n: round(t / c, 4) for n, (t, c) in lk.items()},
+            "gram_hbm_GBps": round(w_bytes / (gram_ms * 1e-3) / 1e9, 1),
+            "gram_hbm_frac": round(w_bytes / (gram_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "gram_mfma_util": round(gram_flop / (gram_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "labels_match_planted": bool((labels_np == hi.labels).all()),
+            "n_retrieval": int(labels_np.sum()),
+        }
+        del wq, wk
+        log(f"labeller {label_info}")
+    labels = torch.from_numpy(np.ascontiguousarray(labels_np)).cuda()
+
+    out = torch.empty((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), dtype=torch.float32, device="cuda")
+    if cfg.clsa:
+        ws = H.shared_index_decode(dims, q, k, v, kd, i_dom, out, labels=None)
+
+        def step():
+            H.shared_index_decode(dims, q, k, v, kd, i_dom, out, labels=None, ws=ws)
+    else:
+        ws = H.sparse_decode_step(dims, q, k, v, kd, i_dom, labels, out)
+
+        def step():
+            H.sparse_decode_step(dims, q, k, v, kd, i_dom, labels, out, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel durations (HIP events on the launch stream)
+    H.timing_enable(True)
+    n_prof = max(5, min(args.steps, 20))
+    for _ in range(n_prof):
+        step()
+    torch.cuda.synchronize()
+    kt = H.timing_collect()
+    H.timing_enable(False)
+    kernels_ms = {n: t / c for n, (t, c) in kt.items()}
+
+    # the timed region
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"{args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
+
+    ab = algorithmic_bytes(cfg, None if cfg.clsa else labels_np)
+    tip_ms = kernels_ms["tip_score"]
+    tip_gbps = ab["tip"] / (tip_ms * 1e-3) / 1e9
+    n_scored = (cfg.batch * cfg.n_kv_heads if cfg.clsa else int(labels_np.sum()) * cfg.batch) * cfg.ctx_len
+    key = f"tip_score_{cfg.name}"
+    roofline = {"kernel": "tip_score", "bound": "hbm", "achieved": round(tip_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(tip_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(key),
+                "algorithmic_bytes_per_launch": ab["tip"], "avg_launch_ms": round(tip_ms, 5)}
+    res = {
+        "metric": METRIC,
+        "value": round(1e3 / ms, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.bf16 else "f32",
+        "data": "synthetic (seeded Philox4x32-10 inputs shaped like the pages' workloads)",
+        "config": {"workload": {
+            "c1": "single Llama-3-8B-shaped layer, batch 1, ctx 32768, 2 of 8 KV groups retrieval",
+            "c2": "single Llama-3-8B-shaped layer, batch 16, ctx 32768, 2 of 8 KV groups retrieval",
+            "c3": "CLSA: 8 layers sharing one KV cache, batch 4, ctx 131072, one shared top-2048 index",
+            "c4": "32-layer Llama-3-8B-shaped sparse decode step, batch 4, ctx 131072, 64 of 256 (layer, KV "
+                  "group) pairs retrieval"}[cfg.name],
+            "name": cfg.name, "layers": cfg.n_layers, "batch": cfg.batch, "ctx_len": cfg.ctx_len,
+            "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "d_head": cfg.d_head, "n_dom": cfg.n_dom,
+            "n_fac": cfg.n_fac, "n_sink": cfg.n_sink, "window": cfg.window},
+        "roofline": roofline,
+        "step_algorithmic_bytes": ab,
+        "step_hbm_GBps": round(ab["total"] / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "tokens_scored_per_s": round(n_scored / (ms * 1e-3), 1),
+        "kernels_ms": {n: round(t, 5) for n, t in kernels_ms.items()},
+        "kdom_pack_ms": round(kdom_ms, 4),
+        "label": label_info,
+    }
+    if not args.no_cpu_baseline and not cfg.clsa:
+        nr, ns = (int(x) for x in args.cpu_sample.split(","))
+        log("timing the CPU oracle on a sample of the step")
+        res["cpu_baseline"] = cpu_baseline(cfg, hi, labels_np, nr, ns)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,4 +21,6 @@ from .binding import (  # noqa: F401
     sparse_decode_step,
     sparse_decode_workspace,
     status_string,
+    timing_collect,
+    timing_enable,
 )

@@ -216,3 +216,26 @@ def aoh_label(w_q, w_k, n_q_heads, n_kv_heads, d_head, labels, n_retrieval=-1, e
                            float(er_threshold), _ptr(er_head), _ptr(er_group), _ptr(labels), _ptr(ws), ws.numel(),
                            _stream(stream)))
     return ws
+
+
+def timing_enable(on=True):
+    L = lib()
+    L.has_timing_enable.argtypes = [ctypes.c_int]
+    L.has_timing_enable.restype = ctypes.c_int
+    _check(L.has_timing_enable(1 if on else 0))
+
+
+def timing_collect(max_kernels=32):
+    """{kernel name: (total_ms, launches)} of the launches recorded since the
+    last collect."""
+    L = lib()
+    L.has_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int), ctypes.c_int]
+    L.has_timing_collect.restype = ctypes.c_int
+    names = (ctypes.c_char_p * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int * max_kernels)()
+    n = L.has_timing_collect(names, ms, cnt, max_kernels)
+    if n < 0:
+        raise HasError(4, last_error())
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(n)}

@@ -6,6 +6,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/has.h"
 #include "internal.h"
@@ -218,9 +220,86 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
   return ok();
 }
 
+// Per-kernel event timing (diagnostics).
+struct TimerRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimerRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
 
+namespace has {
+
+KTimer::KTimer(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing) return;
+  TimerRec r{name, take_event(), take_event()};
+  if (!r.a || !r.b) return;
+  if (hipEventRecord(r.a, s) != hipSuccess) return;
+  slot = (int)g_recs.size();
+  g_recs.push_back(r);
+}
+
+KTimer::~KTimer() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (slot < (int)g_recs.size()) hipEventRecord(g_recs[slot].b, stream);
+}
+
+}  // namespace has
+
 extern "C" {
+
+has_status has_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = on != 0;
+  return ok();
+}
+
+int has_timing_collect(const char** names, double* total_ms, int* launches, int max) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  int n = 0;
+  int rc = 0;
+  for (const TimerRec& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) rc = -1;
+    int k = 0;
+    while (k < n && strcmp(names[k], r.name) != 0) ++k;
+    if (k == n && n < max) {
+      names[n] = r.name;
+      total_ms[n] = 0.0;
+      launches[n] = 0;
+      ++n;
+    }
+    if (k < n) {
+      total_ms[k] += ms;
+      launches[k] += 1;
+    }
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  if (rc < 0) {
+    fail(HAS_ERR_HIP, "timing events failed");
+    return -1;
+  }
+  return n;
+}
 
 const char* has_status_string(has_status s) {
   switch (s) {

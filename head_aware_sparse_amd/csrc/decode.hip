@@ -747,6 +747,7 @@ hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s) {
   const int n_slices = g.Lkv * g.B * g.Hkv;
   const uint32_t per = (uint32_t)g.T * (uint32_t)g.R;
   const dim3 grid(clampi(((long long)per + NT - 1) / NT, 1, 2048), n_slices);
+  KTimer t("kdom_pack", s);
   if (g.bf16)
     kdom_pack_kernel<uint16_t><<<grid, NT, 0, s>>>(g, (uint16_t*)k_dom);
   else
@@ -759,26 +760,47 @@ hipError_t launch_decode(const Geo& g, hipStream_t s) {
   const long long n_idx_items = (long long)(g.clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att_items = (long long)g.Lq * g.Hkv * g.B;
   const int grid_plan = clampi((n_idx_items * kHistBins / 4 + NT - 1) / NT, 1, g.grid);
-  plan_kernel<<<grid_plan, NT, 0, s>>>(g);
+  {
+    KTimer t("plan", s);
+    plan_kernel<<<grid_plan, NT, 0, s>>>(g);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int grid_tip = clampi(n_idx_items * g.nch_t, 1, g.grid);
-  e = g.bf16 ? launch_tip_v<uint16_t>(g, grid_tip, s) : launch_tip_v<float>(g, grid_tip, s);
+  {
+    KTimer t("tip_score", s);
+    e = g.bf16 ? launch_tip_v<uint16_t>(g, grid_tip, s) : launch_tip_v<float>(g, grid_tip, s);
+  }
   if (e != hipSuccess) return e;
-  select_a_kernel<<<grid_tip, NT, 0, s>>>(g);
+  {
+    KTimer t("select_a", s);
+    select_a_kernel<<<grid_tip, NT, 0, s>>>(g);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  select_b_kernel<<<clampi(n_idx_items, 1, g.grid), NT, 0, s>>>(g);
+  {
+    KTimer t("select_b", s);
+    select_b_kernel<<<clampi(n_idx_items, 1, g.grid), NT, 0, s>>>(g);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  select_c_kernel<<<grid_tip, NT, 0, s>>>(g);
+  {
+    KTimer t("select_c", s);
+    select_c_kernel<<<grid_tip, NT, 0, s>>>(g);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long max_units = n_att_items * (long long)(g.nch_f > g.nch_s ? g.nch_f : g.nch_s);
   const int grid_attn = clampi(max_units, 1, g.grid);
-  if (g.bf16)
-    e = g.d == 128 ? launch_attn_g<uint16_t, 128>(g, grid_attn, s) : launch_attn_g<uint16_t, 64>(g, grid_attn, s);
-  else
-    e = g.d == 128 ? launch_attn_g<float, 128>(g, grid_attn, s) : launch_attn_g<float, 64>(g, grid_attn, s);
+  {
+    KTimer t("attention", s);
+    if (g.bf16)
+      e = g.d == 128 ? launch_attn_g<uint16_t, 128>(g, grid_attn, s) : launch_attn_g<uint16_t, 64>(g, grid_attn, s);
+    else
+      e = g.d == 128 ? launch_attn_g<float, 128>(g, grid_attn, s) : launch_attn_g<float, 64>(g, grid_attn, s);
+  }
   if (e != hipSuccess) return e;
   const long long n_out = n_att_items * g.G * g.d;
-  merge_kernel<<<clampi((n_out + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
+  {
+    KTimer t("merge", s);
+    merge_kernel<<<clampi((n_out + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 

@@ -54,6 +54,15 @@ struct Geo {
 
 inline __host__ __device__ int plan_idx_pairs(const int* p) { return p[0]; }
 
+// Brackets one kernel launch with HIP events on its stream while per-kernel
+// timing is enabled (has_timing_enable); a no-op otherwise.
+struct KTimer {
+  KTimer(const char* name, hipStream_t s);
+  ~KTimer();
+  int slot;
+  hipStream_t stream;
+};
+
 hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s);
 hipError_t launch_decode(const Geo& g, hipStream_t s);
 

@@ -170,7 +170,8 @@ __device__ __forceinline__ double wave_sum_d(double x) {
 }
 
 // MFMA f64 16x16x4: A element (lane%16, lane/16), B element (lane/16,
-// lane%16); output (4*(lane/16) + r, lane%16) in register r.
+// lane%16); output (4*r + lane/16, lane%16) in register r (checked on the
+// device: unlike the fp32 16x16 forms, rows interleave across lane groups).
 template <int D>
 __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
   constexpr int LD = D + 1;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
     for (int c = 0; c < CB; ++c)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        T[(size_t)((wave * RB + a) * 16 + 4 * (lane >> 4) + r) * D + c * 16 + (lane & 15)] = acc[a][c][r];
+        T[(size_t)((wave * RB + a) * 16 + 4 * r + (lane >> 4)) * D + c * 16 + (lane & 15)] = acc[a][c][r];
   __threadfence();
   __syncthreads();
 
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
     for (int c = 0; c < CB; ++c)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        A[((wave * RB + a) * 16 + 4 * (lane >> 4) + r) * LD + c * 16 + (lane & 15)] = acc[a][c][r];
+        A[((wave * RB + a) * 16 + 4 * r + (lane >> 4)) * LD + c * 16 + (lane & 15)] = acc[a][c][r];
   __syncthreads();
   for (int e = tid; e < D * D; e += NT) {
     const int i = e / D, j = e - i * D;
@@ -475,21 +476,33 @@ hipError_t launch_label(const LabelArgs& a, hipStream_t s) {
   g.labels = a.labels;
   const int n_mats = a.L * a.Hq + a.L * a.Hkv;
   const int n_heads = a.L * a.Hq;
-  if (a.d == 128) {
-    if (a.bf16) gram_kernel<uint16_t, 128><<<n_mats, NT, 0, s>>>(g);
-    else gram_kernel<float, 128><<<n_mats, NT, 0, s>>>(g);
-    spectrum_kernel<128><<<n_heads, NT, 0, s>>>(g);
-    bisect_kernel<128><<<n_heads, 128, 0, s>>>(g);
-  } else {
-    if (a.bf16) gram_kernel<uint16_t, 64><<<n_mats, NT, 0, s>>>(g);
-    else gram_kernel<float, 64><<<n_mats, NT, 0, s>>>(g);
-    spectrum_kernel<64><<<n_heads, NT, 0, s>>>(g);
-    bisect_kernel<64><<<n_heads, 64, 0, s>>>(g);
+  {
+    KTimer t("gram", s);
+    if (a.d == 128) {
+      if (a.bf16) gram_kernel<uint16_t, 128><<<n_mats, NT, 0, s>>>(g);
+      else gram_kernel<float, 128><<<n_mats, NT, 0, s>>>(g);
+    } else {
+      if (a.bf16) gram_kernel<uint16_t, 64><<<n_mats, NT, 0, s>>>(g);
+      else gram_kernel<float, 64><<<n_mats, NT, 0, s>>>(g);
+    }
+  }
+  {
+    KTimer t("spectrum", s);
+    if (a.d == 128) spectrum_kernel<128><<<n_heads, NT, 0, s>>>(g);
+    else spectrum_kernel<64><<<n_heads, NT, 0, s>>>(g);
+  }
+  {
+    KTimer t("bisect", s);
+    if (a.d == 128) bisect_kernel<128><<<n_heads, 128, 0, s>>>(g);
+    else bisect_kernel<64><<<n_heads, 64, 0, s>>>(g);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int P = a.L * a.Hkv;
-  finalize_kernel<<<(P + NT - 1) / NT, NT, 0, s>>>(g);
+  {
+    KTimer t("finalize", s);
+    finalize_kernel<<<(P + NT - 1) / NT, NT, 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 

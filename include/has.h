@@ -80,7 +80,9 @@ const char* has_last_error(void);
  * [n_layers, n_kv_heads] uint8 is required.
  * Supported: d_head in {64, 128}, d_model a multiple of 64, d_model >= d_head,
  * 0 <= n_retrieval <= n_layers*n_kv_heads (or < 0 for the threshold).
- * Eigenvalues are computed in fp32 (Gram products on the matrix cores). */
+ * Precision: the Gram products W W^T accumulate in fp32 on the matrix
+ * cores; the Cholesky factor, the congruence L^T G_Q L (fp64 matrix cores)
+ * and the tridiagonalisation run in fp64; eigenvalue bisection in fp32. */
 size_t aoh_label_workspace(int n_layers, int n_q_heads, int n_kv_heads, int d_model, int d_head);
 has_status aoh_label(int n_layers, int n_q_heads, int n_kv_heads, int d_model, int d_head,
                      has_dtype wdt, const void* w_q, const void* w_k, int n_retrieval,
@@ -94,7 +96,7 @@ has_status aoh_label(int n_layers, int n_q_heads, int n_kv_heads, int d_model, i
  *   n_q_heads % n_kv_heads == 0, G = n_q_heads / n_kv_heads in {1,2,4,8}
  *   d_head in {64, 128}; 1 <= n_dom <= d_head/2
  *   1 <= n_fac <= ctx_len; n_sink >= 0, window >= 0, n_sink + window >= 1
- *   n_fac <= 65536, ctx_len <= 2^30
+ *   ctx_len <= 4194304; n_layers * n_kv_heads <= 8192
  */
 typedef struct has_decode_dims {
   int n_layers;
@@ -168,6 +170,16 @@ has_status shared_index_decode(const has_decode_dims* dims, const void* q, const
                                const void* k_cache, const void* v_cache, const void* k_dom,
                                const int32_t* i_dom, const uint8_t* labels, float* out,
                                int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------- diagnostics --
+ * Per-kernel device time.  While enabled (process-wide), every kernel the
+ * library launches is bracketed by HIP events recorded on the caller's
+ * stream.  has_timing_collect waits for the recorded events, writes up to
+ * `max` entries (kernel name -- a static string --, summed milliseconds,
+ * launch count), clears the records and returns the number of entries, or
+ * -1 if a HIP event call failed. */
+has_status has_timing_enable(int on);
+int has_timing_collect(const char** names, double* total_ms, int* launches, int max);
 
 #ifdef __cplusplus
 }
