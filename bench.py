@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-label", action="store_true")
     ap.add_argument("--cpu-sample", default="24,72", help="retrieval,streaming items timed on the CPU")
+    ap.add_argument("--calib-bytes", type=int, default=1 << 30,
+                    help="size of the reference copy kernel (torch.neg, fp32) timed beside the step")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -153,6 +155,22 @@ def main():
     kd = torch.empty((cfg.kv_layers, cfg.batch, cfg.n_kv_heads, cfg.ctx_len, H.kdom_row_elems(kd_dims)),
                      dtype=k.dtype, device="cuda")
     log(f"inputs resident ({(k.numel() + v.numel()) * k.element_size() / 1e9:.1f} GB cache) in {time.time() - t0:.1f}s")
+
+    # reference: a plain elementwise copy of known size (reads and writes
+    # calib-bytes each); its rate is the measured stream bandwidth, and under
+    # rocprofv3 its FETCH_SIZE/WRITE_SIZE calibrate the counters
+    cal_x = torch.ones(args.calib_bytes // 4, dtype=torch.float32, device="cuda")
+    cal_y = torch.empty_like(cal_x)
+    torch.neg(cal_x, out=cal_y)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        torch.neg(cal_x, out=cal_y)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * args.calib_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cal_x, cal_y
 
     # cache-write-time packing of the dominant key channels (timed separately)
     H.timing_enable(True)
@@ -279,6 +297,7 @@ def main():
         "tokens_scored_per_s": round(n_scored / (ms * 1e-3), 1),
         "kernels_ms": {n: round(t, 5) for n, t in kernels_ms.items()},
         "kdom_pack_ms": round(kdom_ms, 4),
+        "measured_copy_GBps": round(copy_gbps, 1),
         "label": label_info,
     }
     if not args.no_cpu_baseline and not cfg.clsa:

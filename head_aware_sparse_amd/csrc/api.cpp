@@ -9,7 +9,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/has.h"
+#include "has.h"
 #include "internal.h"
 #include "label.h"
 
@@ -117,6 +117,7 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   g.ct = clampi(pow2_floor((long long)g.T * n_idx / 1024), 256, 4096);
   while ((g.T + g.ct - 1) / g.ct > has::kMaxTipChunks && g.ct < 4096) g.ct *= 2;
   g.nch_t = (g.T + g.ct - 1) / g.ct;
+  g.Ts = (g.T + 63) / 64 * 64;
   g.cf = clampi(pow2_floor((long long)g.n_fac * n_att / 2048), 128, has::kMaxChunkRows);
   g.nch_f = (g.n_fac + g.cf - 1) / g.cf;
   g.s_end = g.n_sink < g.T ? g.n_sink : g.T;
@@ -139,7 +140,7 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   L.off_ngt = take((size_t)n_idx * g.nch_t * 4);
   L.off_off = take((size_t)n_idx * g.nch_t * 4);
   L.off_thr = take((size_t)n_idx * 8);
-  L.off_scores = take((size_t)n_idx * g.T * 4);
+  L.off_scores = take((size_t)n_idx * g.Ts * 4);
   L.off_idx = take((size_t)n_idx * g.n_fac * 4);
   L.off_part = take((size_t)n_att * g.nparts * g.G * (g.d + 4) * 4);
   L.bytes = o;

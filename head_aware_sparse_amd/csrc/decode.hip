@@ -12,7 +12,8 @@
 // Launch sequence (all on the caller's stream, no host synchronisation):
 //   plan      labels -> work lists; clears histograms and counters
 //   tip       scores s_t (fp32) + per-item histogram of the top 11 key bits
-//   select_a  per chunk: count above the threshold bin, collect candidates
+//   select_bin per item: the first-digit bin that holds the n_fac-th score
+//   select_a  per chunk: count above that bin, collect the bin's candidates
 //   select_b  per item: exact threshold (key*, token*) by radix refinement
 //   select_c  per chunk: ordered compaction -> ascending token indices
 //   attn      per (item, chunk of rows): scores, softmax partial, P.V
@@ -217,6 +218,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(Geo g) {
 template <typename E, int V>
 __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
   constexpr int EPV = Vec<E>::N;
+  constexpr int U = V >= 8 ? 1 : 8 / V;  // 64-token steps in flight per wave
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ float s_q[V * EPV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -253,30 +255,35 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
     for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
     const size_t slice = ((size_t)l * g.B + b) * g.Hkv + gi;
     const E* kd = (const E*)g.kdom + slice * (size_t)g.T * R;
-    float* sc = g.scores + (size_t)item * g.T;
+    float* sc = g.scores + (size_t)item * g.Ts;
     const int t0 = ch * g.ct, t1 = min(g.T, t0 + g.ct);
-    for (int base = t0 + wave * 64; base < t1; base += NT) {
-      uint4 raw[V];
+    for (int base = t0 + wave * 64; base < t1; base += NT * U) {
+      uint4 raw[U][V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const int tok = base + i * (64 / V) + lane / V;
-        raw[i] = tok < t1 ? ld16(kd + (size_t)tok * R + (lane % V) * EPV) : make_uint4(0, 0, 0, 0);
-      }
-      float mine = 0.f;
+      for (int j = 0; j < U; ++j)
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        float kv[EPV];
-        Vec<E>::cvt(raw[i], kv);
-        float s = 0.f;
+        for (int i = 0; i < V; ++i) {
+          const int tok = base + j * NT + i * (64 / V) + lane / V;
+          raw[j][i] = tok < t1 ? ld16(kd + (size_t)tok * R + (lane % V) * EPV) : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) s += qr[e] * kv[e];
-        s = group_sum<V>(s);
-        if ((lane % V) == i) mine = s;
-      }
-      const int tok = base + (lane % V) * (64 / V) + lane / V;
-      if (tok < t1) {
-        sc[tok] = mine;
-        atomicAdd(&s_hist[f2key(mine) >> 21], 1u);
+      for (int j = 0; j < U; ++j) {
+        float mine = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float kv[EPV];
+          Vec<E>::cvt(raw[j][i], kv);
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) s += qr[e] * kv[e];
+          s = group_sum<V>(s);
+          if ((lane % V) == i) mine = s;
+        }
+        const int tok = base + j * NT + (lane % V) * (64 / V) + lane / V;
+        if (tok < t1) {
+          sc[tok] = mine;
+          atomicAdd(&s_hist[f2key(mine) >> 21], 1u);
+        }
       }
     }
     __syncthreads();
@@ -292,13 +299,34 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
 }
 
 // ------------------------------------------------------------------ select
-// select_a: threshold bin b1 of the item (from its histogram), tokens above
-// it counted per chunk, tokens inside it appended to the candidate list.
-__global__ __launch_bounds__(NT) void select_a_kernel(Geo g) {
+// select_bin: per index item, the bin b1 of the first key digit that holds
+// the n_fac-th largest score, and the count of tokens above it.
+__global__ __launch_bounds__(NT) void select_bin_kernel(Geo g) {
   __shared__ uint32_t s_hist[kHistBins];
-  __shared__ uint2 s_cand[4096];
   __shared__ int s_w[NWAVE];
   __shared__ uint32_t s_res[2];
+  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    __syncthreads();
+    const uint4* gh = reinterpret_cast<const uint4*>(g.hist + (size_t)item * kHistBins);
+    for (int i = threadIdx.x; i < kHistBins / 4; i += NT) reinterpret_cast<uint4*>(s_hist)[i] = gh[i];
+    __syncthreads();
+    int b1;
+    uint32_t above1;
+    find_bin_top(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, b1, above1);
+    if (threadIdx.x == 0) {
+      g.info[(size_t)item * 4 + 0] = (uint32_t)b1;
+      g.info[(size_t)item * 4 + 1] = above1;
+    }
+  }
+}
+
+// select_a: per chunk, tokens above bin b1 are counted and tokens inside it
+// appended to the item's candidate list.  Each thread reads 4 consecutive
+// scores per 1024-token tile.
+__global__ __launch_bounds__(NT) void select_a_kernel(Geo g) {
+  __shared__ uint2 s_cand[4096];
+  __shared__ int s_w[NWAVE];
   __shared__ int s_n;
   __shared__ uint32_t s_base;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -306,33 +334,31 @@ __global__ __launch_bounds__(NT) void select_a_kernel(Geo g) {
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const int item = u / g.nch_t, ch = u - item * g.nch_t;
     __syncthreads();
-    const uint32_t* gh = g.hist + (size_t)item * kHistBins;
-    for (int i = tid; i < kHistBins; i += NT) s_hist[i] = gh[i];
     if (tid == 0) s_n = 0;
     __syncthreads();
-    int b1;
-    uint32_t above1;
-    find_bin_top(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, b1, above1);
-    if (ch == 0 && tid == 0) {
-      g.info[(size_t)item * 4 + 0] = (uint32_t)b1;
-      g.info[(size_t)item * 4 + 1] = above1;
-    }
-    const float* sc = g.scores + (size_t)item * g.T;
+    const int b1 = (int)g.info[(size_t)item * 4 + 0];
+    const float* sc = g.scores + (size_t)item * g.Ts;
     const int t0 = ch * g.ct, t1 = min(g.T, t0 + g.ct);
     int ngt = 0;
-    for (int base = t0; base < t1; base += NT) {
-      const int tok = base + tid;
-      const bool valid = tok < t1;
-      const uint32_t key = valid ? f2key(sc[tok]) : 0u;
-      const int bin = (int)(key >> 21);
-      ngt += (valid && bin > b1) ? 1 : 0;
-      const bool eq = valid && bin == b1;
-      const uint64_t m = __ballot(eq);
-      if (m) {
-        int wbase = 0;
-        if (lane == 0) wbase = atomicAdd(&s_n, __popcll(m));
-        wbase = __shfl(wbase, 0);
-        if (eq) s_cand[wbase + mbcnt(m)] = make_uint2(key, (uint32_t)tok);
+    for (int base = t0; base < t1; base += 4 * NT) {
+      const int tok0 = base + 4 * tid;
+      const float4 v4 = tok0 < t1 ? *reinterpret_cast<const float4*>(sc + tok0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = tok0 + e;
+        const bool valid = tok < t1;
+        const uint32_t key = f2key(vs[e]);
+        const int bin = (int)(key >> 21);
+        ngt += (valid && bin > b1) ? 1 : 0;
+        const bool eq = valid && bin == b1;
+        const uint64_t m = __ballot(eq);
+        if (m) {
+          int wbase = 0;
+          if (lane == 0) wbase = atomicAdd(&s_n, __popcll(m));
+          wbase = __shfl(wbase, 0);
+          if (eq) s_cand[wbase + mbcnt(m)] = make_uint2(key, (uint32_t)tok);
+        }
       }
     }
     int tot;
@@ -400,7 +426,7 @@ __global__ __launch_bounds__(NT) void select_b_kernel(Geo g) {
     const uint32_t above1 = g.info[(size_t)item * 4 + 1];
     const uint32_t count = g.info[(size_t)item * 4 + 2];
     const bool in_lds = count <= (uint32_t)min(g.cand_cap, kCandLds);
-    CandSource src{nullptr, 0, g.scores + (size_t)item * g.T, g.T, b1};
+    CandSource src{nullptr, 0, g.scores + (size_t)item * g.Ts, g.T, b1};
     if (in_lds) {
       const uint2* cd = g.cand + (size_t)item * g.cand_cap;
       for (int i = tid; i < (int)count; i += NT) s_c[i] = cd[i];
@@ -460,10 +486,11 @@ __global__ __launch_bounds__(NT) void select_b_kernel(Geo g) {
   }
 }
 
-// select_c: ordered compaction of the selected tokens of one chunk.
+// select_c: ordered compaction of the selected tokens of one chunk (each
+// thread owns 4 consecutive tokens of a 1024-token tile).
 __global__ __launch_bounds__(NT) void select_c_kernel(Geo g) {
   __shared__ int s_w[NWAVE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int n_units = plan_idx_pairs(g.plan) * g.B * g.nch_t;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const int item = u / g.nch_t, ch = u - item * g.nch_t;
@@ -471,34 +498,35 @@ __global__ __launch_bounds__(NT) void select_c_kernel(Geo g) {
     const int pair = idx_pairs(g)[pidx];
     const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
     const uint2 th = g.thr[item];
-    const uint32_t run0 = g.off[(size_t)item * g.nch_t + ch];
-    const float* sc = g.scores + (size_t)item * g.T;
+    const float* sc = g.scores + (size_t)item * g.Ts;
     int32_t* ix = g.idx + (size_t)item * g.n_fac;
     int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
     const int t0 = ch * g.ct, t1 = min(g.T, t0 + g.ct);
-    uint32_t run = run0;
-    for (int base = t0; base < t1; base += NT) {
-      const int tok = base + tid;
-      bool sel = false;
-      if (tok < t1) {
-        const uint32_t k = f2key(sc[tok]);
-        sel = k > th.x || (k == th.x && (uint32_t)tok <= th.y);
+    uint32_t run = g.off[(size_t)item * g.nch_t + ch];
+    for (int base = t0; base < t1; base += 4 * NT) {
+      const int tok0 = base + 4 * tid;
+      const float4 v4 = tok0 < t1 ? *reinterpret_cast<const float4*>(sc + tok0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+      uint32_t m = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = f2key(vs[e]);
+        const bool sel = (tok0 + e < t1) && (k > th.x || (k == th.x && (uint32_t)(tok0 + e) <= th.y));
+        m |= sel ? (1u << e) : 0u;
       }
-      const uint64_t m = __ballot(sel);
-      __syncthreads();
-      if (lane == 0) s_w[wave] = __popcll(m);
-      __syncthreads();
-      uint32_t wb = 0, tt = 0;
-      for (int w = 0; w < NWAVE; ++w) {
-        wb += (w < wave) ? (uint32_t)s_w[w] : 0u;
-        tt += (uint32_t)s_w[w];
+      int tot;
+      uint32_t pos = run + (uint32_t)block_excl_scan(__popc(m), s_w, tot);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((m >> e) & 1u) {
+          if (pos < (uint32_t)g.n_fac) {
+            ix[pos] = tok0 + e;
+            if (ox) ox[pos] = tok0 + e;
+          }
+          ++pos;
+        }
       }
-      const uint32_t pos = run + wb + (uint32_t)mbcnt(m);
-      if (sel && pos < (uint32_t)g.n_fac) {
-        ix[pos] = tok;
-        if (ox) ox[pos] = tok;
-      }
-      run += tt;
+      run += (uint32_t)tot;
     }
   }
 }
@@ -771,6 +799,11 @@ hipError_t launch_decode(const Geo& g, hipStream_t s) {
     e = g.bf16 ? launch_tip_v<uint16_t>(g, grid_tip, s) : launch_tip_v<float>(g, grid_tip, s);
   }
   if (e != hipSuccess) return e;
+  {
+    KTimer t("select_bin", s);
+    select_bin_kernel<<<clampi(n_idx_items, 1, g.grid), NT, 0, s>>>(g);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     KTimer t("select_a", s);
     select_a_kernel<<<grid_tip, NT, 0, s>>>(g);

@@ -23,6 +23,7 @@ struct Geo {
   int interleaved;  // rope pairing
   // chunking
   int ct, nch_t;    // score/select chunk tokens and count per item
+  int Ts;           // score row stride (T rounded up to 64)
   int cf, nch_f;    // FAC chunk rows and count per item
   int cs, nch_s;    // stream chunk rows and count per item
   int n_srows, s_end, w_start;  // streaming rows: [0, s_end) U [w_start, T)
@@ -37,7 +38,7 @@ struct Geo {
   uint32_t* ngt;     // [idx items][nch_t] tokens above the first digit bin per chunk
   uint32_t* off;     // [idx items][nch_t] output offset of each chunk
   uint2* thr;        // [idx items] (key*, token*) selection threshold
-  float* scores;     // [idx items][T]
+  float* scores;     // [idx items][Ts]
   int32_t* idx;      // [idx items][n_fac]
   float* part;       // [att items][nparts][G][d + 4]: acc[d], m, l
   // inputs / outputs

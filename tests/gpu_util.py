@@ -104,3 +104,32 @@ def check_index_set(got, scores, n, what=""):
     must_out = scores < sk - band
     assert sel[must_in].all(), f"{what}: {int((~sel[must_in]).sum())} required tokens missing"
     assert not sel[must_out].any(), f"{what}: {int(sel[must_out].sum())} excluded tokens selected"
+
+
+def run_clsa(case, labels=None, q_index=None, idx=True, ws=None):
+    cfg = case.cfg
+    out = torch.full((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), float("nan"), device="cuda")
+    ix = (torch.full((cfg.batch, cfg.n_kv_heads, cfg.n_fac), -7, dtype=torch.int32, device="cuda") if idx else None)
+    lab = None if labels is None else torch.from_numpy(np.ascontiguousarray(labels, dtype=np.uint8)).cuda()
+    ws = H.shared_index_decode(case.dims, case.q, case.k[0], case.v[0], case.k_dom[0], case.i_dom[0], out,
+                               q_index=q_index, labels=lab, idx_out=ix, ws=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (ix.cpu().numpy() if idx else None), ws
+
+
+def oracle_clsa_item(cfg, hi, b, g, labels=None, q_index=None):
+    """(out [N, G, d], idx, fp64 scores) of one (sequence, KV group) of the
+    shared-index mode; q_index [B, Hq, d] storage or None (layer 0)."""
+    G = cfg.group
+    k = f64(hi.rows("k", 0, b, g), cfg)
+    v = f64(hi.rows("v", 0, b, g), cfg)
+    qi = hi.q[0] if q_index is None else q_index
+    scores = fasa.tip_scores(f64(qi[b, g * G:(g + 1) * G], cfg), k, hi.i_dom[0, g])
+    idx = fasa.top_n(scores, cfg.n_fac)
+    rows_s = fasa.stream_rows(cfg.ctx_len, cfg.n_sink, cfg.window)
+    out = np.zeros((cfg.n_layers, G, cfg.d_head))
+    for n in range(cfg.n_layers):
+        rows = idx if (labels is None or labels[n, g]) else rows_s
+        for j in range(G):
+            out[n, j] = fasa.attend(f64(hi.q[n, b, g * G + j], cfg), k[rows], v[rows])
+    return out, idx, scores

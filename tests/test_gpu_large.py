@@ -1,0 +1,87 @@
+"""GPU parity at the full 128K sizes, in the launch configuration the
+benchmark times: CLSA shared-index mode (8 layers share one 131072-token
+cache, batch 4) and the 32-layer step (68.7 GB cache), checked on sampled
+(layer, sequence, KV group) items that the oracle recomputes one by one."""
+import numpy as np
+import pytest
+
+from synth import recipe as R
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def test_clsa_128k_shared_index():
+    cfg = R.get_config("c3")
+    print("case c3 full", flush=True)
+    case = U.DeviceCase(cfg)
+    out, idx, ws = U.run_clsa(case)
+    G = cfg.group
+    for (b, g) in [(0, 0), (1, 3), (2, 5), (3, 7)]:
+        ref, ridx, scores = U.oracle_clsa_item(cfg, case.hi, b, g)
+        U.check_index_set(idx[b, g], scores, cfg.n_fac, f"c3 idx b{b} g{g}")
+        assert np.isin(R.needle_positions(cfg, 0, b, g), idx[b, g]).all()
+        for n in range(cfg.n_layers):
+            U.check_out(out[n, b, g * G:(g + 1) * G], ref[n], f"c3 out n{n} b{b} g{g}")
+    # per-layer labels: layers 2 and 5 treat group 1 as streaming
+    lab = np.ones((cfg.n_layers, cfg.n_kv_heads), np.uint8)
+    lab[2, 1] = lab[5, 1] = 0
+    out2, idx2, _ = U.run_clsa(case, labels=lab, ws=ws)
+    assert (idx2 == idx).all()
+    ref, _, _ = U.oracle_clsa_item(cfg, case.hi, 1, 1, labels=lab)
+    for n in range(cfg.n_layers):
+        U.check_out(out2[n, 1, G:2 * G], ref[n], f"c3 labelled n{n}")
+
+
+def test_clsa_single_layer_equals_sparse_decode():
+    cfg = R.get_config("c3", n_layers=1, ctx_len=20000, batch=2)
+    print("case c3 N=1", flush=True)
+    case = U.DeviceCase(cfg)
+    out, idx, _ = U.run_clsa(case)
+    out2, idx2, _ = case.run()
+    assert (idx2[0] == idx).all()
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-6)
+
+
+def test_clsa_explicit_indexer_query():
+    import torch
+    from synth import device as sdev
+    cfg = R.get_config("c3", ctx_len=16384, batch=2)
+    print("case c3 q_index", flush=True)
+    case = U.DeviceCase(cfg)
+    qi_np = case.hi.q[3]
+    qi = sdev.to_device(qi_np, "cuda", cfg.bf16)
+    out, idx, _ = U.run_clsa(case, q_index=qi)
+    G = cfg.group
+    for (b, g) in [(0, 2), (1, 6)]:
+        ref, _, scores = U.oracle_clsa_item(cfg, case.hi, b, g, q_index=qi_np)
+        U.check_index_set(idx[b, g], scores, cfg.n_fac, "c3 q_index idx")
+        for n in range(cfg.n_layers):
+            U.check_out(out[n, b, g * G:(g + 1) * G], ref[n], f"c3 q_index out n{n}")
+
+
+def test_c4_32_layers_128k_sampled():
+    cfg = R.get_config("c4")
+    print("case c4 full", flush=True)
+    case = U.DeviceCase(cfg)
+    out, idx, _ = case.run()
+    planted = R.planted_groups(cfg)
+    streaming = [(l, g) for l in range(cfg.n_layers) for g in range(cfg.n_kv_heads) if (l, g) not in set(planted)]
+    rng = np.random.default_rng(11)
+    items = [(*planted[i], int(rng.integers(cfg.batch))) for i in rng.choice(len(planted), 3, replace=False)]
+    items += [(*streaming[i], int(rng.integers(cfg.batch))) for i in rng.choice(len(streaming), 3, replace=False)]
+    G = cfg.group
+    for (l, g, b) in items:
+        print(f"  item l{l} b{b} g{g}", flush=True)
+        ref, ridx, scores = U.oracle_item(cfg, case.hi, case.labels_np, l, b, g)
+        U.check_out(out[l, b, g * G:(g + 1) * G], ref, f"c4 out l{l} b{b} g{g}")
+        if case.labels_np[l, g]:
+            U.check_index_set(idx[l, b, g], scores, cfg.n_fac, f"c4 idx l{l} b{b} g{g}")
+            assert np.isin(R.needle_positions(cfg, l, b, g), idx[l, b, g]).all()
+        else:
+            assert (idx[l, b, g] == -1).all()
+    # every retrieval row is a valid ascending index set, every streaming row is -1
+    lab = case.labels_np.astype(bool)
+    ret = idx[np.broadcast_to(lab[:, None, :], idx.shape[:3])]
+    assert (np.diff(ret, axis=1) > 0).all() and ret.min() >= 0 and ret.max() < cfg.ctx_len
+    assert (idx[np.broadcast_to(~lab[:, None, :], idx.shape[:3])] == -1).all()
