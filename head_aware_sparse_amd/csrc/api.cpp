@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -88,7 +89,8 @@ has_status check_dims(const has_decode_dims* d, bool clsa) {
 
 struct Layout {
   has::Geo g;
-  size_t off_plan, off_hist, off_info, off_cand, off_ngt, off_off, off_thr, off_scores, off_idx, off_part;
+  size_t off_plan, off_hist, off_info, off_cand, off_ngt, off_off, off_thr, off_scores, off_idx, off_part, off_tau,
+      off_bm;
   size_t bytes;
 };
 
@@ -126,7 +128,18 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   g.cs = clampi(pow2_floor((long long)g.n_srows * n_att / 2048), 128, has::kMaxChunkRows);
   g.nch_s = (g.n_srows + g.cs - 1) / g.cs;
   g.nparts = g.nch_f > g.nch_s ? g.nch_f : g.nch_s;
-  g.cand_cap = g.T < has::kCandLds ? g.T : has::kCandLds;
+  // Prefiltered selection: a sample of kSampleTokens scores places a key
+  // threshold expected to pass about 2 n_fac tokens (+4 sigma of sampling
+  // noise); used when that fits the kCandFast candidate slots comfortably.
+  {
+    const double S = has::kSampleTokens, p = (double)g.n_fac / g.T;
+    const double r = 2.0 * S * p + 4.0 * std::sqrt(S * p) + 16.0;
+    g.samp_rank = (int)std::ceil(r);
+    g.prefilter = (g.T >= 2 * has::kSampleTokens && g.T <= has::kPrefilterMaxT && 3LL * g.n_fac <= has::kCandFast &&
+                   g.samp_rank < has::kSampleTokens / 2) ? 1 : 0;
+  }
+  g.cand_cap = g.prefilter ? has::kCandFast : (g.T < has::kCandLds ? g.T : has::kCandLds);
+  g.bm_words = (g.T + 31) / 32;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -143,6 +156,8 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   L.off_scores = take((size_t)n_idx * g.Ts * 4);
   L.off_idx = take((size_t)n_idx * g.n_fac * 4);
   L.off_part = take((size_t)n_att * g.nparts * g.G * (g.d + 4) * 4);
+  L.off_tau = take((size_t)n_idx * 4);
+  L.off_bm = take((size_t)n_idx * g.bm_words * 4);
   L.bytes = o;
   return L;
 }
@@ -160,6 +175,36 @@ void carve(Layout& L, void* ws) {
   g.scores = (float*)(b + L.off_scores);
   g.idx = (int32_t*)(b + L.off_idx);
   g.part = (float*)(b + L.off_part);
+  g.tau = (uint32_t*)(b + L.off_tau);
+  g.bitmap = (uint32_t*)(b + L.off_bm);
+}
+
+// Per-device side stream and fork/join events.  The enqueue sequence that
+// uses them is serialised by g_side_mu so concurrent callers cannot
+// interleave their event records.
+struct SideState {
+  int device = -1;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::vector<SideState> g_side;
+
+has_status side_streams(int dev, SideState*& out) {
+  for (SideState& st : g_side)
+    if (st.device == dev) {
+      out = &st;
+      return HAS_OK;
+    }
+  SideState st;
+  st.device = dev;
+  hipError_t e = hipStreamCreateWithFlags(&st.side, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+  if ((e = hipEventCreateWithFlags(&st.fork, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  if ((e = hipEventCreateWithFlags(&st.join, hipEventDisableTiming)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  g_side.push_back(st);
+  out = &g_side.back();
+  return HAS_OK;
 }
 
 has_status persistent_grid(int& grid) {
@@ -216,7 +261,14 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
   g.idx_out = idx_out;
   s = persistent_grid(g.grid);
   if (s != HAS_OK) return s;
-  hipError_t e = has::launch_decode(g, (hipStream_t)stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideState* st = nullptr;
+  s = side_streams(dev, st);
+  if (s != HAS_OK) return s;
+  e = has::launch_decode(g, has::StreamSet{(hipStream_t)stream, st->side, st->fork, st->join});
   if (e != hipSuccess) return hip_fail(e, clsa ? "shared_index_decode launch" : "sparse_decode_step launch");
   return ok();
 }

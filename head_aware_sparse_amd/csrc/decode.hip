@@ -118,6 +118,13 @@ struct Vec<uint16_t> {  // bf16 bits
 };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Streaming (read-once) 16-byte load: nontemporal, so the cache rows and the
+// dominant-key copy, each read once per step, do not evict reused data.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ int label_at(const Geo& g, int pair) {
   return g.labels ? (g.labels[pair] != 0) : 1;
@@ -194,7 +201,8 @@ __global__ __launch_bounds__(NT) void plan_kernel(Geo g) {
   const size_t gtid = (size_t)blockIdx.x * NT + tid, gstride = (size_t)gridDim.x * NT;
   uint4* h4 = reinterpret_cast<uint4*>(g.hist);
   const size_t nh4 = n_items * kHistBins / 4;
-  for (size_t i = gtid; i < nh4; i += gstride) h4[i] = make_uint4(0, 0, 0, 0);
+  if (!g.prefilter)
+    for (size_t i = gtid; i < nh4; i += gstride) h4[i] = make_uint4(0, 0, 0, 0);
   uint4* i4 = reinterpret_cast<uint4*>(g.info);
   for (size_t i = gtid; i < n_items; i += gstride) i4[i] = make_uint4(0, 0, 0, 0);
   // Streaming groups report -1 indices.
@@ -209,51 +217,81 @@ __global__ __launch_bounds__(NT) void plan_kernel(Geo g) {
   }
 }
 
+// Group query of an index item in k_dom channel order (zero padded) into
+// s_q[R]; returns the item's cache slice.  Callers synchronise around it.
+template <typename E>
+__device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
+  const int pidx = item / g.B, b = item - pidx * g.B;
+  const int pair = idx_pairs(g)[pidx];
+  const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
+  const E* qg;
+  if (g.clsa)
+    qg = (const E*)(g.q_index ? g.q_index : g.q) + ((size_t)b * g.Hq + gi * g.G) * g.d;
+  else
+    qg = (const E*)g.q + (((size_t)l * g.B + b) * g.Hq + gi * g.G) * g.d;
+  const int32_t* dom = g.i_dom + (size_t)pair * g.n_dom;
+  const int hd = g.d / 2;
+  for (int c = threadIdx.x; c < g.R; c += NT) {
+    float v = 0.f;
+    if (c < 2 * g.n_dom) {
+      const int f = dom[c >> 1], cc = c & 1;
+      const int chn = g.interleaved ? 2 * f + cc : f + cc * hd;
+      float sum = 0.f;
+      for (int h = 0; h < g.G; ++h) sum += Vec<E>::one(qg, (size_t)h * g.d + chn);
+      v = sum / (float)g.G;
+    }
+    s_q[c] = v;
+  }
+  return ((size_t)l * g.B + b) * g.Hkv + gi;
+}
+
+// One token's TIP score by a single thread (row of R elements).
+template <typename E>
+__device__ __forceinline__ float score_one(const E* row, const float* s_q, int R) {
+  constexpr int EPV = Vec<E>::N;
+  float s = 0.f;
+  for (int v = 0; v < R / EPV; ++v) {
+    float kv[EPV];
+    Vec<E>::cvt(ld16(row + v * EPV), kv);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) s += s_q[v * EPV + e] * kv[e];
+  }
+  return s;
+}
+
+constexpr int kMaxR = 128;  // k_dom row elements: 2 * (d/2) at most
+
 // ------------------------------------------------------------------ TIP
 // One unit = (index item, chunk of ct tokens).  A wave scores 64 tokens per
 // step: lane L loads 16 bytes of row (L / V) of each of V consecutive
 // 64/V-token slabs, the V lanes of a row reduce their partial dot products,
 // and lane L keeps the score of token (L % V) * 64/V + L / V, so each wave
 // writes 64 consecutive scores.
-template <typename E, int V>
+template <typename E, int V, bool PF>
 __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
   constexpr int EPV = Vec<E>::N;
-  constexpr int U = V >= 8 ? 1 : 8 / V;  // 64-token steps in flight per wave
-  __shared__ uint32_t s_hist[kHistBins];
+  constexpr int U = V >= 8 ? 2 : 16 / V;  // 64-token steps in flight per wave (16 loads per lane)
+  __shared__ uint32_t s_hist[PF ? 1 : kHistBins];
+  constexpr int kCandUnit = 1024;  // candidates staged in LDS per unit; the rest go straight out
+  __shared__ uint2 s_cand[PF ? kCandUnit : 1];
   __shared__ float s_q[V * EPV];
+  __shared__ int s_n;
+  __shared__ uint32_t s_base;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_units = plan_idx_pairs(g.plan) * g.B * g.nch_t;
-  for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0;
+  if constexpr (!PF)
+    for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0;
   const int R = V * EPV;
-  const int hd = g.d / 2;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const int item = u / g.nch_t, ch = u - item * g.nch_t;
-    const int pidx = item / g.B, b = item - pidx * g.B;
-    const int pair = idx_pairs(g)[pidx];
-    const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
-    const E* qg;
-    if (g.clsa)
-      qg = (const E*)(g.q_index ? g.q_index : g.q) + ((size_t)b * g.Hq + gi * g.G) * g.d;
-    else
-      qg = (const E*)g.q + (((size_t)l * g.B + b) * g.Hq + gi * g.G) * g.d;
-    const int32_t* dom = g.i_dom + (size_t)pair * g.n_dom;
     __syncthreads();
-    for (int c = tid; c < R; c += NT) {
-      float v = 0.f;
-      if (c < 2 * g.n_dom) {
-        const int f = dom[c >> 1], cc = c & 1;
-        const int chn = g.interleaved ? 2 * f + cc : f + cc * hd;
-        float s = 0.f;
-        for (int h = 0; h < g.G; ++h) s += Vec<E>::one(qg, (size_t)h * g.d + chn);
-        v = s / (float)g.G;
-      }
-      s_q[c] = v;
-    }
+    const size_t slice = group_query_dom<E>(g, item, s_q);
+    if (tid == 0) s_n = 0;
+    const uint32_t tau = PF ? g.tau[item] : 0u;
     __syncthreads();
     float qr[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
-    const size_t slice = ((size_t)l * g.B + b) * g.Hkv + gi;
     const E* kd = (const E*)g.kdom + slice * (size_t)g.T * R;
     float* sc = g.scores + (size_t)item * g.Ts;
     const int t0 = ch * g.ct, t1 = min(g.T, t0 + g.ct);
@@ -264,7 +302,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
           const int tok = base + j * NT + i * (64 / V) + lane / V;
-          raw[j][i] = tok < t1 ? ld16(kd + (size_t)tok * R + (lane % V) * EPV) : make_uint4(0, 0, 0, 0);
+          raw[j][i] = tok < t1 ? ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
       for (int j = 0; j < U; ++j) {
@@ -280,19 +318,47 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
           if ((lane % V) == i) mine = s;
         }
         const int tok = base + j * NT + (lane % V) * (64 / V) + lane / V;
-        if (tok < t1) {
+        if constexpr (PF) {
+          const uint32_t key = f2key(mine);
+          const bool cand = tok < t1 && key >= tau;
+          const uint64_t m = __ballot(cand);
+          if (m) {
+            int wbase = 0;
+            if (lane == 0) wbase = atomicAdd(&s_n, __popcll(m));
+            wbase = __shfl(wbase, 0);
+            if (cand) {
+              const int at = wbase + mbcnt(m);
+              if (at < kCandUnit) {
+                s_cand[at] = make_uint2(key, (uint32_t)tok);
+              } else {  // dense unit: append directly (rare)
+                const uint32_t gpos = atomicAdd(&g.info[(size_t)item * 4 + 2], 1u);
+                if (gpos < (uint32_t)g.cand_cap) g.cand[(size_t)item * g.cand_cap + gpos] = make_uint2(key, (uint32_t)tok);
+              }
+            }
+          }
+        } else if (tok < t1) {
           sc[tok] = mine;
           atomicAdd(&s_hist[f2key(mine) >> 21], 1u);
         }
       }
     }
     __syncthreads();
-    uint32_t* gh = g.hist + (size_t)item * kHistBins;
-    for (int i = tid; i < kHistBins; i += NT) {
-      const uint32_t c = s_hist[i];
-      if (c) {
-        atomicAdd(&gh[i], c);
-        s_hist[i] = 0;
+    if constexpr (PF) {
+      const int n = min(s_n, kCandUnit);
+      if (tid == 0) s_base = atomicAdd(&g.info[(size_t)item * 4 + 2], (uint32_t)n);
+      __syncthreads();
+      const uint32_t cbase = s_base;
+      uint2* cd = g.cand + (size_t)item * g.cand_cap;
+      for (int i = tid; i < n; i += NT)
+        if (cbase + (uint32_t)i < (uint32_t)g.cand_cap) cd[cbase + i] = s_cand[i];
+    } else {
+      uint32_t* gh = g.hist + (size_t)item * kHistBins;
+      for (int i = tid; i < kHistBins; i += NT) {
+        const uint32_t c = s_hist[i];
+        if (c) {
+          atomicAdd(&gh[i], c);
+          s_hist[i] = 0;
+        }
       }
     }
   }
@@ -398,14 +464,302 @@ struct CandSource {
   }
 };
 
-template <class Pred, class Dig>
-__device__ void histogram(const CandSource& src, uint32_t* s_hist, int nbins, Pred pred, Dig dig) {
+template <class Src, class Pred, class Dig>
+__device__ void histogram(const Src& src, uint32_t* s_hist, int nbins, Pred pred, Dig dig) {
   for (int i = threadIdx.x; i < nbins; i += NT) s_hist[i] = 0;
   __syncthreads();
   src.for_each([&](uint32_t key, uint32_t tok) {
     if (pred(key, tok)) atomicAdd(&s_hist[dig(key, tok)], 1u);
   });
   __syncthreads();
+}
+
+// (key, token) pairs held in LDS.
+struct LdsPairs {
+  const uint2* p;
+  int n;
+  template <class F>
+  __device__ __forceinline__ void for_each(F f) const {
+    for (int i = threadIdx.x; i < n; i += NT) f(p[i].x, p[i].y);
+  }
+};
+
+// Keys held in LDS, the position standing in for the token.
+struct LdsKeys {
+  const uint32_t* k;
+  int n;
+  template <class F>
+  __device__ __forceinline__ void for_each(F f) const {
+    for (int i = threadIdx.x; i < n; i += NT) f(k[i], (uint32_t)i);
+  }
+};
+
+// Every token of an item's score row.
+struct ScoreScan {
+  const float* sc;
+  int T;
+  template <class F>
+  __device__ __forceinline__ void for_each(F f) const {
+    for (int t = threadIdx.x; t < T; t += NT) f(f2key(sc[t]), (uint32_t)t);
+  }
+};
+
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t x) {
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+
+// Workgroup min and max of the keys of src (every thread gets both).
+template <class Src>
+__device__ void key_range(const Src& src, uint32_t* s_res, uint32_t& lo, uint32_t& hi) {
+  __shared__ uint32_t s_lo[NWAVE], s_hi[NWAVE];
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+  src.for_each([&](uint32_t k, uint32_t) {
+    a = min(a, k);
+    b = max(b, k);
+  });
+  a = wave_min_u(a);
+  b = wave_max_u(b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    s_lo[wave] = a;
+    s_hi[wave] = b;
+  }
+  __syncthreads();
+  lo = s_lo[0];
+  hi = s_hi[0];
+  for (int w = 1; w < NWAVE; ++w) {
+    lo = min(lo, s_lo[w]);
+    hi = max(hi, s_hi[w]);
+  }
+  (void)s_res;
+}
+
+// The need-th element of src in the order (key desc, token asc).  Keys are
+// resolved in at most three radix digits taken over the span [lo, hi] of
+// the keys present (so the first digit spreads them over its 2048 bins);
+// then, among the elements equal to that key, the need-th smallest token
+// (WITH_TOKEN): directly when all of them are selected, else by three more
+// 10-bit digits.
+template <bool WITH_TOKEN, class Src>
+__device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist, int* s_w, uint32_t* s_res,
+                                uint32_t& kstar, uint32_t& tstar) {
+  uint32_t lo, hi;
+  key_range(src, s_res, lo, hi);
+  const uint32_t span = hi - lo;
+  int rem = span ? 32 - __clz(span) : 0;  // bits of (key - lo) still open
+  uint32_t pre = 0;
+  while (rem > 0) {
+    const int w = rem < 11 ? rem : 11;
+    rem -= w;
+    const int sh = rem;
+    const int nbins = (1 << w) < NT ? NT : (1 << w);
+    const uint32_t p = pre;
+    const int up = sh + w;
+    histogram(src, s_hist, nbins,
+              [=](uint32_t k, uint32_t) { return up >= 32 ? true : (((k - lo) >> up) == p); },
+              [=](uint32_t k, uint32_t) { return ((k - lo) >> sh) & ((1u << w) - 1u); });
+    int bin;
+    uint32_t above;
+    find_bin_top(s_hist, nbins, need, s_w, s_res, bin, above);
+    need -= above;
+    pre = (pre << w) | (uint32_t)bin;
+  }
+  kstar = lo + pre;
+  tstar = 0;
+  if constexpr (WITH_TOKEN) {
+    const uint32_t ks = kstar;
+    // how many elements carry kstar, and the largest such token
+    __shared__ uint32_t s_eq[2 * NWAVE];
+    uint32_t n_eq = 0, t_max = 0;
+    src.for_each([&](uint32_t k, uint32_t t) {
+      if (k == ks) {
+        ++n_eq;
+        t_max = max(t_max, t);
+      }
+    });
+    for (int o = 32; o >= 1; o >>= 1) {
+      n_eq += (uint32_t)__shfl_xor((int)n_eq, o);
+      t_max = max(t_max, (uint32_t)__shfl_xor((int)t_max, o));
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) {
+      s_eq[wave] = n_eq;
+      s_eq[NWAVE + wave] = t_max;
+    }
+    __syncthreads();
+    n_eq = 0;
+    t_max = 0;
+    for (int w = 0; w < NWAVE; ++w) {
+      n_eq += s_eq[w];
+      t_max = max(t_max, s_eq[NWAVE + w]);
+    }
+    if (need == n_eq) {
+      tstar = t_max;
+    } else {
+      uint32_t tpre = 0;
+      for (int shift = 20; shift >= 0; shift -= 10) {
+        const uint32_t hmask = (shift == 20) ? 0u : (0xFFFFFFFFu << (shift + 10));
+        histogram(src, s_hist, 1024, [=](uint32_t k, uint32_t t) { return k == ks && (t & hmask) == tpre; },
+                  [=](uint32_t, uint32_t t) { return 1023u - ((t >> shift) & 0x3FFu); });
+        int bin;
+        uint32_t above;
+        find_bin_top(s_hist, 1024, need, s_w, s_res, bin, above);
+        need -= above;
+        tpre |= (1023u - (uint32_t)bin) << shift;
+      }
+      tstar = tpre;
+    }
+  }
+}
+
+// sample: per index item, TIP scores of kSampleTokens tokens in 16 evenly
+// spread blocks of 256 (each wave scores 64 tokens per block with the same
+// lane layout as tip_kernel); the samp_rank-th largest sampled key becomes
+// the item's candidate threshold tau (tokens with key >= tau are candidates).
+template <typename E, int V>
+__global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
+  constexpr int EPV = Vec<E>::N;
+  constexpr int kBlocks = kSampleTokens / 256;
+  __shared__ float s_q[kMaxR];
+  __shared__ uint32_t s_key[kSampleTokens];
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ int s_w[NWAVE];
+  __shared__ uint32_t s_res[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = V * EPV;
+  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    __syncthreads();
+    const size_t slice = group_query_dom<E>(g, item, s_q);
+    __syncthreads();
+    float qr[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
+    const E* kd = (const E*)g.kdom + slice * (size_t)g.T * R;
+    for (int blk0 = 0; blk0 < kBlocks; blk0 += 2) {
+      uint4 raw[2][V];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int start = (int)((long long)(blk0 + j) * (g.T - 256) / (kBlocks - 1));
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int tok = start + wave * 64 + i * (64 / V) + lane / V;
+          raw[j][i] = ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float mine = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float kv[EPV];
+          Vec<E>::cvt(raw[j][i], kv);
+          float sum = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) sum += qr[e] * kv[e];
+          sum = group_sum<V>(sum);
+          if ((lane % V) == i) mine = sum;
+        }
+        s_key[(blk0 + j) * 256 + wave * 64 + lane] = f2key(mine);
+      }
+    }
+    __syncthreads();
+    uint32_t kr, unused;
+    exact_threshold<false>(LdsKeys{s_key, kSampleTokens}, (uint32_t)g.samp_rank, s_hist, s_w, s_res, kr, unused);
+    if (tid == 0) g.tau[item] = kr;
+  }
+}
+
+// final: per index item, the exact top-n_fac among the candidates (key >=
+// tau) held in LDS.  If the candidates are fewer than n_fac or overflowed,
+// the item is rescored in full here and selected from its score row (exact
+// either way).  The selected tokens are marked in an LDS bitmap and emitted
+// in ascending order.
+template <typename E>
+__global__ __launch_bounds__(NT) void final_kernel(Geo g) {
+  __shared__ uint2 s_c[kCandFast];
+  __shared__ uint32_t s_bm[kPrefilterMaxT / 32];
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ float s_q[kMaxR];
+  __shared__ int s_w[NWAVE];
+  __shared__ uint32_t s_res[2];
+  const int tid = threadIdx.x;
+  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    __syncthreads();
+    const uint32_t count = g.info[(size_t)item * 4 + 2];
+    for (int w = tid; w < g.bm_words; w += NT) s_bm[w] = 0u;
+    uint32_t kstar, tstar;
+    if (count >= (uint32_t)g.n_fac && count <= (uint32_t)g.cand_cap) {
+      // candidates -> LDS, two per 16-byte load, eight loads in flight
+      const uint4* c4 = reinterpret_cast<const uint4*>(g.cand + (size_t)item * g.cand_cap);
+      const int n4 = (int)(count + 1) / 2;
+      for (int i0 = tid; i0 < n4; i0 += 8 * NT) {
+        uint4 r[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = i0 + j * NT < n4 ? c4[i0 + j * NT] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = i0 + j * NT;
+          if (i < n4) {
+            s_c[2 * i] = make_uint2(r[j].x, r[j].y);
+            if (2 * i + 1 < (int)count) s_c[2 * i + 1] = make_uint2(r[j].z, r[j].w);
+          }
+        }
+      }
+      __syncthreads();
+      const LdsPairs src{s_c, (int)count};
+      exact_threshold<true>(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+      src.for_each([&](uint32_t k, uint32_t t) {
+        if (k > kstar || (k == kstar && t <= tstar)) atomicOr(&s_bm[t >> 5], 1u << (t & 31));
+      });
+    } else {
+      const size_t slice = group_query_dom<E>(g, item, s_q);
+      __syncthreads();
+      const E* kd = (const E*)g.kdom + slice * (size_t)g.T * g.R;
+      float* sc = g.scores + (size_t)item * g.Ts;
+      for (int t = tid; t < g.T; t += NT) sc[t] = score_one<E>(kd + (size_t)t * g.R, s_q, g.R);
+      __threadfence();
+      __syncthreads();
+      const ScoreScan src{sc, g.T};
+      exact_threshold<true>(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+      src.for_each([&](uint32_t k, uint32_t t) {
+        if (k > kstar || (k == kstar && t <= tstar)) atomicOr(&s_bm[t >> 5], 1u << (t & 31));
+      });
+    }
+    __syncthreads();
+    // ordered emission: each thread owns a contiguous run of bitmap words
+    const int per = (g.bm_words + NT - 1) / NT;
+    const int w0 = min(g.bm_words, tid * per), w1 = min(g.bm_words, w0 + per);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(s_bm[w]);
+    int tot;
+    uint32_t pos = (uint32_t)block_excl_scan(cnt, s_w, tot);
+    const int pidx = item / g.B, b = item - pidx * g.B;
+    const int pair = idx_pairs(g)[pidx];
+    const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
+    int32_t* ix = g.idx + (size_t)item * g.n_fac;
+    int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = s_bm[w];
+      while (bits) {
+        const int t = w * 32 + __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (pos < (uint32_t)g.n_fac) {
+          ix[pos] = t;
+          if (ox) ox[pos] = t;
+        }
+        ++pos;
+      }
+    }
+  }
 }
 
 // select_b: exact threshold.  Ordering is (score desc, token asc); the
@@ -543,13 +897,15 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
   constexpr int RPW = 64 / LPR;
   constexpr int RPB = RPW * NWAVE;
   constexpr float kScale = (D == 128 ? 0.08838834764831845f : 0.125f) * 1.4426950408889634f;
+  constexpr int AU = 4;  // row groups (16 B per lane each) in flight per wave
   __shared__ float s_z[G][kMaxChunkRows];
   __shared__ int s_rows[kMaxChunkRows];
   __shared__ float s_red[NWAVE][G][D];
   __shared__ float s_ml[G][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane % LPR, rsub = lane / LPR;
-  const int n_ret = g.plan[1], n_str = g.plan[2];
+  const int n_ret = g.attn_mode == 2 ? 0 : g.plan[1];
+  const int n_str = g.attn_mode == 1 ? 0 : g.plan[2];
   const int n_fac_units = n_ret * g.B * g.nch_f;
   const int n_units = n_fac_units + n_str * g.B * g.nch_s;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
@@ -590,17 +946,17 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
     }
     __syncthreads();
     // pass 1: logits (log2 domain) into s_z
-    for (int r0 = wave * RPW; r0 < nrows; r0 += 2 * RPB) {
-      uint4 raw[2];
-      int rr[2];
+    for (int r0 = wave * RPW; r0 < nrows; r0 += AU * RPB) {
+      uint4 raw[AU];
+      int rr[AU];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < AU; ++j) {
         rr[j] = r0 + j * RPB + rsub;
-        raw[j] = rr[j] < nrows ? ld16(kb + (size_t)s_rows[rr[j]] * D + slot * CPL)
+        raw[j] = rr[j] < nrows ? ld16_stream(kb + (size_t)s_rows[rr[j]] * D + slot * CPL)
                                : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < AU; ++j) {
         float kf[CPL];
         Vec<E>::cvt(raw[j], kf);
 #pragma unroll
@@ -637,17 +993,17 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) acc[h][c] = 0.f;
-    for (int r0 = wave * RPW; r0 < nrows; r0 += 2 * RPB) {
-      uint4 raw[2];
-      int rr[2];
+    for (int r0 = wave * RPW; r0 < nrows; r0 += AU * RPB) {
+      uint4 raw[AU];
+      int rr[AU];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < AU; ++j) {
         rr[j] = r0 + j * RPB + rsub;
-        raw[j] = rr[j] < nrows ? ld16(vb + (size_t)s_rows[rr[j]] * D + slot * CPL)
+        raw[j] = rr[j] < nrows ? ld16_stream(vb + (size_t)s_rows[rr[j]] * D + slot * CPL)
                                : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < AU; ++j) {
         if (rr[j] < nrows) {
           float vf[CPL];
           Vec<E>::cvt(raw[j], vf);
@@ -753,15 +1109,35 @@ hipError_t launch_attn_g(const Geo& g, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E>
+hipError_t launch_attn(const Geo& g, int grid, hipStream_t s) {
+  if (g.bf16)
+    return g.d == 128 ? launch_attn_g<uint16_t, 128>(g, grid, s) : launch_attn_g<uint16_t, 64>(g, grid, s);
+  return g.d == 128 ? launch_attn_g<float, 128>(g, grid, s) : launch_attn_g<float, 64>(g, grid, s);
+}
+
+template <typename E, bool PF>
 hipError_t launch_tip_v(const Geo& g, int grid, hipStream_t s) {
   const int V = g.R * (int)sizeof(E) / 16;
   switch (V) {
-    case 1: tip_kernel<E, 1><<<grid, NT, 0, s>>>(g); break;
-    case 2: tip_kernel<E, 2><<<grid, NT, 0, s>>>(g); break;
-    case 4: tip_kernel<E, 4><<<grid, NT, 0, s>>>(g); break;
-    case 8: tip_kernel<E, 8><<<grid, NT, 0, s>>>(g); break;
-    case 16: tip_kernel<E, 16><<<grid, NT, 0, s>>>(g); break;
+    case 1: tip_kernel<E, 1, PF><<<grid, NT, 0, s>>>(g); break;
+    case 2: tip_kernel<E, 2, PF><<<grid, NT, 0, s>>>(g); break;
+    case 4: tip_kernel<E, 4, PF><<<grid, NT, 0, s>>>(g); break;
+    case 8: tip_kernel<E, 8, PF><<<grid, NT, 0, s>>>(g); break;
+    case 16: tip_kernel<E, 16, PF><<<grid, NT, 0, s>>>(g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_sample_v(const Geo& g, int grid, hipStream_t s) {
+  const int V = g.R * (int)sizeof(E) / 16;
+  switch (V) {
+    case 1: sample_kernel<E, 1><<<grid, NT, 0, s>>>(g); break;
+    case 2: sample_kernel<E, 2><<<grid, NT, 0, s>>>(g); break;
+    case 4: sample_kernel<E, 4><<<grid, NT, 0, s>>>(g); break;
+    case 8: sample_kernel<E, 8><<<grid, NT, 0, s>>>(g); break;
+    case 16: sample_kernel<E, 16><<<grid, NT, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -783,8 +1159,10 @@ hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const Geo& g, hipStream_t s) {
+hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   hipError_t e;
+  const hipStream_t s = ss.main;
+  Geo g = g0;
   const long long n_idx_items = (long long)(g.clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att_items = (long long)g.Lq * g.Hkv * g.B;
   const int grid_plan = clampi((n_idx_items * kHistBins / 4 + NT - 1) / NT, 1, g.grid);
@@ -793,42 +1171,73 @@ hipError_t launch_decode(const Geo& g, hipStream_t s) {
     plan_kernel<<<grid_plan, NT, 0, s>>>(g);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // Streaming groups need nothing but the plan: their attention runs on the
+  // side stream, overlapping the scoring and selection of retrieval groups.
+  if ((e = hipEventRecord(ss.fork, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(ss.side, ss.fork, 0)) != hipSuccess) return e;
+  {
+    Geo gs = g;
+    gs.attn_mode = 2;
+    const int grid_s = clampi(n_att_items * (long long)g.nch_s, 1, g.grid);
+    KTimer t("attention_stream", ss.side);
+    e = launch_attn(gs, grid_s, ss.side);
+  }
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(ss.join, ss.side)) != hipSuccess) return e;
   const int grid_tip = clampi(n_idx_items * g.nch_t, 1, g.grid);
+  const int grid_item = clampi(n_idx_items, 1, g.grid);
+  if (g.prefilter) {
+    {
+      KTimer t("sample", s);
+      e = g.bf16 ? launch_sample_v<uint16_t>(g, grid_item, s) : launch_sample_v<float>(g, grid_item, s);
+    }
+    if (e != hipSuccess) return e;
+    {
+      KTimer t("tip_score", s);
+      e = g.bf16 ? launch_tip_v<uint16_t, true>(g, grid_tip, s) : launch_tip_v<float, true>(g, grid_tip, s);
+    }
+    if (e != hipSuccess) return e;
+    {
+      KTimer t("select_final", s);
+      if (g.bf16) final_kernel<uint16_t><<<grid_item, NT, 0, s>>>(g);
+      else final_kernel<float><<<grid_item, NT, 0, s>>>(g);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    {
+      KTimer t("tip_score", s);
+      e = g.bf16 ? launch_tip_v<uint16_t, false>(g, grid_tip, s) : launch_tip_v<float, false>(g, grid_tip, s);
+    }
+    if (e != hipSuccess) return e;
+    {
+      KTimer t("select_bin", s);
+      select_bin_kernel<<<grid_item, NT, 0, s>>>(g);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+      KTimer t("select_a", s);
+      select_a_kernel<<<grid_tip, NT, 0, s>>>(g);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+      KTimer t("select_b", s);
+      select_b_kernel<<<grid_item, NT, 0, s>>>(g);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+      KTimer t("select_c", s);
+      select_c_kernel<<<grid_tip, NT, 0, s>>>(g);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   {
-    KTimer t("tip_score", s);
-    e = g.bf16 ? launch_tip_v<uint16_t>(g, grid_tip, s) : launch_tip_v<float>(g, grid_tip, s);
+    g.attn_mode = 1;
+    const int grid_f = clampi(n_att_items * (long long)g.nch_f, 1, g.grid);
+    KTimer t("attention_fac", s);
+    e = launch_attn(g, grid_f, s);
   }
   if (e != hipSuccess) return e;
-  {
-    KTimer t("select_bin", s);
-    select_bin_kernel<<<clampi(n_idx_items, 1, g.grid), NT, 0, s>>>(g);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    KTimer t("select_a", s);
-    select_a_kernel<<<grid_tip, NT, 0, s>>>(g);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    KTimer t("select_b", s);
-    select_b_kernel<<<clampi(n_idx_items, 1, g.grid), NT, 0, s>>>(g);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    KTimer t("select_c", s);
-    select_c_kernel<<<grid_tip, NT, 0, s>>>(g);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long long max_units = n_att_items * (long long)(g.nch_f > g.nch_s ? g.nch_f : g.nch_s);
-  const int grid_attn = clampi(max_units, 1, g.grid);
-  {
-    KTimer t("attention", s);
-    if (g.bf16)
-      e = g.d == 128 ? launch_attn_g<uint16_t, 128>(g, grid_attn, s) : launch_attn_g<uint16_t, 64>(g, grid_attn, s);
-    else
-      e = g.d == 128 ? launch_attn_g<float, 128>(g, grid_attn, s) : launch_attn_g<float, 64>(g, grid_attn, s);
-  }
-  if (e != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(s, ss.join, 0)) != hipSuccess) return e;
   const long long n_out = n_att_items * g.G * g.d;
   {
     KTimer t("merge", s);

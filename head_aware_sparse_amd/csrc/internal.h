@@ -12,6 +12,9 @@ constexpr int kCandLds = 8192;       // candidates held in LDS by the threshold 
 constexpr int kMaxChunkRows = 512;   // attention rows per work unit
 constexpr int kMaxTipChunks = 1024;  // score chunks per item
 constexpr int kMaxPairs = 8192;      // (layer, KV group) pairs per call
+constexpr int kCandFast = 16384;     // candidates per item on the prefiltered path (LDS)
+constexpr int kSampleTokens = 4096;  // tokens scored per item to place the prefilter
+constexpr int kPrefilterMaxT = 131072;  // token bitmap of the prefiltered path lives in LDS
 
 // One decode call, with the workspace carved.  Passed by value to kernels.
 struct Geo {
@@ -29,7 +32,11 @@ struct Geo {
   int n_srows, s_end, w_start;  // streaming rows: [0, s_end) U [w_start, T)
   int nparts;       // partial slots per attention item
   int cand_cap;     // candidate slots per index item
+  int prefilter;    // 1: sample -> candidates above a threshold -> exact select
+  int samp_rank;    // the threshold is the samp_rank-th largest sampled score
+  int bm_words;     // words of the per-item token bitmap (T / 32 rounded up)
   int grid;         // persistent grid size
+  int attn_mode;    // attention launch: 1 = retrieval (FAC) units, 2 = streaming units
   // workspace
   int* plan;         // [4 + 3*kMaxPairs]: n_idx_pairs, n_att_ret, n_att_str, -, lists
   uint32_t* hist;    // [idx items][kHistBins]
@@ -40,6 +47,8 @@ struct Geo {
   uint2* thr;        // [idx items] (key*, token*) selection threshold
   float* scores;     // [idx items][Ts]
   int32_t* idx;      // [idx items][n_fac]
+  uint32_t* tau;     // [idx items] prefilter key threshold
+  uint32_t* bitmap;  // [idx items][bm_words] selected-token bitmap
   float* part;       // [att items][nparts][G][d + 4]: acc[d], m, l
   // inputs / outputs
   const void* q;
@@ -64,7 +73,16 @@ struct KTimer {
   hipStream_t stream;
 };
 
+// The caller's stream plus a library-owned side stream and two events used
+// to run the streaming-group attention concurrently with the retrieval chain.
+struct StreamSet {
+  hipStream_t main;
+  hipStream_t side;
+  hipEvent_t fork;
+  hipEvent_t join;
+};
+
 hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s);
-hipError_t launch_decode(const Geo& g, hipStream_t s);
+hipError_t launch_decode(const Geo& g, const StreamSet& ss);
 
 }  // namespace has
