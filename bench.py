@@ -223,10 +223,11 @@ def main():
 
     out = torch.empty((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), dtype=torch.float32, device="cuda")
     if cfg.clsa:
-        ws = H.shared_index_decode(dims, q, k, v, kd, i_dom, out, labels=None)
+        k0, v0, kd0, id0 = k[0], v[0], kd[0], i_dom[0]
+        ws = H.shared_index_decode(dims, q, k0, v0, kd0, id0, out, labels=None)
 
         def step():
-            H.shared_index_decode(dims, q, k, v, kd, i_dom, out, labels=None, ws=ws)
+            H.shared_index_decode(dims, q, k0, v0, kd0, id0, out, labels=None, ws=ws)
     else:
         ws = H.sparse_decode_step(dims, q, k, v, kd, i_dom, labels, out)
 
