@@ -90,7 +90,7 @@ has_status check_dims(const has_decode_dims* d, bool clsa) {
 struct Layout {
   has::Geo g;
   size_t off_plan, off_hist, off_info, off_cand, off_ngt, off_off, off_thr, off_scores, off_idx, off_part, off_tau,
-      off_bm;
+      off_bm, off_qbar;
   size_t bytes;
 };
 
@@ -129,16 +129,21 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   g.nch_s = (g.n_srows + g.cs - 1) / g.cs;
   g.nparts = g.nch_f > g.nch_s ? g.nch_f : g.nch_s;
   // Prefiltered selection: a sample of kSampleTokens scores places a key
-  // threshold expected to pass about 2 n_fac tokens (+4 sigma of sampling
-  // noise); used when that fits the kCandFast candidate slots comfortably.
+  // threshold expected to pass about 1.25 n_fac tokens plus 4 standard
+  // deviations of the sampled count; used when that fits the kCandFast
+  // candidate slots comfortably.
   {
     const double S = has::kSampleTokens, p = (double)g.n_fac / g.T;
-    const double r = 2.0 * S * p + 4.0 * std::sqrt(S * p) + 16.0;
+    const double r = 1.25 * S * p + 4.0 * std::sqrt(S * p) + 16.0;
     g.samp_rank = (int)std::ceil(r);
     g.prefilter = (g.T >= 2 * has::kSampleTokens && g.T <= has::kPrefilterMaxT && 3LL * g.n_fac <= has::kCandFast &&
                    g.samp_rank < has::kSampleTokens / 2) ? 1 : 0;
   }
   g.cand_cap = g.prefilter ? has::kCandFast : (g.T < has::kCandLds ? g.T : has::kCandLds);
+  // prefiltered scoring units: about 2048 over the worst-case item count,
+  // between 4096 and 16384 tokens
+  g.ct_tip = clampi(pow2_floor((long long)g.T * n_idx / 2048), 4096, 16384);
+  g.nch_tip = (g.T + g.ct_tip - 1) / g.ct_tip;
   g.bm_words = (g.T + 31) / 32;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -158,6 +163,7 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   L.off_part = take((size_t)n_att * g.nparts * g.G * (g.d + 4) * 4);
   L.off_tau = take((size_t)n_idx * 4);
   L.off_bm = take((size_t)n_idx * g.bm_words * 4);
+  L.off_qbar = take((size_t)n_idx * g.R * 4);
   L.bytes = o;
   return L;
 }
@@ -177,6 +183,7 @@ void carve(Layout& L, void* ws) {
   g.part = (float*)(b + L.off_part);
   g.tau = (uint32_t*)(b + L.off_tau);
   g.bitmap = (uint32_t*)(b + L.off_bm);
+  g.qbar = (float*)(b + L.off_qbar);
 }
 
 // Per-device side stream and fork/join events.  The enqueue sequence that

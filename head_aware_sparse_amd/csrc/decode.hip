@@ -272,29 +272,45 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
   constexpr int EPV = Vec<E>::N;
   constexpr int U = V >= 8 ? 2 : 16 / V;  // 64-token steps in flight per wave (16 loads per lane)
   __shared__ uint32_t s_hist[PF ? 1 : kHistBins];
-  constexpr int kCandUnit = 1024;  // candidates staged in LDS per unit; the rest go straight out
+  constexpr int kCandUnit = 2048;  // candidates staged in LDS per unit; the rest go straight out
   __shared__ uint2 s_cand[PF ? kCandUnit : 1];
   __shared__ float s_q[V * EPV];
   __shared__ int s_n;
   __shared__ uint32_t s_base;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_units = plan_idx_pairs(g.plan) * g.B * g.nch_t;
+  const int nch = PF ? g.nch_tip : g.nch_t;
+  const int ct = PF ? g.ct_tip : g.ct;
+  const int n_units = plan_idx_pairs(g.plan) * g.B * nch;
   if constexpr (!PF)
     for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0;
   const int R = V * EPV;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int item = u / g.nch_t, ch = u - item * g.nch_t;
-    __syncthreads();
-    const size_t slice = group_query_dom<E>(g, item, s_q);
-    if (tid == 0) s_n = 0;
-    const uint32_t tau = PF ? g.tau[item] : 0u;
+    const int item = u / nch, ch = u - item * nch;
     __syncthreads();
     float qr[EPV];
+    size_t slice;
+    uint32_t tau = 0u;
+    if constexpr (PF) {
+      // the sample pass stored the group query; each lane reads its slice
+      const int pidx = item / g.B, b = item - pidx * g.B;
+      const int pair = idx_pairs(g)[pidx];
+      const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
+      slice = ((size_t)l * g.B + b) * g.Hkv + gi;
+      const float* qb = g.qbar + (size_t)item * R + (lane % V) * EPV;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
+      for (int e = 0; e < EPV; ++e) qr[e] = qb[e];
+      tau = g.tau[item];
+      if (tid == 0) s_n = 0;
+      __syncthreads();
+    } else {
+      slice = group_query_dom<E>(g, item, s_q);
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
+    }
     const E* kd = (const E*)g.kdom + slice * (size_t)g.T * R;
     float* sc = g.scores + (size_t)item * g.Ts;
-    const int t0 = ch * g.ct, t1 = min(g.T, t0 + g.ct);
+    const int t0 = ch * ct, t1 = min(g.T, t0 + ct);
     for (int base = t0 + wave * 64; base < t1; base += NT * U) {
       uint4 raw[U][V];
 #pragma unroll
@@ -639,6 +655,7 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
     __syncthreads();
     const size_t slice = group_query_dom<E>(g, item, s_q);
     __syncthreads();
+    for (int c = tid; c < R; c += NT) g.qbar[(size_t)item * R + c] = s_q[c];
     float qr[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
@@ -904,18 +921,40 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
   __shared__ float s_ml[G][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane % LPR, rsub = lane / LPR;
+  // Shared-index retrieval units run over (layer n, j = (group, sequence,
+  // chunk)); the block id puts the layers of one j on one XCD (workgroups are
+  // dealt to the 8 XCDs round-robin) and back to back, so the rows gathered
+  // for the first layer are L2 hits for the others.
+  const bool clsa_fac = g.clsa && g.attn_mode == 1;
   const int n_ret = g.attn_mode == 2 ? 0 : g.plan[1];
   const int n_str = g.attn_mode == 1 ? 0 : g.plan[2];
-  const int n_fac_units = n_ret * g.B * g.nch_f;
+  const int J = g.Hkv * g.B * g.nch_f;
+  const int n_fac_units = clsa_fac ? 8 * g.Lq * ((J + 7) / 8) : n_ret * g.B * g.nch_f;
   const int n_units = n_fac_units + n_str * g.B * g.nch_s;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const bool fac = u < n_fac_units;
-    const int uu = fac ? u : u - n_fac_units;
-    const int nchunk = fac ? g.nch_f : g.nch_s;
-    const int item = uu / nchunk, chunk = uu - item * nchunk;
-    const int pa = item / g.B, b = item - pa * g.B;
-    const int pair = fac ? att_ret_pairs(g)[pa] : att_str_pairs(g)[pa];
-    const int lq = pair / g.Hkv, gi = pair - lq * g.Hkv;
+    int lq, gi, b, chunk, pa = 0;
+    if (clsa_fac) {
+      const int rest = u >> 3;
+      const int j = (rest / g.Lq) * 8 + (u & 7);
+      if (j >= J) continue;
+      lq = rest - (rest / g.Lq) * g.Lq;
+      chunk = j % g.nch_f;
+      const int r2 = j / g.nch_f;
+      b = r2 % g.B;
+      gi = r2 / g.B;
+      if (!label_at(g, lq * g.Hkv + gi)) continue;
+    } else {
+      const int uu = fac ? u : u - n_fac_units;
+      const int nchunk = fac ? g.nch_f : g.nch_s;
+      const int item = uu / nchunk;
+      chunk = uu - item * nchunk;
+      pa = item / g.B;
+      b = item - pa * g.B;
+      const int pair = fac ? att_ret_pairs(g)[pa] : att_str_pairs(g)[pa];
+      lq = pair / g.Hkv;
+      gi = pair - lq * g.Hkv;
+    }
     const int lkv = g.clsa ? 0 : lq;
     const size_t kvs = ((size_t)lkv * g.B + b) * g.Hkv + gi;
     const E* kb = (const E*)g.k + kvs * (size_t)g.T * D;
@@ -1193,8 +1232,9 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     }
     if (e != hipSuccess) return e;
     {
+      const int grid_tip_pf = clampi(n_idx_items * g.nch_tip, 1, g.grid);
       KTimer t("tip_score", s);
-      e = g.bf16 ? launch_tip_v<uint16_t, true>(g, grid_tip, s) : launch_tip_v<float, true>(g, grid_tip, s);
+      e = g.bf16 ? launch_tip_v<uint16_t, true>(g, grid_tip_pf, s) : launch_tip_v<float, true>(g, grid_tip_pf, s);
     }
     if (e != hipSuccess) return e;
     {
@@ -1232,7 +1272,8 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   }
   {
     g.attn_mode = 1;
-    const int grid_f = clampi(n_att_items * (long long)g.nch_f, 1, g.grid);
+    const long long fac_units = g.clsa ? 8LL * g.Lq * ((g.Hkv * g.B * g.nch_f + 7) / 8) : n_att_items * (long long)g.nch_f;
+    const int grid_f = clampi(fac_units, 1, g.grid);
     KTimer t("attention_fac", s);
     e = launch_attn(g, grid_f, s);
   }

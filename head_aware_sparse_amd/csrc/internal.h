@@ -48,6 +48,9 @@ struct Geo {
   float* scores;     // [idx items][Ts]
   int32_t* idx;      // [idx items][n_fac]
   uint32_t* tau;     // [idx items] prefilter key threshold
+  float* qbar;       // [idx items][R] group query in k_dom channel order (prefiltered path)
+  int ct_tip;        // tokens per scoring unit on the prefiltered path
+  int nch_tip;       // scoring units per item on the prefiltered path
   uint32_t* bitmap;  // [idx items][bm_words] selected-token bitmap
   float* part;       // [att items][nparts][G][d + 4]: acc[d], m, l
   // inputs / outputs
