@@ -318,7 +318,7 @@ KTimer::KTimer(const char* name, hipStream_t s) : slot(-1), stream(s) {
 KTimer::~KTimer() {
   if (slot < 0) return;
   std::lock_guard<std::mutex> lk(g_tmu);
-  if (slot < (int)g_recs.size()) hipEventRecord(g_recs[slot].b, stream);
+  if (slot < (int)g_recs.size()) (void)hipEventRecord(g_recs[slot].b, stream);
 }
 
 }  // namespace has

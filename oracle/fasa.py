@@ -23,9 +23,12 @@ Readings where the pages leave a step open:
 import numpy as np
 
 
-def fc_channels(i_dom, d_head):
-    """Channel indices of the chunks in i_dom: (f..., f + d/2 ...)."""
+def fc_channels(i_dom, d_head, pairing="rotate_half"):
+    """Channel indices of the chunks in i_dom: (f..., f + d/2 ...) for the
+    rotate-half RoPE layout, (2f..., 2f + 1 ...) for the interleaved one."""
     f = np.asarray(i_dom, dtype=np.int64)
+    if pairing == "interleaved":
+        return np.concatenate([2 * f, 2 * f + 1])
     return np.concatenate([f, f + d_head // 2])
 
 
@@ -34,11 +37,11 @@ def group_query(q_group):
     return np.asarray(q_group, dtype=np.float64).mean(axis=0)
 
 
-def tip_scores(q_group, keys, i_dom):
+def tip_scores(q_group, keys, i_dom, pairing="rotate_half"):
     """Per-token importance: sum over chunks f in I_dom of the 2-D chunk dot
     product between the group query and the key.  keys [T, d] -> [T]."""
     keys = np.asarray(keys, dtype=np.float64)
-    ch = fc_channels(i_dom, keys.shape[1])
+    ch = fc_channels(i_dom, keys.shape[1], pairing)
     return keys[:, ch] @ group_query(q_group)[ch]
 
 
@@ -67,11 +70,11 @@ def attend(q, keys, values):
     return p @ values
 
 
-def decode_group(q_group, keys, values, i_dom, retrieval, n_fac, n_sink, window):
+def decode_group(q_group, keys, values, i_dom, retrieval, n_fac, n_sink, window, pairing="rotate_half"):
     """One (layer, sequence, KV group): (out [G, d], idx [n_fac] or None)."""
     T = keys.shape[0]
     if retrieval:
-        idx = top_n(tip_scores(q_group, keys, i_dom), n_fac)
+        idx = top_n(tip_scores(q_group, keys, i_dom, pairing), n_fac)
     else:
         idx = None
     rows = idx if retrieval else stream_rows(T, n_sink, window)

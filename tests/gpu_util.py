@@ -133,3 +133,9 @@ def oracle_clsa_item(cfg, hi, b, g, labels=None, q_index=None):
         for j in range(G):
             out[n, j] = fasa.attend(f64(hi.q[n, b, g * G + j], cfg), k[rows], v[rows])
     return out, idx, scores
+
+
+def oracle_item_custom(cfg, q_group, k, v, i_dom, retrieval, pairing="rotate_half"):
+    """Oracle for one item from explicit storage-dtype arrays."""
+    return fasa.decode_group(f64(q_group, cfg), f64(k, cfg), f64(v, cfg), i_dom, retrieval, cfg.n_fac, cfg.n_sink,
+                             cfg.window, pairing=pairing)

@@ -153,3 +153,61 @@ def test_device_fill_equals_host_generator():
         assert (k[l, b, g] == case.hi.rows("k", l, b, g)).all()
         assert (v[l, b, g] == case.hi.rows("v", l, b, g)).all()
     assert (k[0, 1, 0] == case.hi.rows("k", 0, 1, 0)).all()
+
+
+def test_interleaved_rope_pairing():
+    """rope_layout = interleaved: chunk f is channels (2f, 2f+1) in k_dom and
+    in the group query (the cache data itself is only data here)."""
+    cfg = R.get_config("c1", ctx_len=9000, n_fac=700, batch=2)
+    print("case interleaved", flush=True)
+    case = U.DeviceCase(cfg)
+    dims = U.dims_of(cfg, rope_layout=1)
+    kd = torch.empty_like(case.k_dom)
+    H.kdom_pack(dims, case.k, case.i_dom, kd)
+    out = torch.empty((1, cfg.batch, cfg.n_q_heads, cfg.d_head), device="cuda")
+    ix = torch.empty((1, cfg.batch, cfg.n_kv_heads, cfg.n_fac), dtype=torch.int32, device="cuda")
+    H.sparse_decode_step(dims, case.q, case.k, case.v, kd, case.i_dom, case.labels, out, ix)
+    torch.cuda.synchronize()
+    out, ix = out.cpu().numpy(), ix.cpu().numpy()
+    G = cfg.group
+    from oracle import fasa
+    for (l, g) in R.planted_groups(cfg):
+        for b in range(cfg.batch):
+            k = U.f64(case.hi.rows("k", l, b, g), cfg)
+            v = U.f64(case.hi.rows("v", l, b, g), cfg)
+            q = U.f64(case.hi.q[l, b, g * G:(g + 1) * G], cfg)
+            ref, ridx = fasa.decode_group(q, k, v, case.hi.i_dom[l, g], True, cfg.n_fac, cfg.n_sink, cfg.window,
+                                          pairing="interleaved")
+            scores = fasa.tip_scores(q, k, case.hi.i_dom[l, g], pairing="interleaved")
+            U.check_index_set(ix[l, b, g], scores, cfg.n_fac, f"interleaved idx b{b} g{g}")
+            U.check_out(out[l, b, g * G:(g + 1) * G], ref, f"interleaved out b{b} g{g}")
+
+
+def test_prefilter_fallback_too_few_candidates():
+    """Adversarial scores: the keys at the sampled token positions are scaled
+    up 40x, so the sample places its threshold far above the true n_fac-th
+    score and fewer than n_fac tokens pass; the selection must fall back to a
+    full rescoring of the item and stay exact."""
+    import numpy as np
+    cfg = R.get_config("c1", ctx_len=32768, batch=1)
+    print("case prefilter fallback", flush=True)
+    hi = R.HostInputs(cfg, with_weights=False)
+    T = cfg.ctx_len
+    sampled = np.concatenate([np.arange(256) + (blk * (T - 256)) // 15 for blk in range(16)])
+    (l, g) = R.planted_groups(cfg)[0]
+    case = U.DeviceCase(cfg, hi=hi)
+    kk = case.k[l, 0, g].float()
+    kk[torch.from_numpy(sampled).cuda()] *= 40.0
+    case.k[l, 0, g] = kk.to(case.k.dtype)
+    H.kdom_pack(case.kd_dims, case.k, case.i_dom, case.k_dom)
+    torch.cuda.synchronize()
+    out, idx, _ = case.run()
+    k_host = case.k[l, 0, g].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert (np.delete(k_host, sampled, axis=0) == np.delete(hi.rows("k", l, 0, g), sampled, axis=0)).all()
+    ref, ridx = U.oracle_item_custom(cfg, hi.q[l, 0, g * cfg.group:(g + 1) * cfg.group], k_host,
+                                     hi.rows("v", l, 0, g), hi.i_dom[l, g], True)
+    from oracle import fasa
+    scores = fasa.tip_scores(U.f64(hi.q[l, 0, g * cfg.group:(g + 1) * cfg.group], cfg), U.f64(k_host, cfg),
+                             hi.i_dom[l, g])
+    U.check_index_set(idx[l, 0, g], scores, cfg.n_fac, "fallback idx")
+    U.check_out(out[l, 0, g * cfg.group:(g + 1) * cfg.group], ref, "fallback out")

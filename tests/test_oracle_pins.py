@@ -288,3 +288,28 @@ def test_shared_index_reuses_the_indexer_selection():
     rows = fasa.stream_rows(T, 2, 5)
     np.testing.assert_allclose(out_l[1, 0, 0], _sdpa(q[1, 0, 0], k[0, 0, rows], v[0, 0, rows]), rtol=1e-12)
     np.testing.assert_allclose(out_l[0], out[0], rtol=1e-12)
+
+
+def test_tip_interleaved_chunk_is_a_rope_rotation_plane():
+    """Same pin for the interleaved RoPE layout: chunk f = channels (2f, 2f+1)."""
+    r = _rng(15)
+    d = 64
+
+    def rope_interleaved(x, pos, base=10000.0):
+        th = base ** (-2.0 * np.arange(d // 2) / d)
+        c, s = np.cos(pos * th), np.sin(pos * th)
+        y = x.copy()
+        y[0::2] = x[0::2] * c - x[1::2] * s
+        y[1::2] = x[1::2] * c + x[0::2] * s
+        return y
+
+    qv, kv = r.standard_normal(d), r.standard_normal(d)
+    for f in [0, 9, 31]:
+        vals = [fasa.tip_scores(rope_interleaved(qv, m)[None], rope_interleaved(kv, n)[None], [f],
+                                pairing="interleaved")[0] for m, n in [(50, 10), (90, 50), (700, 660)]]
+        np.testing.assert_allclose(vals, vals[0], rtol=1e-9, atol=1e-9)
+    # all chunks in either pairing give the exact logit
+    q = r.standard_normal((2, d))
+    k = r.standard_normal((5, d))
+    np.testing.assert_allclose(fasa.tip_scores(q, k, np.arange(d // 2), pairing="interleaved"),
+                               k @ q.mean(axis=0), rtol=1e-12)
