@@ -120,7 +120,8 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   while ((g.T + g.ct - 1) / g.ct > has::kMaxTipChunks && g.ct < 4096) g.ct *= 2;
   g.nch_t = (g.T + g.ct - 1) / g.ct;
   g.Ts = (g.T + 63) / 64 * 64;
-  g.cf = clampi(pow2_floor((long long)g.n_fac * n_att / 2048), 128, has::kMaxChunkRows);
+  g.clsa_mfma = clsa && g.bf16 && g.d == 128 && g.Lq * g.G <= 32;
+  g.cf = g.clsa_mfma ? has::kClsaRows : clampi(pow2_floor((long long)g.n_fac * n_att / 2048), 128, has::kMaxChunkRows);
   g.nch_f = (g.n_fac + g.cf - 1) / g.cf;
   g.s_end = g.n_sink < g.T ? g.n_sink : g.T;
   g.w_start = (g.T - g.window) > g.s_end ? (g.T - g.window) : g.s_end;

@@ -921,40 +921,18 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
   __shared__ float s_ml[G][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane % LPR, rsub = lane / LPR;
-  // Shared-index retrieval units run over (layer n, j = (group, sequence,
-  // chunk)); the block id puts the layers of one j on one XCD (workgroups are
-  // dealt to the 8 XCDs round-robin) and back to back, so the rows gathered
-  // for the first layer are L2 hits for the others.
-  const bool clsa_fac = g.clsa && g.attn_mode == 1;
   const int n_ret = g.attn_mode == 2 ? 0 : g.plan[1];
   const int n_str = g.attn_mode == 1 ? 0 : g.plan[2];
-  const int J = g.Hkv * g.B * g.nch_f;
-  const int n_fac_units = clsa_fac ? 8 * g.Lq * ((J + 7) / 8) : n_ret * g.B * g.nch_f;
+  const int n_fac_units = n_ret * g.B * g.nch_f;
   const int n_units = n_fac_units + n_str * g.B * g.nch_s;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const bool fac = u < n_fac_units;
-    int lq, gi, b, chunk, pa = 0;
-    if (clsa_fac) {
-      const int rest = u >> 3;
-      const int j = (rest / g.Lq) * 8 + (u & 7);
-      if (j >= J) continue;
-      lq = rest - (rest / g.Lq) * g.Lq;
-      chunk = j % g.nch_f;
-      const int r2 = j / g.nch_f;
-      b = r2 % g.B;
-      gi = r2 / g.B;
-      if (!label_at(g, lq * g.Hkv + gi)) continue;
-    } else {
-      const int uu = fac ? u : u - n_fac_units;
-      const int nchunk = fac ? g.nch_f : g.nch_s;
-      const int item = uu / nchunk;
-      chunk = uu - item * nchunk;
-      pa = item / g.B;
-      b = item - pa * g.B;
-      const int pair = fac ? att_ret_pairs(g)[pa] : att_str_pairs(g)[pa];
-      lq = pair / g.Hkv;
-      gi = pair - lq * g.Hkv;
-    }
+    const int uu = fac ? u : u - n_fac_units;
+    const int nchunk = fac ? g.nch_f : g.nch_s;
+    const int item = uu / nchunk, chunk = uu - item * nchunk;
+    const int pa = item / g.B, b = item - pa * g.B;
+    const int pair = fac ? att_ret_pairs(g)[pa] : att_str_pairs(g)[pa];
+    const int lq = pair / g.Hkv, gi = pair - lq * g.Hkv;
     const int lkv = g.clsa ? 0 : lq;
     const size_t kvs = ((size_t)lkv * g.B + b) * g.Hkv + gi;
     const E* kb = (const E*)g.k + kvs * (size_t)g.T * D;
@@ -1100,15 +1078,166 @@ __global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
     const int np = label_at(g, lq * g.Hkv + gi) ? g.nch_f : g.nch_s;
     const float* pp = g.part + (a * g.nparts * g.G + h) * (size_t)dd;
     const size_t stride = (size_t)g.G * dd;
-    float M = -INFINITY;
-    for (int s = 0; s < np; ++s) M = fmaxf(M, pp[s * stride + g.d]);
-    float L = 0.f, O = 0.f;
+    // single pass, online log-sum-exp; partial loads are independent of the
+    // running state, so unrolling keeps several in flight
+    float M = -INFINITY, L = 0.f, O = 0.f;
+#pragma unroll 8
     for (int s = 0; s < np; ++s) {
-      const float w = exp2f(pp[s * stride + g.d] - M);
-      L += w * pp[s * stride + g.d + 1];
-      O += w * pp[s * stride + c];
+      const float* q = pp + s * stride;
+      const float ms = q[g.d], ls = q[g.d + 1], as = q[c];
+      const float Mn = fmaxf(M, ms);
+      const float f_old = exp2f(M - Mn), f_new = exp2f(ms - Mn);
+      L = L * f_old + ls * f_new;
+      O = O * f_old + as * f_new;
+      M = Mn;
     }
     g.out[(((size_t)lq * g.B + b) * g.Hq + (size_t)gi * g.G + h) * g.d + c] = O / L;
+  }
+}
+
+// ------------------------------------------------------------------ CLSA attention
+// Shared-index retrieval attention on the matrix cores.  With one index per
+// (sequence, group) the N layers' G query heads -- QV = N*G <= 32 query
+// vectors -- all attend to the same gathered rows, a dense contraction:
+//   S[qv][row] = Q[qv][:] . K[row][:]       (bf16 MFMA 32x32x16, fp32 sums)
+//   P = softmax over the unit's rows per qv (fp32, in LDS)
+//   O[qv][d]   = sum_row P[qv][row] V[row][d] (fp32 MFMA 32x32x2)
+// One unit = (group, sequence, chunk of kClsaRows = 128 selected rows); its K
+// and V rows are gathered into LDS once.  Wave w owns row block w for S and
+// channel block w for O.  MFMA 32x32: A element (lane%32, k-slice lane/32),
+// B element (k-slice lane/32, lane%32), result (8*(r/4) + 4*(lane/32) +
+// r%4, lane%32) in register r.  Layers labelled streaming for the group are
+// computed and discarded.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kClsaPad = 136;  // bf16 elements per LDS row (128 + 16 B of padding)
+
+__global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
+  constexpr int D = 128;
+  constexpr int ROWS = kClsaRows;
+  constexpr float kScale = 0.08838834764831845f * 1.4426950408889634f;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[ROWS][kClsaPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[ROWS][kClsaPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[32][kClsaPad];
+  __shared__ float s_p[32][ROWS + 1];
+  __shared__ float s_ml[32][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int QV = g.Lq * g.G;
+  const int J = g.Hkv * g.B * g.nch_f;
+  for (int j = blockIdx.x; j < J; j += gridDim.x) {
+    const int chunk = j % g.nch_f;
+    const int r2 = j / g.nch_f;
+    const int b = r2 % g.B, gi = r2 / g.B;
+    const int32_t* ix = g.idx + ((size_t)gi * g.B + b) * g.n_fac + (size_t)chunk * g.cf;
+    const int nrows = min(g.cf, g.n_fac - chunk * g.cf);
+    const size_t kvs = (size_t)b * g.Hkv + gi;
+    const uint16_t* kb = (const uint16_t*)g.k + kvs * (size_t)g.T * D;
+    const uint16_t* vb = (const uint16_t*)g.v + kvs * (size_t)g.T * D;
+    __syncthreads();
+    // gather rows (16 bytes per element e = row * 16 + part), zero padding rows
+    for (int e0 = tid; e0 < ROWS * 16; e0 += 8 * NT) {
+      uint4 rk[8], rv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * NT, r = e >> 4;
+        rk[u] = rv[u] = make_uint4(0, 0, 0, 0);
+        if (r < nrows) {
+          // indices come from the selection and lie in [0, T); the clamp only
+          // keeps a corrupted workspace from turning into out-of-range reads
+          const int row = min(max(ix[r], 0), g.T - 1);
+          rk[u] = ld16_stream(kb + (size_t)row * D + (e & 15) * 8);
+          rv[u] = ld16_stream(vb + (size_t)row * D + (e & 15) * 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * NT, r = e >> 4;
+        *reinterpret_cast<uint4*>(&s_k[r][(e & 15) * 8]) = rk[u];
+        *reinterpret_cast<uint4*>(&s_v[r][(e & 15) * 8]) = rv[u];
+      }
+    }
+    // query vectors qv = n * G + h (zero rows past QV)
+    for (int e = tid; e < 32 * 16; e += NT) {
+      const int qv = e >> 4, part = e & 15;
+      uint4 v4 = make_uint4(0, 0, 0, 0);
+      if (qv < QV) {
+        const int n = qv / g.G, h = qv - n * g.G;
+        v4 = ld16((const uint16_t*)g.q + (((size_t)n * g.B + b) * g.Hq + (size_t)gi * g.G + h) * D + part * 8);
+      }
+      *reinterpret_cast<uint4*>(&s_q[qv][part * 8]) = v4;
+    }
+    __syncthreads();
+    // S = Q K^T for row block `wave`
+    {
+      f32x16_t acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      const int kofs = (lane >> 5) * 8;
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 16) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s_q[lane & 31][k0 + kofs]);
+        const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&s_k[wave * 32 + (lane & 31)][k0 + kofs]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+      }
+      const int row = wave * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qv = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        s_p[qv][row] = row < nrows ? acc[r] * kScale : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // softmax per query vector over the unit's rows (wave w: qv 8w .. 8w+7)
+    for (int qv = wave * 8; qv < wave * 8 + 8; ++qv) {
+      float z0 = s_p[qv][lane], z1 = s_p[qv][lane + 64];
+      const float m = wave_max(fmaxf(z0, z1));
+      const float p0 = exp2f(z0 - m), p1 = exp2f(z1 - m);
+      const float l = wave_sum(p0 + p1);
+      s_p[qv][lane] = p0;
+      s_p[qv][lane + 64] = p1;
+      if (lane == 0) {
+        s_ml[qv][0] = m;
+        s_ml[qv][1] = l;
+      }
+    }
+    __syncthreads();
+    // O = P V for channel block `wave`
+    f32x16_t o;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] = 0.f;
+    {
+      const int dcol = wave * 32 + (lane & 31), ks = lane >> 5;
+#pragma unroll 8
+      for (int k0 = 0; k0 < ROWS; k0 += 2) {
+        const float a = s_p[lane & 31][k0 + ks];
+        const float bv = __uint_as_float((uint32_t)s_v[k0 + ks][dcol] << 16);
+        o = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, o, 0, 0, 0);
+      }
+    }
+    // partials: acc for (layer, head) = qv, channel block `wave`
+    {
+      const int dcol = wave * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qv = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (qv < QV) {
+          const int n = qv / g.G, h = qv - n * g.G;
+          if (label_at(g, n * g.Hkv + gi)) {
+            const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
+            g.part[(((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4) + dcol] = o[r];
+          }
+        }
+      }
+    }
+    if (tid < QV) {
+      const int n = tid / g.G, h = tid - n * g.G;
+      if (label_at(g, n * g.Hkv + gi)) {
+        const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
+        float* pp = g.part + (((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4);
+        pp[D] = s_ml[tid][0];
+        pp[D + 1] = s_ml[tid][1];
+      }
+    }
   }
 }
 
@@ -1272,10 +1401,13 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   }
   {
     g.attn_mode = 1;
-    const long long fac_units = g.clsa ? 8LL * g.Lq * ((g.Hkv * g.B * g.nch_f + 7) / 8) : n_att_items * (long long)g.nch_f;
-    const int grid_f = clampi(fac_units, 1, g.grid);
     KTimer t("attention_fac", s);
-    e = launch_attn(g, grid_f, s);
+    if (g.clsa_mfma) {
+      attn_clsa_mfma_kernel<<<clampi((long long)g.Hkv * g.B * g.nch_f, 1, g.grid), NT, 0, s>>>(g);
+      e = hipGetLastError();
+    } else {
+      e = launch_attn(g, clampi(n_att_items * (long long)g.nch_f, 1, g.grid), s);
+    }
   }
   if (e != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(s, ss.join, 0)) != hipSuccess) return e;

@@ -10,6 +10,7 @@ namespace has {
 constexpr int kHistBins = 2048;      // first radix digit: key bits 31..21
 constexpr int kCandLds = 8192;       // candidates held in LDS by the threshold pass
 constexpr int kMaxChunkRows = 512;   // attention rows per work unit
+constexpr int kClsaRows = 128;       // rows per layer-fused shared-index unit (staged in LDS)
 constexpr int kMaxTipChunks = 1024;  // score chunks per item
 constexpr int kMaxPairs = 8192;      // (layer, KV group) pairs per call
 constexpr int kCandFast = 16384;     // candidates per item on the prefiltered path (LDS)
@@ -23,6 +24,7 @@ struct Geo {
   int R;            // k_dom row elements
   int bf16;         // kv dtype
   int clsa;         // 1: one index per (b, g) shared by Lq layers over one cache
+  int clsa_mfma;    // shared-index retrieval attention on the matrix cores (bf16, d 128, Lq*G <= 32)
   int interleaved;  // rope pairing
   // chunking
   int ct, nch_t;    // score/select chunk tokens and count per item

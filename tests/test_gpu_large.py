@@ -40,7 +40,9 @@ def test_clsa_single_layer_equals_sparse_decode():
     out, idx, _ = U.run_clsa(case)
     out2, idx2, _ = case.run()
     assert (idx2[0] == idx).all()
-    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-6)
+    # same selection; the attention sums differ only in fp32 summation order
+    # (matrix cores in the shared-index mode, vector ALUs in the plain step)
+    np.testing.assert_allclose(out2, out, rtol=1e-4, atol=1e-5)
 
 
 def test_clsa_explicit_indexer_query():
