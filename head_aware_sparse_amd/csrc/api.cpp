@@ -89,7 +89,7 @@ has_status check_dims(const has_decode_dims* d, bool clsa) {
 
 struct Layout {
   has::Geo g;
-  size_t off_plan, off_hist, off_info, off_cand, off_ngt, off_off, off_thr, off_scores, off_idx, off_part, off_tau,
+  size_t off_plan, off_hist, off_info, off_cand, off_ngt, off_off, off_thr, off_scores, off_idx, off_part, off_skeys, off_tau,
       off_bm, off_qbar;
   size_t bytes;
 };
@@ -162,7 +162,8 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   L.off_scores = take((size_t)n_idx * g.Ts * 4);
   L.off_idx = take((size_t)n_idx * g.n_fac * 4);
   L.off_part = take((size_t)n_att * g.nparts * g.G * (g.d + 4) * 4);
-  L.off_tau = take((size_t)n_idx * 4);
+  L.off_skeys = take((size_t)n_idx * has::kSampleTokens * 4);
+  L.off_tau = take((size_t)n_idx * 8);
   L.off_bm = take((size_t)n_idx * g.bm_words * 4);
   L.off_qbar = take((size_t)n_idx * g.R * 4);
   L.bytes = o;
@@ -182,7 +183,8 @@ void carve(Layout& L, void* ws) {
   g.scores = (float*)(b + L.off_scores);
   g.idx = (int32_t*)(b + L.off_idx);
   g.part = (float*)(b + L.off_part);
-  g.tau = (uint32_t*)(b + L.off_tau);
+  g.skeys = (uint32_t*)(b + L.off_skeys);
+  g.tau = (uint2*)(b + L.off_tau);
   g.bitmap = (uint32_t*)(b + L.off_bm);
   g.qbar = (float*)(b + L.off_qbar);
 }

@@ -261,6 +261,84 @@ __device__ __forceinline__ float score_one(const E* row, const float* s_q, int R
 
 constexpr int kMaxR = 128;  // k_dom row elements: 2 * (d/2) at most
 
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t x) {
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+
+__device__ uint2 item_tau(const Geo& g, int item, uint32_t* s_hist, int* s_w, uint32_t* s_res) {
+  constexpr int KPT = kSampleTokens / NT;
+  const uint32_t* sk = g.skeys + (size_t)item * kSampleTokens;
+  uint32_t k[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) k[i] = sk[i * NT + threadIdx.x];
+  uint32_t lo = k[0], hi = k[0];
+#pragma unroll
+  for (int i = 1; i < KPT; ++i) {
+    lo = min(lo, k[i]);
+    hi = max(hi, k[i]);
+  }
+  lo = wave_min_u(lo);
+  hi = wave_max_u(hi);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kHistBins; i += NT) s_hist[i] = 0;
+  if (lane == 0) {
+    s_w[wave] = (int)lo;
+    s_w[NWAVE + wave] = (int)hi;
+  }
+  __syncthreads();
+  for (int w = 0; w < NWAVE; ++w) {
+    lo = min(lo, (uint32_t)s_w[w]);
+    hi = max(hi, (uint32_t)s_w[NWAVE + w]);
+  }
+  const uint32_t span = hi - lo;
+  const int bits = span ? 32 - __clz(span) : 0;
+  const int sh = bits > 11 ? bits - 11 : 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) atomicAdd(&s_hist[(k[i] - lo) >> sh], 1u);
+  __syncthreads();
+  int bin;
+  uint32_t above;
+  find_bin_top(s_hist, kHistBins, (uint32_t)g.samp_rank, s_w, s_res, bin, above);
+  uint32_t tau = lo + ((uint32_t)bin << sh);
+  if (sh > 0) {
+    // second digit inside that bin
+    const int sh2 = sh > 11 ? sh - 11 : 0;
+    const uint32_t b1 = (uint32_t)bin;
+    for (int i = threadIdx.x; i < kHistBins; i += NT) s_hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (((k[i] - lo) >> sh) == b1) atomicAdd(&s_hist[((k[i] - lo) >> sh2) & (kHistBins - 1)], 1u);
+    __syncthreads();
+    find_bin_top(s_hist, kHistBins, (uint32_t)g.samp_rank - above, s_w, s_res, bin, above);
+    tau += (uint32_t)bin << sh2;
+  }
+  return make_uint2(tau, hi);
+}
+
+// tau: per index item, the candidate threshold from its sampled keys -- the
+// lower edge of the bin, of two range-relative 11-bit digits, that holds the
+// samp_rank-th largest sampled key (so at least samp_rank sampled keys are
+// >= tau; the final selection is exact whatever tau is) -- and the largest
+// sampled key.
+__global__ __launch_bounds__(NT) void tau_kernel(Geo g) {
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ int s_w[2 * NWAVE];
+  __shared__ uint32_t s_res[2];
+  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    __syncthreads();
+    const uint2 t = item_tau(g, item, s_hist, s_w, s_res);
+    if (threadIdx.x == 0) g.tau[item] = t;
+  }
+}
+
+
 // ------------------------------------------------------------------ TIP
 // One unit = (index item, chunk of ct tokens).  A wave scores 64 tokens per
 // step: lane L loads 16 bytes of row (L / V) of each of V consecutive
@@ -299,7 +377,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
       const float* qb = g.qbar + (size_t)item * R + (lane % V) * EPV;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) qr[e] = qb[e];
-      tau = g.tau[item];
+      tau = g.tau[item].x;
       if (tid == 0) s_n = 0;
       __syncthreads();
     } else {
@@ -490,23 +568,25 @@ __device__ void histogram(const Src& src, uint32_t* s_hist, int nbins, Pred pred
   __syncthreads();
 }
 
+// Sources of (key, token) elements for the selection helpers.  for_each
+// visits each element once, in the calling thread's strided share; reads are
+// issued four at a time so their latencies overlap.
+
 // (key, token) pairs held in LDS.
 struct LdsPairs {
   const uint2* p;
   int n;
   template <class F>
   __device__ __forceinline__ void for_each(F f) const {
-    for (int i = threadIdx.x; i < n; i += NT) f(p[i].x, p[i].y);
-  }
-};
-
-// Keys held in LDS, the position standing in for the token.
-struct LdsKeys {
-  const uint32_t* k;
-  int n;
-  template <class F>
-  __device__ __forceinline__ void for_each(F f) const {
-    for (int i = threadIdx.x; i < n; i += NT) f(k[i], (uint32_t)i);
+    int i = threadIdx.x;
+    for (; i + 3 * NT < n; i += 4 * NT) {
+      const uint2 a = p[i], b = p[i + NT], c = p[i + 2 * NT], d = p[i + 3 * NT];
+      f(a.x, a.y);
+      f(b.x, b.y);
+      f(c.x, c.y);
+      f(d.x, d.y);
+    }
+    for (; i < n; i += NT) f(p[i].x, p[i].y);
   }
 };
 
@@ -516,18 +596,17 @@ struct ScoreScan {
   int T;
   template <class F>
   __device__ __forceinline__ void for_each(F f) const {
-    for (int t = threadIdx.x; t < T; t += NT) f(f2key(sc[t]), (uint32_t)t);
+    int t = threadIdx.x;
+    for (; t + 3 * NT < T; t += 4 * NT) {
+      const float a = sc[t], b = sc[t + NT], c = sc[t + 2 * NT], d = sc[t + 3 * NT];
+      f(f2key(a), (uint32_t)t);
+      f(f2key(b), (uint32_t)(t + NT));
+      f(f2key(c), (uint32_t)(t + 2 * NT));
+      f(f2key(d), (uint32_t)(t + 3 * NT));
+    }
+    for (; t < T; t += NT) f(f2key(sc[t]), (uint32_t)t);
   }
 };
-
-__device__ __forceinline__ uint32_t wave_min_u(uint32_t x) {
-  for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
-}
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
-}
 
 // Workgroup min and max of the keys of src (every thread gets both).
 template <class Src>
@@ -556,13 +635,51 @@ __device__ void key_range(const Src& src, uint32_t* s_res, uint32_t& lo, uint32_
   (void)s_res;
 }
 
-// The need-th element of src in the order (key desc, token asc).  Keys are
-// resolved in at most three radix digits taken over the span [lo, hi] of
-// the keys present (so the first digit spreads them over its 2048 bins);
-// then, among the elements equal to that key, the need-th smallest token
-// (WITH_TOKEN): directly when all of them are selected, else by three more
-// 10-bit digits.
-template <bool WITH_TOKEN, class Src>
+constexpr int kRankMax = 256;  // bin size resolved by direct ranking
+
+// The element of rank need-1 (0-based) in the order (key desc, token asc)
+// among the elements whose key satisfies ((key - lo) >> sh) == pre; there
+// are at most kRankMax of them.  Each counts the members ordered before it.
+template <class Src>
+__device__ void rank_in_bin(const Src& src, uint32_t lo, int sh, uint32_t pre, uint32_t need, uint32_t* s_res,
+                            uint32_t& kstar, uint32_t& tstar) {
+  __shared__ uint2 s_list[kRankMax];
+  __shared__ int s_m;
+  if (threadIdx.x == 0) s_m = 0;
+  __syncthreads();
+  src.for_each([&](uint32_t k, uint32_t t) {
+    if (((k - lo) >> sh) == pre) s_list[atomicAdd(&s_m, 1)] = make_uint2(k, t);
+  });
+  __syncthreads();
+  const int m = s_m;
+  for (int i = threadIdx.x; i < m; i += NT) {
+    const uint2 me = s_list[i];
+    uint32_t r = 0;
+#pragma unroll 8
+    for (int j = 0; j < m; ++j) {
+      const uint2 o = s_list[j];
+      r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+    }
+    if (r == need - 1) {
+      s_res[0] = me.x;
+      s_res[1] = me.y;
+    }
+  }
+  __syncthreads();
+  kstar = s_res[0];
+  tstar = s_res[1];
+  __syncthreads();
+}
+
+// The need-th element of src in the order (key desc, token asc), as (key*,
+// token*).  Keys are resolved by radix digits of at most 11 bits taken over
+// the span [lo, hi] of the keys present (so the first digit spreads them over
+// its 2048 bins).  As soon as the bin holding the element has at most
+// kRankMax members it is resolved by ranking them directly; otherwise the
+// digits run out at key*, and the need-th smallest token among the elements
+// equal to key* follows: directly when all of them are selected, else by
+// three more 10-bit digits.
+template <class Src>
 __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist, int* s_w, uint32_t* s_res,
                                 uint32_t& kstar, uint32_t& tstar) {
   uint32_t lo, hi;
@@ -583,122 +700,118 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
     int bin;
     uint32_t above;
     find_bin_top(s_hist, nbins, need, s_w, s_res, bin, above);
+    const uint32_t members = s_hist[bin];
+    __syncthreads();
     need -= above;
     pre = (pre << w) | (uint32_t)bin;
+    if (rem > 0 && members <= (uint32_t)kRankMax) {
+      rank_in_bin(src, lo, sh, pre, need, s_res, kstar, tstar);
+      return;
+    }
   }
   kstar = lo + pre;
   tstar = 0;
-  if constexpr (WITH_TOKEN) {
-    const uint32_t ks = kstar;
-    // how many elements carry kstar, and the largest such token
-    __shared__ uint32_t s_eq[2 * NWAVE];
-    uint32_t n_eq = 0, t_max = 0;
-    src.for_each([&](uint32_t k, uint32_t t) {
-      if (k == ks) {
-        ++n_eq;
-        t_max = max(t_max, t);
-      }
-    });
-    for (int o = 32; o >= 1; o >>= 1) {
-      n_eq += (uint32_t)__shfl_xor((int)n_eq, o);
-      t_max = max(t_max, (uint32_t)__shfl_xor((int)t_max, o));
+  const uint32_t ks = kstar;
+  // how many elements carry kstar, and the largest such token
+  __shared__ uint32_t s_eq[2 * NWAVE];
+  uint32_t n_eq = 0, t_max = 0;
+  src.for_each([&](uint32_t k, uint32_t t) {
+    if (k == ks) {
+      ++n_eq;
+      t_max = max(t_max, t);
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane == 0) {
-      s_eq[wave] = n_eq;
-      s_eq[NWAVE + wave] = t_max;
+  });
+  for (int o = 32; o >= 1; o >>= 1) {
+    n_eq += (uint32_t)__shfl_xor((int)n_eq, o);
+    t_max = max(t_max, (uint32_t)__shfl_xor((int)t_max, o));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    s_eq[wave] = n_eq;
+    s_eq[NWAVE + wave] = t_max;
+  }
+  __syncthreads();
+  n_eq = 0;
+  t_max = 0;
+  for (int w = 0; w < NWAVE; ++w) {
+    n_eq += s_eq[w];
+    t_max = max(t_max, s_eq[NWAVE + w]);
+  }
+  if (need == n_eq) {
+    tstar = t_max;
+  } else {
+    uint32_t tpre = 0;
+    for (int shift = 20; shift >= 0; shift -= 10) {
+      const uint32_t hmask = (shift == 20) ? 0u : (0xFFFFFFFFu << (shift + 10));
+      histogram(src, s_hist, 1024, [=](uint32_t k, uint32_t t) { return k == ks && (t & hmask) == tpre; },
+                [=](uint32_t, uint32_t t) { return 1023u - ((t >> shift) & 0x3FFu); });
+      int bin;
+      uint32_t above;
+      find_bin_top(s_hist, 1024, need, s_w, s_res, bin, above);
+      need -= above;
+      tpre |= (1023u - (uint32_t)bin) << shift;
     }
-    __syncthreads();
-    n_eq = 0;
-    t_max = 0;
-    for (int w = 0; w < NWAVE; ++w) {
-      n_eq += s_eq[w];
-      t_max = max(t_max, s_eq[NWAVE + w]);
-    }
-    if (need == n_eq) {
-      tstar = t_max;
-    } else {
-      uint32_t tpre = 0;
-      for (int shift = 20; shift >= 0; shift -= 10) {
-        const uint32_t hmask = (shift == 20) ? 0u : (0xFFFFFFFFu << (shift + 10));
-        histogram(src, s_hist, 1024, [=](uint32_t k, uint32_t t) { return k == ks && (t & hmask) == tpre; },
-                  [=](uint32_t, uint32_t t) { return 1023u - ((t >> shift) & 0x3FFu); });
-        int bin;
-        uint32_t above;
-        find_bin_top(s_hist, 1024, need, s_w, s_res, bin, above);
-        need -= above;
-        tpre |= (1023u - (uint32_t)bin) << shift;
-      }
-      tstar = tpre;
-    }
+    tstar = tpre;
   }
 }
 
-// sample: per index item, TIP scores of kSampleTokens tokens in 16 evenly
-// spread blocks of 256 (each wave scores 64 tokens per block with the same
-// lane layout as tip_kernel); the samp_rank-th largest sampled key becomes
-// the item's candidate threshold tau (tokens with key >= tau are candidates).
+// sample: TIP keys of kSampleTokens tokens per index item, in 16 evenly
+// spread blocks of 256; one unit = (item, block), each wave scoring 64 tokens
+// with the same lane layout as tip_kernel.  Block 0 also stores the item's
+// group query for the scoring pass.
 template <typename E, int V>
 __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
   constexpr int EPV = Vec<E>::N;
   constexpr int kBlocks = kSampleTokens / 256;
   __shared__ float s_q[kMaxR];
-  __shared__ uint32_t s_key[kSampleTokens];
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ int s_w[NWAVE];
-  __shared__ uint32_t s_res[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = V * EPV;
-  const int n_items = plan_idx_pairs(g.plan) * g.B;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  const int n_units = plan_idx_pairs(g.plan) * g.B * kBlocks;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int item = u / kBlocks, blk = u - item * kBlocks;
     __syncthreads();
     const size_t slice = group_query_dom<E>(g, item, s_q);
     __syncthreads();
-    for (int c = tid; c < R; c += NT) g.qbar[(size_t)item * R + c] = s_q[c];
+    if (blk == 0)
+      for (int c = tid; c < R; c += NT) g.qbar[(size_t)item * R + c] = s_q[c];
     float qr[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
     const E* kd = (const E*)g.kdom + slice * (size_t)g.T * R;
-    for (int blk0 = 0; blk0 < kBlocks; blk0 += 2) {
-      uint4 raw[2][V];
+    const int start = (int)((long long)blk * (g.T - 256) / (kBlocks - 1));
+    uint4 raw[V];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int start = (int)((long long)(blk0 + j) * (g.T - 256) / (kBlocks - 1));
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          const int tok = start + wave * 64 + i * (64 / V) + lane / V;
-          raw[j][i] = ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float mine = 0.f;
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          float kv[EPV];
-          Vec<E>::cvt(raw[j][i], kv);
-          float sum = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) sum += qr[e] * kv[e];
-          sum = group_sum<V>(sum);
-          if ((lane % V) == i) mine = sum;
-        }
-        s_key[(blk0 + j) * 256 + wave * 64 + lane] = f2key(mine);
-      }
+    for (int i = 0; i < V; ++i) {
+      const int tok = start + wave * 64 + i * (64 / V) + lane / V;
+      raw[i] = ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV);
     }
-    __syncthreads();
-    uint32_t kr, unused;
-    exact_threshold<false>(LdsKeys{s_key, kSampleTokens}, (uint32_t)g.samp_rank, s_hist, s_w, s_res, kr, unused);
-    if (tid == 0) g.tau[item] = kr;
+    float mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float kv[EPV];
+      Vec<E>::cvt(raw[i], kv);
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) sum += qr[e] * kv[e];
+      sum = group_sum<V>(sum);
+      if ((lane % V) == i) mine = sum;
+    }
+    g.skeys[(size_t)item * kSampleTokens + blk * 256 + wave * 64 + lane] = f2key(mine);
   }
 }
 
 // final: per index item, the exact top-n_fac among the candidates (key >=
-// tau) held in LDS.  If the candidates are fewer than n_fac or overflowed,
-// the item is rescored in full here and selected from its score row (exact
-// either way).  The selected tokens are marked in an LDS bitmap and emitted
-// in ascending order.
+// tau) held in LDS.  While the candidates load, they are counted in 2048
+// bins of (key - tau) >> sh, sh sized so the largest sampled key falls in the
+// top bin (larger keys are clamped into it); the bin holding the n_fac-th
+// candidate is resolved by ranking its members when it has at most kRankMax
+// of them and is not the clamped top bin, else by the general radix
+// threshold.  If the candidates are fewer than n_fac or overflowed, the item
+// is rescored in full here and selected from its score row (exact either
+// way).  The selected tokens are marked in an LDS bitmap; a token's output
+// slot is the number of marked tokens before it, from per-word prefix
+// counts, which emits the selection in ascending order.
 template <typename E>
 __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
   __shared__ uint2 s_c[kCandFast];
@@ -707,15 +820,56 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
   __shared__ float s_q[kMaxR];
   __shared__ int s_w[NWAVE];
   __shared__ uint32_t s_res[2];
+  static_assert(kHistBins * sizeof(uint32_t) >= (kPrefilterMaxT / 32) * sizeof(uint16_t), "u16 prefix alias");
+  static_assert(kCandFast * sizeof(uint2) >= (kPrefilterMaxT / 32) * sizeof(uint32_t), "u32 prefix alias");
+  static_assert(kCandFast / 3 < 65536, "prefiltered n_fac fits u16 prefixes");
   const int tid = threadIdx.x;
   const int n_items = plan_idx_pairs(g.plan) * g.B;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     __syncthreads();
     const uint32_t count = g.info[(size_t)item * 4 + 2];
+    const uint2 th = g.tau[item];
     for (int w = tid; w < g.bm_words; w += NT) s_bm[w] = 0u;
-    uint32_t kstar, tstar;
+    for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+    const int pidx = item / g.B, b = item - pidx * g.B;
+    const int pair = idx_pairs(g)[pidx];
+    const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
+    int32_t* ix = g.idx + (size_t)item * g.n_fac;
+    int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
+    // marks the selected tokens, then writes each to its slot; s_pre holds
+    // the per-word prefix counts (bm_words entries, in LDS no longer needed)
+    auto emit = [&](const auto& src, uint32_t kstar, uint32_t tstar, auto* s_pre) {
+      src.for_each([&](uint32_t k, uint32_t t) {
+        if (k > kstar || (k == kstar && t <= tstar)) atomicOr(&s_bm[t >> 5], 1u << (t & 31));
+      });
+      __syncthreads();
+      const int per = (g.bm_words + NT - 1) / NT;
+      const int w0 = min(g.bm_words, tid * per), w1 = min(g.bm_words, w0 + per);
+      int cnt = 0;
+      for (int w = w0; w < w1; ++w) cnt += __popc(s_bm[w]);
+      int tot;
+      uint32_t run = (uint32_t)block_excl_scan(cnt, s_w, tot);
+      for (int w = w0; w < w1; ++w) {
+        s_pre[w] = run;  // < n_fac, which fits the prefix type
+        run += __popc(s_bm[w]);
+      }
+      __syncthreads();
+      src.for_each([&](uint32_t k, uint32_t t) {
+        if (k > kstar || (k == kstar && t <= tstar)) {
+          const uint32_t pos = s_pre[t >> 5] + __popc(s_bm[t >> 5] & ((1u << (t & 31)) - 1u));
+          ix[pos] = (int32_t)t;
+          if (ox) ox[pos] = (int32_t)t;
+        }
+      });
+    };
     if (count >= (uint32_t)g.n_fac && count <= (uint32_t)g.cand_cap) {
-      // candidates -> LDS, two per 16-byte load, eight loads in flight
+      const uint32_t tau = th.x;
+      const uint32_t span = th.y > tau ? th.y - tau : 0u;
+      const int bits = span ? 32 - __clz(span) : 0;
+      const int sh = bits > 11 ? bits - 11 : 0;
+      __syncthreads();
+      // candidates -> LDS, two per 16-byte load, eight loads in flight,
+      // counted by their first digit on the way
       const uint4* c4 = reinterpret_cast<const uint4*>(g.cand + (size_t)item * g.cand_cap);
       const int n4 = (int)(count + 1) / 2;
       for (int i0 = tid; i0 < n4; i0 += 8 * NT) {
@@ -727,16 +881,28 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
           const int i = i0 + j * NT;
           if (i < n4) {
             s_c[2 * i] = make_uint2(r[j].x, r[j].y);
-            if (2 * i + 1 < (int)count) s_c[2 * i + 1] = make_uint2(r[j].z, r[j].w);
+            atomicAdd(&s_hist[min((r[j].x - tau) >> sh, (uint32_t)kHistBins - 1u)], 1u);
+            if (2 * i + 1 < (int)count) {
+              s_c[2 * i + 1] = make_uint2(r[j].z, r[j].w);
+              atomicAdd(&s_hist[min((r[j].z - tau) >> sh, (uint32_t)kHistBins - 1u)], 1u);
+            }
           }
         }
       }
       __syncthreads();
       const LdsPairs src{s_c, (int)count};
-      exact_threshold<true>(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
-      src.for_each([&](uint32_t k, uint32_t t) {
-        if (k > kstar || (k == kstar && t <= tstar)) atomicOr(&s_bm[t >> 5], 1u << (t & 31));
-      });
+      int bin;
+      uint32_t above;
+      find_bin_top(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, bin, above);
+      const uint32_t members = s_hist[bin];
+      __syncthreads();
+      uint32_t kstar, tstar;
+      if (bin < kHistBins - 1 && members <= (uint32_t)kRankMax)
+        rank_in_bin(src, tau, sh, (uint32_t)bin, (uint32_t)g.n_fac - above, s_res, kstar, tstar);
+      else
+        exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+      // the threshold's histogram is free by then; n_fac < 2^16 here
+      emit(src, kstar, tstar, reinterpret_cast<uint16_t*>(s_hist));
     } else {
       const size_t slice = group_query_dom<E>(g, item, s_q);
       __syncthreads();
@@ -746,35 +912,9 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
       __threadfence();
       __syncthreads();
       const ScoreScan src{sc, g.T};
-      exact_threshold<true>(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
-      src.for_each([&](uint32_t k, uint32_t t) {
-        if (k > kstar || (k == kstar && t <= tstar)) atomicOr(&s_bm[t >> 5], 1u << (t & 31));
-      });
-    }
-    __syncthreads();
-    // ordered emission: each thread owns a contiguous run of bitmap words
-    const int per = (g.bm_words + NT - 1) / NT;
-    const int w0 = min(g.bm_words, tid * per), w1 = min(g.bm_words, w0 + per);
-    int cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(s_bm[w]);
-    int tot;
-    uint32_t pos = (uint32_t)block_excl_scan(cnt, s_w, tot);
-    const int pidx = item / g.B, b = item - pidx * g.B;
-    const int pair = idx_pairs(g)[pidx];
-    const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
-    int32_t* ix = g.idx + (size_t)item * g.n_fac;
-    int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
-    for (int w = w0; w < w1; ++w) {
-      uint32_t bits = s_bm[w];
-      while (bits) {
-        const int t = w * 32 + __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (pos < (uint32_t)g.n_fac) {
-          ix[pos] = t;
-          if (ox) ox[pos] = t;
-        }
-        ++pos;
-      }
+      uint32_t kstar, tstar;
+      exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+      emit(src, kstar, tstar, reinterpret_cast<uint32_t*>(s_c));
     }
   }
 }
@@ -1357,9 +1497,15 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   if (g.prefilter) {
     {
       KTimer t("sample", s);
-      e = g.bf16 ? launch_sample_v<uint16_t>(g, grid_item, s) : launch_sample_v<float>(g, grid_item, s);
+      const int grid_sample = clampi(n_idx_items * (kSampleTokens / 256), 1, g.grid);
+      e = g.bf16 ? launch_sample_v<uint16_t>(g, grid_sample, s) : launch_sample_v<float>(g, grid_sample, s);
     }
     if (e != hipSuccess) return e;
+    {
+      KTimer t("tau", s);
+      tau_kernel<<<grid_item, NT, 0, s>>>(g);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     {
       const int grid_tip_pf = clampi(n_idx_items * g.nch_tip, 1, g.grid);
       KTimer t("tip_score", s);

@@ -49,7 +49,8 @@ struct Geo {
   uint2* thr;        // [idx items] (key*, token*) selection threshold
   float* scores;     // [idx items][Ts]
   int32_t* idx;      // [idx items][n_fac]
-  uint32_t* tau;     // [idx items] prefilter key threshold
+  uint32_t* skeys;   // [idx items][kSampleTokens] sampled TIP keys (prefiltered path)
+  uint2* tau;        // [idx items] candidate key threshold and largest sampled key (prefiltered path)
   float* qbar;       // [idx items][R] group query in k_dom channel order (prefiltered path)
   int ct_tip;        // tokens per scoring unit on the prefiltered path
   int nch_tip;       // scoring units per item on the prefiltered path
@@ -83,8 +84,8 @@ struct KTimer {
 struct StreamSet {
   hipStream_t main;
   hipStream_t side;
-  hipEvent_t fork;
-  hipEvent_t join;
+  hipEvent_t fork;  // main -> side: the plan is ready
+  hipEvent_t join;  // side -> main: streaming attention is done
 };
 
 hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s);

@@ -211,3 +211,39 @@ def test_prefilter_fallback_too_few_candidates():
                              hi.i_dom[l, g])
     U.check_index_set(idx[l, 0, g], scores, cfg.n_fac, "fallback idx")
     U.check_out(out[l, 0, g * cfg.group:(g + 1) * cfg.group], ref, "fallback out")
+
+
+@pytest.mark.parametrize("shared_q,levels", [(True, 1), (False, 2)], ids=["coarse-ties", "fine-ties"])
+def test_tied_scores_select_exactly(shared_q, levels):
+    """Integer-valued cache rows and queries make the TIP scores exact small
+    multiples of 1/G with hundreds to thousands of tokens on each value, so
+    the n_fac-th score is shared by many tokens (ties go to the lower index)
+    and the bin that holds it is crowded: the selection must stay exact."""
+    cfg = R.get_config("c1", ctx_len=32768, batch=1)
+    print(f"case ties shared_q={shared_q} levels={levels}", flush=True)
+    hi = R.HostInputs(cfg, with_weights=False)
+    (l, g) = R.planted_groups(cfg)[0]
+    G = cfg.group
+    rng = np.random.default_rng(7 + levels)
+    case = U.DeviceCase(cfg, hi=hi)
+    k_int = rng.integers(-levels, levels + 1, size=(cfg.ctx_len, cfg.d_head)).astype(np.float32)
+    q_int = rng.integers(-levels, levels + 1, size=(G, cfg.d_head)).astype(np.float32)
+    if shared_q:
+        q_int[:] = q_int[0]
+    case.k[l, 0, g] = torch.from_numpy(k_int).to(case.k.dtype).cuda()
+    case.q[l, 0, g * G:(g + 1) * G] = torch.from_numpy(q_int).to(case.q.dtype).cuda()
+    H.kdom_pack(case.kd_dims, case.k, case.i_dom, case.k_dom)
+    torch.cuda.synchronize()
+    out, idx, _ = case.run()
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    k_host, q_host = bits(case.k[l, 0, g]), bits(case.q[l, 0, g * G:(g + 1) * G])
+    assert (U.f64(k_host, cfg) == k_int).all() and (U.f64(q_host, cfg) == q_int).all()
+    from oracle import fasa
+    scores = fasa.tip_scores(U.f64(q_host, cfg), U.f64(k_host, cfg), hi.i_dom[l, g])
+    sk = -np.sort(-scores)[cfg.n_fac - 1]
+    assert (scores == sk).sum() > 50, "the case must tie many tokens at the threshold"
+    # exact ties: the set is unique under (score desc, index asc)
+    want = np.sort(fasa.top_n(scores, cfg.n_fac))
+    assert (idx[l, 0, g] == want).all()
+    ref, _ = U.oracle_item_custom(cfg, q_host, k_host, hi.rows("v", l, 0, g), hi.i_dom[l, g], True)
+    U.check_out(out[l, 0, g * G:(g + 1) * G], ref, "ties out")
