@@ -55,6 +55,17 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Max over aligned groups of N (<= 16) consecutive lanes, as group_sum.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<0xB1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
+  static_assert(N <= 16, "group_max covers one DPP row");
+  return x;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
@@ -1241,26 +1252,39 @@ __global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
 // vectors -- all attend to the same gathered rows, a dense contraction:
 //   S[qv][row] = Q[qv][:] . K[row][:]       (bf16 MFMA 32x32x16, fp32 sums)
 //   P = softmax over the unit's rows per qv (fp32, in LDS)
-//   O[qv][d]   = sum_row P[qv][row] V[row][d] (fp32 MFMA 32x32x2)
-// One unit = (group, sequence, chunk of kClsaRows = 128 selected rows); its K
-// and V rows are gathered into LDS once.  Wave w owns row block w for S and
-// channel block w for O.  MFMA 32x32: A element (lane%32, k-slice lane/32),
-// B element (k-slice lane/32, lane%32), result (8*(r/4) + 4*(lane/32) +
-// r%4, lane%32) in register r.  Layers labelled streaming for the group are
-// computed and discarded.
+//   O[qv][d]   = sum_row P[qv][row] V[row][d]
+// P V also runs on bf16 MFMA: P = P_hi + P_lo with both halves rounded to
+// bf16, so the product keeps about 16 bits of P (V is bf16 already) and
+// accumulates in fp32.  One unit = (group, sequence, chunk of kClsaRows =
+// 128 selected rows); its K and V rows are gathered into LDS once, and P
+// reuses the K tile's LDS once S is computed.  Wave w owns row block w for S
+// and channel block w for O.  MFMA 32x32: A element (lane%32, k-slice
+// lane/32), B element (k-slice lane/32, lane%32), result (8*(r/4) +
+// 4*(lane/32) + r%4, lane%32) in register r.  Layers labelled streaming for
+// the group are computed and discarded.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-constexpr int kClsaPad = 136;  // bf16 elements per LDS row (128 + 16 B of padding)
+constexpr int kClsaPad = 136;          // bf16 elements per K/V/Q LDS row (128 + 16 B of padding)
+constexpr int kPPad = kClsaRows + 4;   // floats per P row (16-byte aligned rows)
+
+// bf16 bits of x rounded to nearest even (x finite)
+__device__ __forceinline__ unsigned short bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
 
 __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
   constexpr int D = 128;
   constexpr int ROWS = kClsaRows;
   constexpr float kScale = 0.08838834764831845f * 1.4426950408889634f;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[ROWS][kClsaPad];
+  static_assert(32 * kPPad * sizeof(float) <= ROWS * kClsaPad * sizeof(uint16_t), "P fits the K tile");
+  __shared__ __attribute__((aligned(16))) uint16_t s_kp[ROWS * kClsaPad];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[ROWS][kClsaPad];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[32][kClsaPad];
-  __shared__ float s_p[32][ROWS + 1];
   __shared__ float s_ml[32][2];
+  uint16_t (*s_k)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(s_kp);
+  float (*s_p)[kPPad] = reinterpret_cast<float (*)[kPPad]>(s_kp);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int QV = g.Lq * g.G;
   const int J = g.Hkv * g.B * g.nch_f;
@@ -1307,7 +1331,7 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
       *reinterpret_cast<uint4*>(&s_q[qv][part * 8]) = v4;
     }
     __syncthreads();
-    // S = Q K^T for row block `wave`
+    // S = Q K^T for row block `wave`, then (the K tile being free) into s_p
     {
       f32x16_t acc;
 #pragma unroll
@@ -1319,6 +1343,7 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
         const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&s_k[wave * 32 + (lane & 31)][k0 + kofs]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
       }
+      __syncthreads();
       const int row = wave * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -1327,31 +1352,60 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
       }
     }
     __syncthreads();
-    // softmax per query vector over the unit's rows (wave w: qv 8w .. 8w+7)
-    for (int qv = wave * 8; qv < wave * 8 + 8; ++qv) {
-      float z0 = s_p[qv][lane], z1 = s_p[qv][lane + 64];
-      const float m = wave_max(fmaxf(z0, z1));
-      const float p0 = exp2f(z0 - m), p1 = exp2f(z1 - m);
-      const float l = wave_sum(p0 + p1);
-      s_p[qv][lane] = p0;
-      s_p[qv][lane + 64] = p1;
-      if (lane == 0) {
+    // softmax: 8 consecutive lanes per query vector, 16 rows each
+    {
+      const int qv = tid >> 3, seg = tid & 7;
+      float4* pr = reinterpret_cast<float4*>(&s_p[qv][seg * 16]);
+      float z[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v4 = pr[i];
+        z[4 * i] = v4.x;
+        z[4 * i + 1] = v4.y;
+        z[4 * i + 2] = v4.z;
+        z[4 * i + 3] = v4.w;
+      }
+      float m = z[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, z[i]);
+      m = group_max<8>(m);
+      float l = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        z[i] = exp2f(z[i] - m);
+        l += z[i];
+      }
+      l = group_sum<8>(l);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = make_float4(z[4 * i], z[4 * i + 1], z[4 * i + 2], z[4 * i + 3]);
+      if (seg == 0) {
         s_ml[qv][0] = m;
         s_ml[qv][1] = l;
       }
     }
     __syncthreads();
-    // O = P V for channel block `wave`
+    // O = P V for channel block `wave`, P split into bf16 hi + lo
     f32x16_t o;
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[r] = 0.f;
     {
-      const int dcol = wave * 32 + (lane & 31), ks = lane >> 5;
-#pragma unroll 8
-      for (int k0 = 0; k0 < ROWS; k0 += 2) {
-        const float a = s_p[lane & 31][k0 + ks];
-        const float bv = __uint_as_float((uint32_t)s_v[k0 + ks][dcol] << 16);
-        o = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv, o, 0, 0, 0);
+      const int dcol = wave * 32 + (lane & 31), ks = (lane >> 5) * 8;
+#pragma unroll 2
+      for (int k0 = 0; k0 < ROWS; k0 += 16) {
+        const float4 p0 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks]);
+        const float4 p1 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks + 4]);
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        u16x8_t hi, lo, vv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const unsigned short h = bf16_rne(pv[i]);
+          hi[i] = h;
+          lo[i] = bf16_rne(pv[i] - __uint_as_float((uint32_t)h << 16));
+          vv[i] = s_v[k0 + ks + i][dcol];
+        }
+        const bf16x8_t vb8 = __builtin_bit_cast(bf16x8_t, vv);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, hi), vb8, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lo), vb8, o, 0, 0, 0);
       }
     }
     // partials: acc for (layer, head) = qv, channel block `wave`
