@@ -142,8 +142,8 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   }
   g.cand_cap = g.prefilter ? has::kCandFast : (g.T < has::kCandLds ? g.T : has::kCandLds);
   // prefiltered scoring units: about 2048 over the worst-case item count,
-  // between 4096 and 16384 tokens
-  g.ct_tip = clampi(pow2_floor((long long)g.T * n_idx / 2048), 4096, 16384);
+  // between 1024 and 16384 tokens
+  g.ct_tip = clampi(pow2_floor((long long)g.T * n_idx / 2048), 1024, 16384);
   g.nch_tip = (g.T + g.ct_tip - 1) / g.ct_tip;
   g.bm_words = (g.T + 31) / 32;
   size_t o = 0;

@@ -1535,17 +1535,21 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Streaming groups need nothing but the plan: their attention runs on the
   // side stream, overlapping the scoring and selection of retrieval groups.
-  if ((e = hipEventRecord(ss.fork, s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(ss.side, ss.fork, 0)) != hipSuccess) return e;
-  {
-    Geo gs = g;
-    gs.attn_mode = 2;
-    const int grid_s = clampi(n_att_items * (long long)g.nch_s, 1, g.grid);
-    KTimer t("attention_stream", ss.side);
-    e = launch_attn(gs, grid_s, ss.side);
+  // (The shared-index mode without labels has none.)
+  const bool side = !(g.clsa && g.labels == nullptr);
+  if (side) {
+    if ((e = hipEventRecord(ss.fork, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss.side, ss.fork, 0)) != hipSuccess) return e;
+    {
+      Geo gs = g;
+      gs.attn_mode = 2;
+      const int grid_s = clampi(n_att_items * (long long)g.nch_s, 1, g.grid);
+      KTimer t("attention_stream", ss.side);
+      e = launch_attn(gs, grid_s, ss.side);
+    }
+    if (e != hipSuccess) return e;
+    if ((e = hipEventRecord(ss.join, ss.side)) != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
-  if ((e = hipEventRecord(ss.join, ss.side)) != hipSuccess) return e;
   const int grid_tip = clampi(n_idx_items * g.nch_t, 1, g.grid);
   const int grid_item = clampi(n_idx_items, 1, g.grid);
   if (g.prefilter) {
@@ -1610,7 +1614,7 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     }
   }
   if (e != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(s, ss.join, 0)) != hipSuccess) return e;
+  if (side && (e = hipStreamWaitEvent(s, ss.join, 0)) != hipSuccess) return e;
   const long long n_out = n_att_items * g.G * g.d;
   {
     KTimer t("merge", s);
