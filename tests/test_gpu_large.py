@@ -87,3 +87,27 @@ def test_c4_32_layers_128k_sampled():
     ret = idx[np.broadcast_to(lab[:, None, :], idx.shape[:3])]
     assert (np.diff(ret, axis=1) > 0).all() and ret.min() >= 0 and ret.max() < cfg.ctx_len
     assert (idx[np.broadcast_to(~lab[:, None, :], idx.shape[:3])] == -1).all()
+
+
+@pytest.mark.parametrize("over", [
+    dict(kv_dtype="f32"),                  # fp32 cache: vector-ALU attention
+    dict(d_head=64, n_dom=8),              # d 64: vector-ALU attention
+    dict(n_layers=12),                     # 12 layers x 4 heads = 48 query vectors > 32
+    dict(n_layers=3, n_fac=1000),          # ragged last row block on the matrix cores
+], ids=["f32", "d64", "48qv", "ragged-mfma"])
+def test_clsa_attention_paths(over):
+    """Shared-index mode on both attention paths (matrix cores for bf16,
+    d 128, N*G <= 32; vector ALUs otherwise), with one layer treating a group
+    as streaming."""
+    cfg = R.get_config("c3", ctx_len=9000, batch=2, **{"n_fac": 700, **over})
+    print(f"case clsa paths {over}", flush=True)
+    case = U.DeviceCase(cfg)
+    lab = np.ones((cfg.n_layers, cfg.n_kv_heads), np.uint8)
+    lab[cfg.n_layers - 1, 3] = 0
+    out, idx, _ = U.run_clsa(case, labels=lab)
+    G = cfg.group
+    for (b, g) in [(0, 0), (1, 3), (1, 7)]:
+        ref, _, scores = U.oracle_clsa_item(cfg, case.hi, b, g, labels=lab)
+        U.check_index_set(idx[b, g], scores, cfg.n_fac, f"clsa {over} idx b{b} g{g}")
+        for n in range(cfg.n_layers):
+            U.check_out(out[n, b, g * G:(g + 1) * G], ref[n], f"clsa {over} out n{n} b{b} g{g}")
