@@ -128,6 +128,7 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   g.n_srows = g.s_end + (g.T - g.w_start);
   g.cs = clampi(pow2_floor((long long)g.n_srows * n_att / 2048), 128, has::kMaxChunkRows);
   g.nch_s = (g.n_srows + g.cs - 1) / g.cs;
+  g.cs = (g.n_srows + g.nch_s - 1) / g.nch_s;  // equal chunks (no short tail)
   g.nparts = g.nch_f > g.nch_s ? g.nch_f : g.nch_s;
   // Prefiltered selection: a sample of kSampleTokens scores places a key
   // threshold expected to pass about 1.25 n_fac tokens plus 4 standard
@@ -267,6 +268,7 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
   g.kdom = k_dom;
   g.i_dom = i_dom;
   g.labels = labels;
+  g.host_plan = (clsa && labels == nullptr && g.prefilter) ? 1 : 0;
   g.out = out;
   g.idx_out = idx_out;
   s = persistent_grid(g.grid);

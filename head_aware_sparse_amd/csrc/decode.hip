@@ -141,9 +141,16 @@ __device__ __forceinline__ int label_at(const Geo& g, int pair) {
   return g.labels ? (g.labels[pair] != 0) : 1;
 }
 
-__device__ __forceinline__ const int* idx_pairs(const Geo& g) { return g.plan + 4; }
-__device__ __forceinline__ const int* att_ret_pairs(const Geo& g) { return g.plan + 4 + kMaxPairs; }
-__device__ __forceinline__ const int* att_str_pairs(const Geo& g) { return g.plan + 4 + 2 * kMaxPairs; }
+// Plan accessors: index pairs (one selection each), retrieval and streaming
+// (layer, group) pairs for attention.  With a host-known plan (shared-index
+// mode without labels) every KV group is an index pair, every (layer, group)
+// is retrieval and nothing streams, so no plan launch is needed.
+__device__ __forceinline__ int n_idx_pairs(const Geo& g) { return g.host_plan ? g.Hkv : g.plan[0]; }
+__device__ __forceinline__ int idx_pair(const Geo& g, int i) { return g.host_plan ? i : g.plan[4 + i]; }
+__device__ __forceinline__ int n_ret_pairs(const Geo& g) { return g.host_plan ? g.Lq * g.Hkv : g.plan[1]; }
+__device__ __forceinline__ int ret_pair(const Geo& g, int i) { return g.host_plan ? i : g.plan[4 + kMaxPairs + i]; }
+__device__ __forceinline__ int n_str_pairs(const Geo& g) { return g.host_plan ? 0 : g.plan[2]; }
+__device__ __forceinline__ int str_pair(const Geo& g, int i) { return g.plan[4 + 2 * kMaxPairs + i]; }
 
 // Finds, over s_hist[0..nbins) read from the top bin down, the bin where the
 // running count first reaches `need` (1 <= need <= total).  Returns the bin
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(Geo g) {
 template <typename E>
 __device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
   const int pidx = item / g.B, b = item - pidx * g.B;
-  const int pair = idx_pairs(g)[pidx];
+  const int pair = idx_pair(g, pidx);
   const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
   const E* qg;
   if (g.clsa)
@@ -341,7 +348,7 @@ __global__ __launch_bounds__(NT) void tau_kernel(Geo g) {
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ int s_w[2 * NWAVE];
   __shared__ uint32_t s_res[2];
-  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  const int n_items = n_idx_pairs(g) * g.B;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     __syncthreads();
     const uint2 t = item_tau(g, item, s_hist, s_w, s_res);
@@ -369,7 +376,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = PF ? g.nch_tip : g.nch_t;
   const int ct = PF ? g.ct_tip : g.ct;
-  const int n_units = plan_idx_pairs(g.plan) * g.B * nch;
+  const int n_units = n_idx_pairs(g) * g.B * nch;
   if constexpr (!PF)
     for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0;
   const int R = V * EPV;
@@ -382,7 +389,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
     if constexpr (PF) {
       // the sample pass stored the group query; each lane reads its slice
       const int pidx = item / g.B, b = item - pidx * g.B;
-      const int pair = idx_pairs(g)[pidx];
+      const int pair = idx_pair(g, pidx);
       const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
       slice = ((size_t)l * g.B + b) * g.Hkv + gi;
       const float* qb = g.qbar + (size_t)item * R + (lane % V) * EPV;
@@ -476,7 +483,7 @@ __global__ __launch_bounds__(NT) void select_bin_kernel(Geo g) {
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ int s_w[NWAVE];
   __shared__ uint32_t s_res[2];
-  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  const int n_items = n_idx_pairs(g) * g.B;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     __syncthreads();
     const uint4* gh = reinterpret_cast<const uint4*>(g.hist + (size_t)item * kHistBins);
@@ -501,7 +508,7 @@ __global__ __launch_bounds__(NT) void select_a_kernel(Geo g) {
   __shared__ int s_n;
   __shared__ uint32_t s_base;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int n_units = plan_idx_pairs(g.plan) * g.B * g.nch_t;
+  const int n_units = n_idx_pairs(g) * g.B * g.nch_t;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const int item = u / g.nch_t, ch = u - item * g.nch_t;
     __syncthreads();
@@ -778,14 +785,16 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
   __shared__ float s_q[kMaxR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = V * EPV;
-  const int n_units = plan_idx_pairs(g.plan) * g.B * kBlocks;
+  const int n_units = n_idx_pairs(g) * g.B * kBlocks;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const int item = u / kBlocks, blk = u - item * kBlocks;
     __syncthreads();
     const size_t slice = group_query_dom<E>(g, item, s_q);
     __syncthreads();
-    if (blk == 0)
+    if (blk == 0) {
       for (int c = tid; c < R; c += NT) g.qbar[(size_t)item * R + c] = s_q[c];
+      if (g.host_plan && tid < 4) g.info[(size_t)item * 4 + tid] = 0u;  // else the plan clears them
+    }
     float qr[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
@@ -835,7 +844,7 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
   static_assert(kCandFast * sizeof(uint2) >= (kPrefilterMaxT / 32) * sizeof(uint32_t), "u32 prefix alias");
   static_assert(kCandFast / 3 < 65536, "prefiltered n_fac fits u16 prefixes");
   const int tid = threadIdx.x;
-  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  const int n_items = n_idx_pairs(g) * g.B;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     __syncthreads();
     const uint32_t count = g.info[(size_t)item * 4 + 2];
@@ -843,7 +852,7 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
     for (int w = tid; w < g.bm_words; w += NT) s_bm[w] = 0u;
     for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
     const int pidx = item / g.B, b = item - pidx * g.B;
-    const int pair = idx_pairs(g)[pidx];
+    const int pair = idx_pair(g, pidx);
     const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
     int32_t* ix = g.idx + (size_t)item * g.n_fac;
     int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
@@ -941,7 +950,7 @@ __global__ __launch_bounds__(NT) void select_b_kernel(Geo g) {
   __shared__ int s_w[NWAVE];
   __shared__ uint32_t s_res[2];
   const int tid = threadIdx.x;
-  const int n_items = plan_idx_pairs(g.plan) * g.B;
+  const int n_items = n_idx_pairs(g) * g.B;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     __syncthreads();
     const uint32_t b1 = g.info[(size_t)item * 4 + 0];
@@ -1013,11 +1022,11 @@ __global__ __launch_bounds__(NT) void select_b_kernel(Geo g) {
 __global__ __launch_bounds__(NT) void select_c_kernel(Geo g) {
   __shared__ int s_w[NWAVE];
   const int tid = threadIdx.x;
-  const int n_units = plan_idx_pairs(g.plan) * g.B * g.nch_t;
+  const int n_units = n_idx_pairs(g) * g.B * g.nch_t;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const int item = u / g.nch_t, ch = u - item * g.nch_t;
     const int pidx = item / g.B, b = item - pidx * g.B;
-    const int pair = idx_pairs(g)[pidx];
+    const int pair = idx_pair(g, pidx);
     const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
     const uint2 th = g.thr[item];
     const float* sc = g.scores + (size_t)item * g.Ts;
@@ -1072,8 +1081,8 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
   __shared__ float s_ml[G][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane % LPR, rsub = lane / LPR;
-  const int n_ret = g.attn_mode == 2 ? 0 : g.plan[1];
-  const int n_str = g.attn_mode == 1 ? 0 : g.plan[2];
+  const int n_ret = g.attn_mode == 2 ? 0 : n_ret_pairs(g);
+  const int n_str = g.attn_mode == 1 ? 0 : n_str_pairs(g);
   const int n_fac_units = n_ret * g.B * g.nch_f;
   const int n_units = n_fac_units + n_str * g.B * g.nch_s;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
@@ -1082,7 +1091,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
     const int nchunk = fac ? g.nch_f : g.nch_s;
     const int item = uu / nchunk, chunk = uu - item * nchunk;
     const int pa = item / g.B, b = item - pa * g.B;
-    const int pair = fac ? att_ret_pairs(g)[pa] : att_str_pairs(g)[pa];
+    const int pair = fac ? ret_pair(g, pa) : str_pair(g, pa);
     const int lq = pair / g.Hkv, gi = pair - lq * g.Hkv;
     const int lkv = g.clsa ? 0 : lq;
     const size_t kvs = ((size_t)lkv * g.B + b) * g.Hkv + gi;
@@ -1528,11 +1537,11 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   const long long n_idx_items = (long long)(g.clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att_items = (long long)g.Lq * g.Hkv * g.B;
   const int grid_plan = clampi((n_idx_items * kHistBins / 4 + NT - 1) / NT, 1, g.grid);
-  {
+  if (!g.host_plan) {
     KTimer t("plan", s);
     plan_kernel<<<grid_plan, NT, 0, s>>>(g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   // Streaming groups need nothing but the plan: their attention runs on the
   // side stream, overlapping the scoring and selection of retrieval groups.
   // (The shared-index mode without labels has none.)

@@ -26,6 +26,7 @@ struct Geo {
   int clsa;         // 1: one index per (b, g) shared by Lq layers over one cache
   int clsa_mfma;    // shared-index retrieval attention on the matrix cores (bf16, d 128, Lq*G <= 32)
   int interleaved;  // rope pairing
+  int host_plan;    // shared-index mode, no labels, prefiltered: the plan is implicit (no plan launch)
   // chunking
   int ct, nch_t;    // score/select chunk tokens and count per item
   int Ts;           // score row stride (T rounded up to 64)
@@ -68,7 +69,6 @@ struct Geo {
   int32_t* idx_out;
 };
 
-inline __host__ __device__ int plan_idx_pairs(const int* p) { return p[0]; }
 
 // Brackets one kernel launch with HIP events on its stream while per-kernel
 // timing is enabled (has_timing_enable); a no-op otherwise.
