@@ -824,10 +824,11 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
 // final: per index item, the exact top-n_fac among the candidates (key >=
 // tau) held in LDS.  While the candidates load, they are counted in 2048
 // bins of (key - tau) >> sh, sh sized so the largest sampled key falls in the
-// top bin (larger keys are clamped into it); the bin holding the n_fac-th
-// candidate is resolved by ranking its members when it has at most kRankMax
-// of them and is not the clamped top bin, else by the general radix
-// threshold.  If the candidates are fewer than n_fac or overflowed, the item
+// top bin (larger keys are clamped into it).  When the bin holding the
+// n_fac-th candidate is not the clamped top bin and has at most kRankMax
+// members, one pass marks every candidate above it and lists its members,
+// and the members are ranked directly; otherwise the general radix threshold
+// decides.  If the candidates are fewer than n_fac or overflowed, the item
 // is rescored in full here and selected from its score row (exact either
 // way).  The selected tokens are marked in an LDS bitmap; a token's output
 // slot is the number of marked tokens before it, from per-word prefix
@@ -835,48 +836,54 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
 template <typename E>
 __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
   __shared__ uint2 s_c[kCandFast];
-  __shared__ uint32_t s_bm[kPrefilterMaxT / 32];
+  __shared__ __attribute__((aligned(16))) uint32_t s_bm[kPrefilterMaxT / 32];
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ float s_q[kMaxR];
   __shared__ int s_w[NWAVE];
   __shared__ uint32_t s_res[2];
+  __shared__ uint2 s_list[kRankMax];
+  __shared__ int s_m;
   static_assert(kHistBins * sizeof(uint32_t) >= (kPrefilterMaxT / 32) * sizeof(uint16_t), "u16 prefix alias");
   static_assert(kCandFast * sizeof(uint2) >= (kPrefilterMaxT / 32) * sizeof(uint32_t), "u32 prefix alias");
   static_assert(kCandFast / 3 < 65536, "prefiltered n_fac fits u16 prefixes");
   const int tid = threadIdx.x;
   const int n_items = n_idx_pairs(g) * g.B;
+  // bitmap words per thread for the prefix counts: a multiple of 4 (16-byte
+  // reads); NT * per <= kPrefilterMaxT / 32 as bm_words <= that
+  const int per = ((g.bm_words + NT - 1) / NT + 3) & ~3;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     __syncthreads();
     const uint32_t count = g.info[(size_t)item * 4 + 2];
     const uint2 th = g.tau[item];
-    for (int w = tid; w < g.bm_words; w += NT) s_bm[w] = 0u;
+    for (int w = tid; w < NT * per; w += NT) s_bm[w] = 0u;
     for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+    if (tid == 0) s_m = 0;
     const int pidx = item / g.B, b = item - pidx * g.B;
     const int pair = idx_pair(g, pidx);
     const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
     int32_t* ix = g.idx + (size_t)item * g.n_fac;
     int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
-    // marks the selected tokens, then writes each to its slot; s_pre holds
-    // the per-word prefix counts (bm_words entries, in LDS no longer needed)
-    auto emit = [&](const auto& src, uint32_t kstar, uint32_t tstar, auto* s_pre) {
-      src.for_each([&](uint32_t k, uint32_t t) {
-        if (k > kstar || (k == kstar && t <= tstar)) atomicOr(&s_bm[t >> 5], 1u << (t & 31));
-      });
-      __syncthreads();
-      const int per = (g.bm_words + NT - 1) / NT;
-      const int w0 = min(g.bm_words, tid * per), w1 = min(g.bm_words, w0 + per);
+    auto mark = [&](uint32_t t) { atomicOr(&s_bm[t >> 5], 1u << (t & 31)); };
+    // writes every marked element of src to its slot; s_pre holds the
+    // per-word prefix counts (in LDS no longer needed)
+    auto emit = [&](const auto& src, auto* s_pre) {
+      const uint4* q4 = reinterpret_cast<const uint4*>(s_bm + tid * per);
       int cnt = 0;
-      for (int w = w0; w < w1; ++w) cnt += __popc(s_bm[w]);
+      for (int v = 0; v < per / 4; ++v) {
+        const uint4 x = q4[v];
+        cnt += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+      }
       int tot;
       uint32_t run = (uint32_t)block_excl_scan(cnt, s_w, tot);
-      for (int w = w0; w < w1; ++w) {
+      for (int w = tid * per; w < (tid + 1) * per; ++w) {
         s_pre[w] = run;  // < n_fac, which fits the prefix type
         run += __popc(s_bm[w]);
       }
       __syncthreads();
-      src.for_each([&](uint32_t k, uint32_t t) {
-        if (k > kstar || (k == kstar && t <= tstar)) {
-          const uint32_t pos = s_pre[t >> 5] + __popc(s_bm[t >> 5] & ((1u << (t & 31)) - 1u));
+      src.for_each([&](uint32_t, uint32_t t) {
+        const uint32_t word = s_bm[t >> 5], bit = 1u << (t & 31);
+        if (word & bit) {
+          const uint32_t pos = s_pre[t >> 5] + __popc(word & (bit - 1u));
           ix[pos] = (int32_t)t;
           if (ox) ox[pos] = (int32_t)t;
         }
@@ -916,13 +923,38 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
       find_bin_top(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, bin, above);
       const uint32_t members = s_hist[bin];
       __syncthreads();
-      uint32_t kstar, tstar;
-      if (bin < kHistBins - 1 && members <= (uint32_t)kRankMax)
-        rank_in_bin(src, tau, sh, (uint32_t)bin, (uint32_t)g.n_fac - above, s_res, kstar, tstar);
-      else
+      if (bin < kHistBins - 1 && members <= (uint32_t)kRankMax) {
+        const uint32_t ub = (uint32_t)bin;
+        src.for_each([&](uint32_t k, uint32_t t) {
+          const uint32_t d = min((k - tau) >> sh, (uint32_t)kHistBins - 1u);
+          if (d > ub) mark(t);
+          else if (d == ub) s_list[atomicAdd(&s_m, 1)] = make_uint2(k, t);
+        });
+        __syncthreads();
+        // a member is selected when fewer than need members precede it in
+        // the order (key desc, token asc)
+        const uint32_t need = (uint32_t)g.n_fac - above;
+        const int m = s_m;
+        for (int i = tid; i < m; i += NT) {
+          const uint2 me = s_list[i];
+          uint32_t r = 0;
+#pragma unroll 8
+          for (int j = 0; j < m; ++j) {
+            const uint2 o = s_list[j];
+            r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+          }
+          if (r < need) mark(me.y);
+        }
+      } else {
+        uint32_t kstar, tstar;
         exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
-      // the threshold's histogram is free by then; n_fac < 2^16 here
-      emit(src, kstar, tstar, reinterpret_cast<uint16_t*>(s_hist));
+        src.for_each([&](uint32_t k, uint32_t t) {
+          if (k > kstar || (k == kstar && t <= tstar)) mark(t);
+        });
+      }
+      __syncthreads();
+      // the histogram is free by then; n_fac < 2^16 here
+      emit(src, reinterpret_cast<uint16_t*>(s_hist));
     } else {
       const size_t slice = group_query_dom<E>(g, item, s_q);
       __syncthreads();
@@ -934,7 +966,11 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
       const ScoreScan src{sc, g.T};
       uint32_t kstar, tstar;
       exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
-      emit(src, kstar, tstar, reinterpret_cast<uint32_t*>(s_c));
+      src.for_each([&](uint32_t k, uint32_t t) {
+        if (k > kstar || (k == kstar && t <= tstar)) mark(t);
+      });
+      __syncthreads();
+      emit(src, reinterpret_cast<uint32_t*>(s_c));
     }
   }
 }
