@@ -247,3 +247,19 @@ def test_tied_scores_select_exactly(shared_q, levels):
     assert (idx[l, 0, g] == want).all()
     ref, _ = U.oracle_item_custom(cfg, q_host, k_host, hi.rows("v", l, 0, g), hi.i_dom[l, g], True)
     U.check_out(out[l, 0, g * G:(g + 1) * G], ref, "ties out")
+
+
+@pytest.mark.parametrize("over", [
+    dict(ctx_len=150000, n_fac=2048, batch=1),   # above the prefiltered path's 131072-token limit
+    dict(ctx_len=8191, n_fac=500, batch=2),      # just below its 8192-token minimum
+    dict(ctx_len=32768, n_fac=6000, batch=1),    # 3 n_fac above its 16384 candidate slots
+    dict(ctx_len=8192, n_fac=3000, batch=1),     # near its largest n_fac at its smallest T (prefiltered)
+], ids=["T150000", "T8191", "nfac6000", "edge-prefilter"])
+def test_selection_path_boundaries(over):
+    """The general selection path (every score written, radix threshold over
+    chunks) and the prefiltered one at the edges of the rule choosing
+    between them give the oracle's selection."""
+    cfg = R.get_config("c1", **over)
+    print(f"case boundaries {over}", flush=True)
+    case = U.DeviceCase(cfg)
+    _check_items(case, _all_items(cfg)[:cfg.n_kv_heads * 2], f"boundary {over}")
