@@ -394,6 +394,8 @@ has_status kdom_pack(const has_decode_dims* dims, const void* k_cache, const int
   Layout L = make_layout(dims, false);
   L.g.k = k_cache;
   L.g.i_dom = i_dom;
+  s = persistent_grid(L.g.grid);
+  if (s != HAS_OK) return s;
   hipError_t e = has::launch_kdom_pack(L.g, k_dom, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kdom_pack launch");
   return ok();

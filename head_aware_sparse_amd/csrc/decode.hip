@@ -1483,24 +1483,61 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
 // ------------------------------------------------------------------ kdom_pack
 template <typename E>
 __global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd) {
-  const int s = blockIdx.y;  // (l, b, gi) slice
-  const int gi = s % g.Hkv;
-  const int l = s / (g.Hkv * g.B);
-  const int32_t* dom = g.i_dom + ((size_t)l * g.Hkv + gi) * g.n_dom;
-  const E* k = (const E*)g.k + (size_t)s * g.T * g.d;
-  E* o = kd + (size_t)s * g.T * g.R;
-  const uint32_t per = (uint32_t)g.T * (uint32_t)g.R;
+  // One work item = (slice, tile of 32 KB of cache rows): the tile is read
+  // whole (16-byte nontemporal loads, all issued before any is used) into
+  // LDS, then each thread gathers 16-byte output vectors of dominant-chunk
+  // channels.
+  constexpr int EPV = 16 / (int)sizeof(E);
+  constexpr int kTileVec = 8 * NT;  // 16-byte vectors per tile (32 KB)
+  __shared__ uint4 s_rows[kTileVec];
+  const int vpr = g.d * (int)sizeof(E) / 16;  // 16-byte vectors per cache row (8, 16 or 32)
+  const int tt = kTileVec / vpr;              // tokens per tile
+  const int ovt = g.R / EPV;                  // 16-byte output vectors per token
+  const int n_slices = g.Lkv * g.B * g.Hkv;
+  const int n_tiles = (g.T + tt - 1) / tt;
+  const long long n_work = (long long)n_slices * n_tiles;
   const int hd = g.d / 2;
-  for (uint32_t i = blockIdx.x * NT + threadIdx.x; i < per; i += gridDim.x * NT) {
-    const uint32_t t = i / (uint32_t)g.R;
-    const int e = (int)(i - t * (uint32_t)g.R);
-    E v = E(0);
-    if (e < 2 * g.n_dom) {
-      const int f = dom[e >> 1], cc = e & 1;
-      const int chn = g.interleaved ? 2 * f + cc : f + cc * hd;
-      v = k[(size_t)t * g.d + chn];
+  // the next tile's rows are loaded into registers while this one is gathered
+  auto load_tile = [&](long long w, uint4* r) {
+    const int s = (int)(w / n_tiles), tile = (int)(w - (long long)s * n_tiles);
+    const int t0 = tile * tt, nv = min(tt, g.T - t0) * vpr;
+    const uint4* src = reinterpret_cast<const uint4*>((const E*)g.k + ((size_t)s * g.T + t0) * g.d);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int v = threadIdx.x + j * NT;
+      r[j] = v < nv ? ld16_stream(src + v) : make_uint4(0, 0, 0, 0);
     }
-    o[i] = v;
+  };
+  uint4 r[8];
+  if (blockIdx.x < n_work) load_tile(blockIdx.x, r);
+  for (long long w = blockIdx.x; w < n_work; w += gridDim.x) {
+    const int s = (int)(w / n_tiles), tile = (int)(w - (long long)s * n_tiles);
+    const int gi = s % g.Hkv, l = s / (g.Hkv * g.B);
+    const int32_t* dom = g.i_dom + ((size_t)l * g.Hkv + gi) * g.n_dom;
+    const int t0 = tile * tt, nt = min(tt, g.T - t0);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_rows[threadIdx.x + j * NT] = r[j];
+    __syncthreads();
+    if (w + gridDim.x < n_work) load_tile(w + gridDim.x, r);
+    for (int o = threadIdx.x; o < nt * ovt; o += NT) {
+      const int tok = o / ovt, part = o - tok * ovt;
+      const E* row = reinterpret_cast<const E*>(s_rows + tok * vpr);
+      E vals[EPV];
+#pragma unroll
+      for (int q = 0; q < EPV; ++q) {
+        const int e = part * EPV + q;
+        E v = E(0);
+        if (e < 2 * g.n_dom) {
+          const int f = dom[e >> 1], cc = e & 1;
+          v = row[g.interleaved ? 2 * f + cc : f + cc * hd];
+        }
+        vals[q] = v;
+      }
+      uint4 packed;
+      __builtin_memcpy(&packed, vals, sizeof(packed));
+      *reinterpret_cast<uint4*>(kd + ((size_t)s * g.T + t0 + tok) * g.R + part * EPV) = packed;
+    }
   }
 }
 
@@ -1555,9 +1592,9 @@ int clampi(long long v, int lo, int hi) { return (int)(v < lo ? lo : (v > hi ? h
 }  // namespace
 
 hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s) {
-  const int n_slices = g.Lkv * g.B * g.Hkv;
-  const uint32_t per = (uint32_t)g.T * (uint32_t)g.R;
-  const dim3 grid(clampi(((long long)per + NT - 1) / NT, 1, 2048), n_slices);
+  const int tt = 8 * NT * 16 / (g.d * (g.bf16 ? 2 : 4));  // tokens per 32 KB tile
+  const long long n_work = (long long)g.Lkv * g.B * g.Hkv * ((g.T + tt - 1) / tt);
+  const int grid = clampi(n_work, 1, 8 * g.grid);
   KTimer t("kdom_pack", s);
   if (g.bf16)
     kdom_pack_kernel<uint16_t><<<grid, NT, 0, s>>>(g, (uint16_t*)k_dom);

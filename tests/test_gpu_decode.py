@@ -130,15 +130,24 @@ def test_deterministic_and_idx_optional():
     assert (out.cpu().numpy() == o1).all()
 
 
-def test_kdom_pack_matches_channels():
-    cfg = R.get_config("c1", ctx_len=3000, batch=2)
+@pytest.mark.parametrize("over,layout", [
+    (dict(), 0), (dict(kv_dtype="f32"), 0), (dict(d_head=64, n_dom=5), 0), (dict(n_dom=13), 1),
+], ids=["bf16", "f32", "d64-ndom5", "interleaved-ndom13"])
+def test_kdom_pack_matches_channels(over, layout):
+    """k_dom holds the dominant chunks' channel pairs of every token (a
+    ragged last tile of tokens included) and zeros in the padding."""
+    cfg = R.get_config("c1", ctx_len=3000, batch=2, **over)
     case = U.DeviceCase(cfg)
-    kd = case.k_dom.cpu().float().numpy()
+    kd_t = torch.empty_like(case.k_dom)
+    H.kdom_pack(U.dims_of(cfg, rope_layout=layout), case.k, case.i_dom, kd_t)
+    torch.cuda.synchronize()
+    kd = kd_t.cpu().float().numpy()
     k = case.k.cpu().float().numpy()
     d2 = cfg.d_head // 2
-    for (l, b, g) in [(0, 0, 0), (0, 1, 5)]:
+    for (l, b, g) in [(0, 0, 0), (0, 1, 5), (0, 1, 7)]:
         f = case.hi.i_dom[l, g]
-        want = np.stack([k[l, b, g][:, f], k[l, b, g][:, f + d2]], axis=-1).reshape(cfg.ctx_len, -1)
+        pair = (2 * f, 2 * f + 1) if layout else (f, f + d2)
+        want = np.stack([k[l, b, g][:, pair[0]], k[l, b, g][:, pair[1]]], axis=-1).reshape(cfg.ctx_len, -1)
         assert (kd[l, b, g][:, :2 * cfg.n_dom] == want).all()
         assert (kd[l, b, g][:, 2 * cfg.n_dom:] == 0).all()
 
