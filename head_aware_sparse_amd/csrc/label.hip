@@ -10,9 +10,10 @@
 //   gram      G = W W^T for every query and key head (matrix cores, bf16 or
 //             fp32 in, fp32 accumulate).  Reads every weight once: the
 //             HBM-bound step.
-//   spectrum  per query head, in fp64 LDS: Cholesky G_K = L L^T, then the
-//             symmetric S = L^T G_Q L (fp64 matrix cores), which is similar
-//             to C_h = G_Q G_K; Householder tridiagonalisation of S.
+//   cholesky  per key head, in fp64 LDS: G_K = L L^T.
+//   spectrum  per query head: the symmetric S = L^T G_Q L (fp64 matrix
+//             cores), which is similar to C_h = G_Q G_K; Householder
+//             tridiagonalisation of S in fp64 LDS.
 //   bisect    eigenvalues of the tridiagonal by Sturm-count bisection (one
 //             thread per eigenvalue), sigma = sqrt(max(lambda, 0)) and ER.
 //   finalize  group mean of ER, global rank with ties to the lower index,
@@ -37,6 +38,7 @@ struct LGeo {
   const void* wq;
   const void* wk;
   float* gram;     // [L*Hq + L*Hkv][d][d]: query heads, then key heads
+  double* lscr;    // [L*Hkv][d][d] Cholesky factor of each key head's Gram matrix
   double* tscr;    // [L*Hq][d][d] scratch for G_Q L
   float* tri;      // [L*Hq][2][d]: diagonal, off-diagonal (fp32)
   float* er_head;  // [L*Hq]
@@ -47,7 +49,7 @@ struct LGeo {
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct LabelLayout {
-  size_t gram, tscr, tri, erh, erg, bytes;
+  size_t gram, lscr, tscr, tri, erh, erg, bytes;
 };
 
 LabelLayout label_layout(int L, int Hq, int Hkv, int d) {
@@ -55,6 +57,8 @@ LabelLayout label_layout(int L, int Hq, int Hkv, int d) {
   size_t at = 0;
   o.gram = at;
   at = align256(at + (size_t)(L * Hq + L * Hkv) * d * d * 4);
+  o.lscr = at;
+  at = align256(at + (size_t)L * Hkv * d * d * 8);
   o.tscr = at;
   at = align256(at + (size_t)L * Hq * d * d * 8);
   o.tri = at;
@@ -169,9 +173,53 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return x;
 }
 
+// Cholesky G_K = L L^T of each key head's Gram matrix (fp64, in LDS), once
+// per (layer, KV group): right-looking, the trailing update tiled 16 x 16
+// over the threads.  Columns whose pivot is not positive (rank-deficient key
+// projections) are zeroed.  L (lower, zeros above) goes to lscr.
+template <int D>
+__global__ __launch_bounds__(NT) void chol_kernel(LGeo g) {
+  constexpr int LD = D + 1;
+  __shared__ double s_m[D * LD];
+  __shared__ double s_ld[D];  // the diagonal of L, written back at the end
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int grp = blockIdx.x;  // l*Hkv + gk
+  const float* GK = g.gram + (size_t)(g.L * g.Hq + grp) * D * D;
+  double* A = s_m;
+  for (int e = tid; e < D * D; e += NT) A[(e / D) * LD + (e % D)] = (double)GK[e];
+  __syncthreads();
+  double dmax = 0.0;
+  for (int i = 0; i < D; ++i) dmax = fmax(dmax, A[i * LD + i]);
+  const double tol = 1e-12 * dmax;
+  for (int j = 0; j < D; ++j) {
+    // the diagonal entry is only read here (its square root is kept apart),
+    // so the column can be scaled without waiting for every thread to read it
+    const double piv = A[j * LD + j];
+    const bool zero = !(piv > tol);
+    const double ljj = zero ? 0.0 : sqrt(piv);
+    const double inv = zero ? 0.0 : 1.0 / ljj;
+    if (tid == 0) s_ld[j] = ljj;
+    for (int i = j + 1 + tid; i < D; i += NT) A[i * LD + j] *= inv;
+    __syncthreads();
+    for (int r = j + 1 + ty; r < D; r += 16) {
+      const double arj = A[r * LD + j];
+      for (int c = j + 1 + tx; c <= r; c += 16) A[r * LD + c] -= arj * A[c * LD + j];
+    }
+    __syncthreads();
+  }
+  double* Lo = g.lscr + (size_t)grp * D * D;
+  for (int e = tid; e < D * D; e += NT) {
+    const int i = e / D, j = e % D;
+    Lo[e] = j < i ? A[i * LD + j] : (j == i ? s_ld[i] : 0.0);
+  }
+}
+
 // MFMA f64 16x16x4: A element (lane%16, lane/16), B element (lane/16,
 // lane%16); output (4*r + lane/16, lane%16) in register r (checked on the
 // device: unlike the fp32 16x16 forms, rows interleave across lane groups).
+// Per query head: S = L^T G_Q L (similar to C_h = G_Q G_K) on the fp64 matrix
+// cores, then Householder tridiagonalisation of S in LDS, holding only the
+// lower triangle of the symmetric trailing matrix.
 template <int D>
 __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
   constexpr int LD = D + 1;
@@ -179,61 +227,17 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
   constexpr int CB = D / 16;  // 16-col bands
   __shared__ double s_m[D * LD];
   __shared__ double s_v[D], s_p[D];
-  __shared__ double s_red[NWAVE];
+  __shared__ double s_red[NWAVE], s_red2[NWAVE];
   __shared__ float s_d[D], s_e[D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.x;                 // l*Hq + h
   const int l = head / g.Hq, h = head - l * g.Hq;
-  const int gk = g.L * g.Hq + l * g.Hkv + h / g.G;
+  const int grp = l * g.Hkv + h / g.G;
   const float* GQ = g.gram + (size_t)head * D * D;
-  const float* GK = g.gram + (size_t)gk * D * D;
+  const double* Lg = g.lscr + (size_t)grp * D * D;
   double* A = s_m;
 
-  auto block_sum = [&](double x) -> double {
-    x = wave_sum_d(x);
-    if (lane == 0) s_red[wave] = x;
-    __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) t += s_red[w];
-    __syncthreads();
-    return t;
-  };
-
-  // 1. G_K -> LDS (fp64); right-looking Cholesky G_K = L L^T, columns whose
-  //    pivot is not positive (rank-deficient key projections) are zeroed.
-  double dmax = 0.0;
-  for (int e = tid; e < D * D; e += NT) {
-    const int i = e / D, j = e - i * D;
-    A[i * LD + j] = (double)GK[e];
-  }
-  __syncthreads();
-  for (int i = 0; i < D; ++i) dmax = fmax(dmax, A[i * LD + i]);
-  const double tol = 1e-12 * dmax;
-  for (int j = 0; j < D; ++j) {
-    const double piv = A[j * LD + j];
-    __syncthreads();
-    const bool zero = !(piv > tol);
-    const double ljj = zero ? 0.0 : sqrt(piv);
-    for (int i = j + tid; i < D; i += NT) A[i * LD + j] = zero ? 0.0 : (i == j ? ljj : A[i * LD + j] / ljj);
-    __syncthreads();
-    const int m = D - j - 1;
-    for (int e = tid; e < m * m; e += NT) {
-      const int ii = e / m, kk = e - ii * m;
-      if (kk <= ii) {
-        const int r = j + 1 + ii, c = j + 1 + kk;
-        A[r * LD + c] -= A[r * LD + j] * A[c * LD + j];
-      }
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < D * D; e += NT) {
-    const int i = e / D, j = e - i * D;
-    if (j > i) A[i * LD + j] = 0.0;
-  }
-  __syncthreads();
-
-  // 2. T = G_Q L (A operand G_Q from global fp32, B operand L from LDS).
+  // 1. T = G_Q L (A operand G_Q fp32 -> fp64, B operand L, both from global).
   f64x4 acc[RB][CB];
 #pragma unroll
   for (int a = 0; a < RB; ++a)
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
     for (int a = 0; a < RB; ++a) av[a] = (double)GQ[(size_t)((wave * RB + a) * 16 + (lane & 15)) * D + kk];
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
-      const double bv = A[kk * LD + c * 16 + (lane & 15)];
+      const double bv = Lg[(size_t)kk * D + c * 16 + (lane & 15)];
 #pragma unroll
       for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
     }
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
   __threadfence();
   __syncthreads();
 
-  // 3. S = L^T T (A operand L^T from LDS, B operand T from global).
+  // 2. S = L^T T (A operand L^T, B operand T, from global) into LDS.
 #pragma unroll
   for (int a = 0; a < RB; ++a)
 #pragma unroll
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
     const int kk = k + (lane >> 4);
     double av[RB];
 #pragma unroll
-    for (int a = 0; a < RB; ++a) av[a] = A[kk * LD + (wave * RB + a) * 16 + (lane & 15)];
+    for (int a = 0; a < RB; ++a) av[a] = Lg[(size_t)kk * D + (wave * RB + a) * 16 + (lane & 15)];
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       const double bv = T[(size_t)kk * D + c * 16 + (lane & 15)];
@@ -279,7 +283,6 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
       for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
     }
   }
-  __syncthreads();
 #pragma unroll
   for (int a = 0; a < RB; ++a)
 #pragma unroll
@@ -288,47 +291,101 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
       for (int r = 0; r < 4; ++r)
         A[((wave * RB + a) * 16 + 4 * r + (lane >> 4)) * LD + c * 16 + (lane & 15)] = acc[a][c][r];
   __syncthreads();
+  // symmetrise into the lower triangle
   for (int e = tid; e < D * D; e += NT) {
-    const int i = e / D, j = e - i * D;
-    if (j > i) {
-      const double s = 0.5 * (A[i * LD + j] + A[j * LD + i]);
-      A[i * LD + j] = s;
-      A[j * LD + i] = s;
-    }
+    const int i = e / D, j = e % D;
+    if (j < i) A[i * LD + j] = 0.5 * (A[i * LD + j] + A[j * LD + i]);
   }
   __syncthreads();
 
-  // 4. Householder tridiagonalisation of S (similarity, eigenvalues kept).
+  // 3. Householder tridiagonalisation (similarity, eigenvalues kept).  Step k
+  //    reflects rows/columns k+1.. of the trailing m x m block with
+  //    v = x - alpha e1 (x: column k below the diagonal), p = beta A v,
+  //    w = p - (beta/2)(v.p) v, A -= v w^T + w v^T.  Four barriers per step.
   for (int k = 0; k < D - 2; ++k) {
     const int m = D - k - 1, r0 = k + 1;
     const double x = tid < m ? A[(r0 + tid) * LD + k] : 0.0;
-    const double nrm2 = block_sum(x * x);
+    const double part = wave_sum_d(x * x);
+    if (lane == 0) s_red[wave] = part;
+    __syncthreads();
+    double nrm2 = 0.0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) nrm2 += s_red[w];
     const double x0 = A[r0 * LD + k];
     const double alpha = x0 >= 0.0 ? -sqrt(nrm2) : sqrt(nrm2);
     const double vn2 = nrm2 - x0 * x0 + (x0 - alpha) * (x0 - alpha);
-    if (tid == 0) s_d[k] = (float)A[k * LD + k];
-    if (!(vn2 > 0.0)) {
-      if (tid == 0) s_e[k] = (float)x0;
+    if (tid == 0) {
+      s_d[k] = (float)A[k * LD + k];
+      s_e[k] = (float)(vn2 > 0.0 ? alpha : x0);
+    }
+    if (!(vn2 > 0.0)) {  // uniform: the column is already reduced
+      __syncthreads();
       continue;
     }
-    if (tid == 0) s_e[k] = (float)alpha;
     const double beta = 2.0 / vn2;
     if (tid < m) s_v[tid] = tid == 0 ? x0 - alpha : x;
     __syncthreads();
-    if (tid < m) {
-      const double* row = A + (r0 + tid) * LD + r0;
-      double s = 0.0;
-      for (int j = 0; j < m; ++j) s += row[j] * s_v[j];
-      s_p[tid] = beta * s;
+    // p = beta A v: two threads per row, each over half of the columns with
+    // four partial sums; the symmetric element (i, j > i) is read at (j, i)
+    {
+      const int i = tid >> 1, hh = tid & 1;
+      const int half = (m + 1) >> 1, jb = hh * half, je = min(m, jb + half);
+      double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+      if (i < m) {
+        auto a_ij = [&](int j) { return j <= i ? A[(r0 + i) * LD + r0 + j] : A[(r0 + j) * LD + r0 + i]; };
+        int j = jb;
+        for (; j + 7 < je; j += 8) {
+          s0 += a_ij(j) * s_v[j] + a_ij(j + 4) * s_v[j + 4];
+          s1 += a_ij(j + 1) * s_v[j + 1] + a_ij(j + 5) * s_v[j + 5];
+          s2 += a_ij(j + 2) * s_v[j + 2] + a_ij(j + 6) * s_v[j + 6];
+          s3 += a_ij(j + 3) * s_v[j + 3] + a_ij(j + 7) * s_v[j + 7];
+        }
+        for (; j < je; ++j) s0 += a_ij(j) * s_v[j];
+      }
+      double sum = (s0 + s1) + (s2 + s3);
+      sum += __shfl_xor(sum, 1);
+      const double pi = beta * sum;
+      if (hh == 0 && i < m) s_p[i] = pi;
+      const double vp = wave_sum_d((hh == 0 && i < m) ? s_v[i] * pi : 0.0);
+      if (lane == 0) s_red2[wave] = vp;
     }
     __syncthreads();
-    const double kk = 0.5 * beta * block_sum(tid < m ? s_v[tid] * s_p[tid] : 0.0);
-    if (tid < m) s_p[tid] -= kk * s_v[tid];
-    __syncthreads();
-    for (int i = wave; i < m; i += NWAVE) {
-      const double vi = s_v[i], wi = s_p[i];
-      double* row = A + (r0 + i) * LD + r0;
-      for (int j = lane; j < m; j += 64) row[j] -= vi * s_p[j] + wi * s_v[j];
+    double vp = 0.0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) vp += s_red2[w];
+    const double kk = 0.5 * beta * vp;
+    // lane j's entries of v and w for columns j and j + 64 stay in registers;
+    // each wave updates four of its rows per pass so their LDS round trips
+    // overlap
+    double vj[2], wj[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int j = lane + 64 * c;
+      vj[c] = j < m ? s_v[j] : 0.0;
+      wj[c] = j < m ? s_p[j] - kk * vj[c] : 0.0;
+    }
+    for (int i0 = wave; i0 < m; i0 += 4 * NWAVE) {
+      double vi[4], wi[4], a[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = min(i0 + q * NWAVE, m - 1);
+        vi[q] = s_v[i];
+        wi[q] = s_p[i] - kk * vi[q];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int j = lane + 64 * c;
+          a[q][c] = j <= i ? A[(r0 + i) * LD + r0 + j] : 0.0;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q * NWAVE;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int j = lane + 64 * c;
+          if (i < m && j <= i) A[(r0 + i) * LD + r0 + j] = a[q][c] - (vi[q] * wj[c] + wi[q] * vj[c]);
+        }
+      }
     }
     __syncthreads();
   }
@@ -469,6 +526,7 @@ hipError_t launch_label(const LabelArgs& a, hipStream_t s) {
   g.wq = a.w_q;
   g.wk = a.w_k;
   g.gram = (float*)(ws + lo.gram);
+  g.lscr = (double*)(ws + lo.lscr);
   g.tscr = (double*)(ws + lo.tscr);
   g.tri = (float*)(ws + lo.tri);
   g.er_head = a.er_head ? a.er_head : (float*)(ws + lo.erh);
@@ -485,6 +543,11 @@ hipError_t launch_label(const LabelArgs& a, hipStream_t s) {
       if (a.bf16) gram_kernel<uint16_t, 64><<<n_mats, NT, 0, s>>>(g);
       else gram_kernel<float, 64><<<n_mats, NT, 0, s>>>(g);
     }
+  }
+  {
+    KTimer t("cholesky", s);
+    if (a.d == 128) chol_kernel<128><<<a.L * a.Hkv, NT, 0, s>>>(g);
+    else chol_kernel<64><<<a.L * a.Hkv, NT, 0, s>>>(g);
   }
   {
     KTimer t("spectrum", s);
