@@ -221,11 +221,11 @@ __global__ __launch_bounds__(NT) void chol_kernel(LGeo g) {
 // cores, then Householder tridiagonalisation of S in LDS, holding only the
 // lower triangle of the symmetric trailing matrix.
 template <int D>
-__global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
-  constexpr int LD = D + 1;
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void spectrum_kernel(LGeo g) {
   constexpr int RB = D / 64;  // 16-row bands per wave
   constexpr int CB = D / 16;  // 16-col bands
-  __shared__ double s_m[D * LD];
+  constexpr int CH = CB / 2;  // column bands per pass
+  __shared__ double s_m[D * (D + 1) / 2];
   __shared__ double s_v[D], s_p[D];
   __shared__ double s_red[NWAVE], s_red2[NWAVE];
   __shared__ float s_d[D], s_e[D];
@@ -236,67 +236,84 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
   const float* GQ = g.gram + (size_t)head * D * D;
   const double* Lg = g.lscr + (size_t)grp * D * D;
   double* A = s_m;
+  auto pk = [](int i, int j) { return i * (i + 1) / 2 + j; };  // (i, j <= i)
 
-  // 1. T = G_Q L (A operand G_Q fp32 -> fp64, B operand L, both from global).
-  f64x4 acc[RB][CB];
-#pragma unroll
-  for (int a = 0; a < RB; ++a)
-#pragma unroll
-    for (int c = 0; c < CB; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int k = 0; k < D; k += 4) {
-    const int kk = k + (lane >> 4);
-    double av[RB];
-#pragma unroll
-    for (int a = 0; a < RB; ++a) av[a] = (double)GQ[(size_t)((wave * RB + a) * 16 + (lane & 15)) * D + kk];
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const double bv = Lg[(size_t)kk * D + c * 16 + (lane & 15)];
-#pragma unroll
-      for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
-    }
-  }
+  // 1. T = G_Q L (A operand G_Q fp32 -> fp64, B operand L, both from global),
+  //    in two halves of the columns to bound the accumulator registers.
   double* T = g.tscr + (size_t)head * D * D;
+  f64x4 acc[RB][CH];
+  for (int c0 = 0; c0 < CB; c0 += CH) {
 #pragma unroll
-  for (int a = 0; a < RB; ++a)
+    for (int a = 0; a < RB; ++a)
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
+      for (int c = 0; c < CH; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int k = 0; k < D; k += 4) {
+      const int kk = k + (lane >> 4);
+      double av[RB];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        T[(size_t)((wave * RB + a) * 16 + 4 * r + (lane >> 4)) * D + c * 16 + (lane & 15)] = acc[a][c][r];
+      for (int a = 0; a < RB; ++a) av[a] = (double)GQ[(size_t)((wave * RB + a) * 16 + (lane & 15)) * D + kk];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const double bv = Lg[(size_t)kk * D + (c0 + c) * 16 + (lane & 15)];
+#pragma unroll
+        for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          T[(size_t)((wave * RB + a) * 16 + 4 * r + (lane >> 4)) * D + (c0 + c) * 16 + (lane & 15)] = acc[a][c][r];
+  }
   __threadfence();
   __syncthreads();
 
-  // 2. S = L^T T (A operand L^T, B operand T, from global) into LDS.
+  // 2. S = L^T T (A operand L^T, B operand T, from global) in two column
+  //    halves, symmetrised into the packed lower triangle straight from the
+  //    registers: each pass first writes its elements on or below the
+  //    diagonal (halved off it), then, after a barrier, adds half of each of
+  //    its elements above the diagonal to the mirror element -- which an
+  //    earlier write of this pass or of the first pass placed.
+  for (int c0 = 0; c0 < CB; c0 += CH) {
 #pragma unroll
-  for (int a = 0; a < RB; ++a)
+    for (int a = 0; a < RB; ++a)
 #pragma unroll
-    for (int c = 0; c < CB; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int k = 0; k < D; k += 4) {
-    const int kk = k + (lane >> 4);
-    double av[RB];
+      for (int c = 0; c < CH; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int k = 0; k < D; k += 4) {
+      const int kk = k + (lane >> 4);
+      double av[RB];
 #pragma unroll
-    for (int a = 0; a < RB; ++a) av[a] = Lg[(size_t)kk * D + (wave * RB + a) * 16 + (lane & 15)];
+      for (int a = 0; a < RB; ++a) av[a] = Lg[(size_t)kk * D + (wave * RB + a) * 16 + (lane & 15)];
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const double bv = T[(size_t)kk * D + c * 16 + (lane & 15)];
+      for (int c = 0; c < CH; ++c) {
+        const double bv = T[(size_t)kk * D + (c0 + c) * 16 + (lane & 15)];
 #pragma unroll
-      for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
+        for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
+      }
     }
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = (wave * RB + a) * 16 + 4 * r + (lane >> 4), j = (c0 + c) * 16 + (lane & 15);
+          if (j <= i) A[pk(i, j)] = j == i ? acc[a][c][r] : 0.5 * acc[a][c][r];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = (wave * RB + a) * 16 + 4 * r + (lane >> 4), j = (c0 + c) * 16 + (lane & 15);
+          if (j > i) A[pk(j, i)] += 0.5 * acc[a][c][r];
+        }
+    __syncthreads();
   }
-#pragma unroll
-  for (int a = 0; a < RB; ++a)
-#pragma unroll
-    for (int c = 0; c < CB; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        A[((wave * RB + a) * 16 + 4 * r + (lane >> 4)) * LD + c * 16 + (lane & 15)] = acc[a][c][r];
-  __syncthreads();
-  // symmetrise into the lower triangle
-  for (int e = tid; e < D * D; e += NT) {
-    const int i = e / D, j = e % D;
-    if (j < i) A[i * LD + j] = 0.5 * (A[i * LD + j] + A[j * LD + i]);
-  }
-  __syncthreads();
 
   // 3. Householder tridiagonalisation (similarity, eigenvalues kept).  Step k
   //    reflects rows/columns k+1.. of the trailing m x m block with
@@ -304,18 +321,18 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
   //    w = p - (beta/2)(v.p) v, A -= v w^T + w v^T.  Four barriers per step.
   for (int k = 0; k < D - 2; ++k) {
     const int m = D - k - 1, r0 = k + 1;
-    const double x = tid < m ? A[(r0 + tid) * LD + k] : 0.0;
+    const double x = tid < m ? A[pk(r0 + tid, k)] : 0.0;
     const double part = wave_sum_d(x * x);
     if (lane == 0) s_red[wave] = part;
     __syncthreads();
     double nrm2 = 0.0;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) nrm2 += s_red[w];
-    const double x0 = A[r0 * LD + k];
+    const double x0 = A[pk(r0, k)];
     const double alpha = x0 >= 0.0 ? -sqrt(nrm2) : sqrt(nrm2);
     const double vn2 = nrm2 - x0 * x0 + (x0 - alpha) * (x0 - alpha);
     if (tid == 0) {
-      s_d[k] = (float)A[k * LD + k];
+      s_d[k] = (float)A[pk(k, k)];
       s_e[k] = (float)(vn2 > 0.0 ? alpha : x0);
     }
     if (!(vn2 > 0.0)) {  // uniform: the column is already reduced
@@ -332,7 +349,7 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
       const int half = (m + 1) >> 1, jb = hh * half, je = min(m, jb + half);
       double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
       if (i < m) {
-        auto a_ij = [&](int j) { return j <= i ? A[(r0 + i) * LD + r0 + j] : A[(r0 + j) * LD + r0 + i]; };
+        auto a_ij = [&](int j) { return j <= i ? A[pk(r0 + i, r0 + j)] : A[pk(r0 + j, r0 + i)]; };
         int j = jb;
         for (; j + 7 < je; j += 8) {
           s0 += a_ij(j) * s_v[j] + a_ij(j + 4) * s_v[j + 4];
@@ -374,7 +391,7 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int j = lane + 64 * c;
-          a[q][c] = j <= i ? A[(r0 + i) * LD + r0 + j] : 0.0;
+          a[q][c] = j <= i ? A[pk(r0 + i, r0 + j)] : 0.0;
         }
       }
 #pragma unroll
@@ -383,16 +400,16 @@ __global__ __launch_bounds__(NT) void spectrum_kernel(LGeo g) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int j = lane + 64 * c;
-          if (i < m && j <= i) A[(r0 + i) * LD + r0 + j] = a[q][c] - (vi[q] * wj[c] + wi[q] * vj[c]);
+          if (i < m && j <= i) A[pk(r0 + i, r0 + j)] = a[q][c] - (vi[q] * wj[c] + wi[q] * vj[c]);
         }
       }
     }
     __syncthreads();
   }
   if (tid == 0) {
-    s_d[D - 2] = (float)A[(D - 2) * LD + D - 2];
-    s_e[D - 2] = (float)A[(D - 1) * LD + D - 2];
-    s_d[D - 1] = (float)A[(D - 1) * LD + D - 1];
+    s_d[D - 2] = (float)A[pk(D - 2, D - 2)];
+    s_e[D - 2] = (float)A[pk(D - 1, D - 2)];
+    s_d[D - 1] = (float)A[pk(D - 1, D - 1)];
     s_e[D - 1] = 0.f;
   }
   __syncthreads();
