@@ -27,6 +27,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
@@ -77,7 +78,7 @@ LabelLayout label_layout(int L, int Hq, int Hkv, int d) {
 // a row band of 32 x 32 output tiles.  MFMA 32x32: output element
 // (8*(r/4) + 4*(lane/32) + r%4, lane%32) sits in register r of lane.
 template <typename E, int D>
-__global__ __launch_bounds__(NT) void gram_kernel(LGeo g) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void gram_kernel(LGeo g) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int KT = 128 / sizeof(E);           // elements per k tile
   constexpr int LDW = BF ? KT + 8 : KT + 1;     // padded LDS row
@@ -91,16 +92,19 @@ __global__ __launch_bounds__(NT) void gram_kernel(LGeo g) {
   const int nq = g.L * g.Hq;
   const E* W = m < nq ? (const E*)g.wq + (size_t)m * D * g.dm
                       : (const E*)g.wk + (size_t)(m - nq) * D * g.dm;
-  uint4 reg[CH];
-  auto gload = [&](int k0) {
+  // two k tiles in flight: a ring of two register sets, the loop unrolled by
+  // two so that each set is named statically
+  uint4 ra[CH], rb2[CH];
+  auto gload = [&](int k0, uint4* reg) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int id = tid + c * NT;
       const int row = id / CPR, col = (id % CPR) * (16 / (int)sizeof(E));
-      reg[c] = *reinterpret_cast<const uint4*>(W + (size_t)row * g.dm + k0 + col);
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)row * g.dm + k0 + col));
+      reg[c] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const uint4* reg) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int id = tid + c * NT;
@@ -121,12 +125,11 @@ __global__ __launch_bounds__(NT) void gram_kernel(LGeo g) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   const int nk = g.dm / KT;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
+  // one k tile: tile kt is in LDS buffer kt & 1, tile kt + 1 in `next`; the
+  // loads of tile kt + 2 go to `free` (which held tile kt)
+  auto step = [&](int kt, uint4* next, uint4* free) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * KT);
+    if (kt + 2 < nk) gload((kt + 2) * KT, free);
     if constexpr (BF) {
 #pragma unroll
       for (int ks = 0; ks < KT; ks += 16) {
@@ -152,8 +155,16 @@ __global__ __launch_bounds__(NT) void gram_kernel(LGeo g) {
         }
       }
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (kt + 1 < nk) sstore(buf ^ 1, next);
     __syncthreads();
+  };
+  gload(0, ra);
+  if (nk > 1) gload(KT, rb2);
+  sstore(0, ra);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, rb2, ra);
+    if (kt + 1 < nk) step(kt + 1, ra, rb2);
   }
   float* out = g.gram + (size_t)m * D * D;
 #pragma unroll
