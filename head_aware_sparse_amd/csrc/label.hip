@@ -179,9 +179,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void gr
 }
 
 // ------------------------------------------------------------------ spectrum
+// fp64 lane moves: DPP on the two 32-bit halves, readlane into a uniform value
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const unsigned long long u = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(u & 0xFFFFFFFFull), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const unsigned long long u = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane((int)(u & 0xFFFFFFFFull), l);
+  const int hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+  return __longlong_as_double(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+// Sum over the wave, identical in every lane: DPP within each 16-lane row
+// (quad swaps, half-row and row mirrors), then the four row sums.
 __device__ __forceinline__ double wave_sum_d(double x) {
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dpp_d<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_d<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_d<0x141>(x);  // row_half_mirror
+  x += dpp_d<0x140>(x);  // row_mirror
+  return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
 }
 
 // Cholesky G_K = L L^T of each key head's Gram matrix (fp64, in LDS), once
@@ -371,7 +390,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
         for (; j < je; ++j) s0 += a_ij(j) * s_v[j];
       }
       double sum = (s0 + s1) + (s2 + s3);
-      sum += __shfl_xor(sum, 1);
+      sum += dpp_d<0xB1>(sum);  // the row's other half (lane pair)
       const double pi = beta * sum;
       if (hh == 0 && i < m) s_p[i] = pi;
       const double vp = wave_sum_d((hh == 0 && i < m) ? s_v[i] * pi : 0.0);
