@@ -42,38 +42,55 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Lane exchanges across 16-lane rows (gfx950): with both operands equal,
+// v_permlane16_swap / v_permlane32_swap return x and the value of lane ^ 16
+// (lane ^ 32) as the pair, in some order; their sum or max is the same in
+// both lanes of each pair.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Sum over aligned groups of N consecutive lanes; every lane of the group
-// receives the total.  quad_perm swaps, then half-row and row mirrors.
+// receives the total.  quad_perm swaps, half-row and row mirrors, then the
+// row exchanges.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
   if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
   if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
   if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  if constexpr (N >= 32) x = xor16_sum(x);
+  if constexpr (N >= 64) x = xor32_sum(x);
   return x;
 }
 
-// Max over aligned groups of N (<= 16) consecutive lanes, as group_sum.
+// Max over aligned groups of N consecutive lanes, as group_sum.
 template <int N>
 __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 2) x = fmaxf(x, dpp<0xB1>(x));
   if constexpr (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
   if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
   if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
-  static_assert(N <= 16, "group_max covers one DPP row");
+  if constexpr (N >= 32) x = xor16_max(x);
+  if constexpr (N >= 64) x = xor32_max(x);
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
+__device__ __forceinline__ float wave_max(float x) { return group_max<64>(x); }
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -279,13 +296,23 @@ __device__ __forceinline__ float score_one(const E* row, const float* s_q, int R
 
 constexpr int kMaxR = 128;  // k_dom row elements: 2 * (d/2) at most
 
+// Wave-wide reduction of a uint32 with the same lane exchanges as group_sum.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u(uint32_t x, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(r32[0], r32[1]);
+}
 __device__ __forceinline__ uint32_t wave_min_u(uint32_t x) {
-  for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
+  return wave_reduce_u(x, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 __device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
+  return wave_reduce_u(x, [](uint32_t a, uint32_t b) { return max(a, b); });
 }
 
 __device__ uint2 item_tau(const Geo& g, int item, uint32_t* s_hist, int* s_w, uint32_t* s_res) {
@@ -437,7 +464,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
           if (m) {
             int wbase = 0;
             if (lane == 0) wbase = atomicAdd(&s_n, __popcll(m));
-            wbase = __shfl(wbase, 0);
+            wbase = __builtin_amdgcn_readfirstlane(wbase);
             if (cand) {
               const int at = wbase + mbcnt(m);
               if (at < kCandUnit) {
@@ -534,7 +561,7 @@ __global__ __launch_bounds__(NT) void select_a_kernel(Geo g) {
         if (m) {
           int wbase = 0;
           if (lane == 0) wbase = atomicAdd(&s_n, __popcll(m));
-          wbase = __shfl(wbase, 0);
+          wbase = __builtin_amdgcn_readfirstlane(wbase);
           if (eq) s_cand[wbase + mbcnt(m)] = make_uint2(key, (uint32_t)tok);
         }
       }
@@ -739,10 +766,8 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
       t_max = max(t_max, t);
     }
   });
-  for (int o = 32; o >= 1; o >>= 1) {
-    n_eq += (uint32_t)__shfl_xor((int)n_eq, o);
-    t_max = max(t_max, (uint32_t)__shfl_xor((int)t_max, o));
-  }
+  n_eq = wave_reduce_u(n_eq, [](uint32_t a, uint32_t b) { return a + b; });
+  t_max = wave_max_u(t_max);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) {
@@ -1229,12 +1254,18 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
         }
       }
     }
+    // sum over the row groups of the wave (lanes LPR, 2 LPR, ... apart)
+    static_assert(LPR >= 8 && LPR <= 32, "row groups of 8 to 32 lanes");
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[h][c] += __shfl_xor(acc[h][c], o);
+      for (int c = 0; c < CPL; ++c) {
+        float x = acc[h][c];
+        if constexpr (LPR <= 8) x += dpp<0x128>(x);  // row_ror:8 = lane ^ 8 within a row
+        if constexpr (LPR <= 16) x = xor16_sum(x);
+        x = xor32_sum(x);
+        acc[h][c] = x;
+      }
     if (rsub == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
