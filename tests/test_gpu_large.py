@@ -111,3 +111,28 @@ def test_clsa_attention_paths(over):
         U.check_index_set(idx[b, g], scores, cfg.n_fac, f"clsa {over} idx b{b} g{g}")
         for n in range(cfg.n_layers):
             U.check_out(out[n, b, g * G:(g + 1) * G], ref[n], f"clsa {over} out n{n} b{b} g{g}")
+
+
+def test_max_context_4m_tokens():
+    """The largest context the library takes (4194304 tokens: 1024 chunks of
+    4096), on the general selection path, one retrieval and one streaming
+    group; the needles planted in the retrieval group are selected."""
+    from tests.test_gpu_decode import _check_items
+    cfg = R.get_config("c1", ctx_len=4194304, batch=1, n_q_heads=8, n_kv_heads=2)
+    print("case T=4194304", flush=True)
+    lab = np.array([[1, 0]], np.uint8)
+    case = U.DeviceCase(cfg, labels=lab)
+    out, idx = _check_items(case, [(0, 0, 0), (0, 0, 1)], "T4M")
+    assert np.isin(R.needle_positions(cfg, 0, 0, 0), idx[0, 0, 0]).all()
+
+
+def test_max_pairs_8192():
+    """8192 (layer, KV group) pairs in one call (the most the plan holds),
+    half of them retrieval, checked on items spread over the layers."""
+    from tests.test_gpu_decode import _check_items
+    cfg = R.get_config("c1", n_layers=1024, ctx_len=512, batch=1, n_q_heads=8, n_kv_heads=8, n_fac=64, window=64)
+    print("case 8192 pairs", flush=True)
+    lab = (np.random.default_rng(3).random((cfg.n_layers, cfg.n_kv_heads)) < 0.5).astype(np.uint8)
+    case = U.DeviceCase(cfg, labels=lab)
+    items = [(l, 0, g) for l in (0, 1, 511, 512, 1022, 1023) for g in (0, 3, 7)]
+    _check_items(case, items, "8192 pairs")
