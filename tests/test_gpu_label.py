@@ -88,3 +88,34 @@ def test_rank_deficient_key_projection():
     print("case label rank-deficient", flush=True)
     got, ref = _run(cfg, k=2, w=(w_q, w_k))
     _check(got, ref, 2)
+
+
+@pytest.mark.parametrize("over", [
+    dict(kv_dtype="f32"),                           # fp32 weights, d 128
+    dict(d_head=64, n_dom=8),                       # bf16 weights, d 64
+    dict(n_q_heads=64, n_kv_heads=8),               # 8 query heads per group
+], ids=["f32-d128", "bf16-d64", "G8"])
+def test_weight_types_and_shapes(over):
+    cfg = R.get_config("c1", **over)
+    print(f"case label {over}", flush=True)
+    got, ref = _run(cfg, k=cfg.n_retrieval)
+    _check(got, ref, cfg.n_retrieval)
+
+
+def test_rank_extremes():
+    """k = 0 labels every pair streaming, k = L * H_kv every pair retrieval."""
+    cfg = R.get_config("c0", n_layers=2)
+    print("case label k extremes", flush=True)
+    for k in (0, cfg.n_layers * cfg.n_kv_heads):
+        got, ref = _run(cfg, k=k)
+        _check(got, ref, k)
+        assert got[2].sum() == k
+
+
+def test_max_pairs_8192():
+    """1024 layers x 8 KV groups: the most (layer, group) pairs per call, all
+    ranked together."""
+    cfg = R.get_config("c0", n_layers=1024, n_q_heads=8, n_kv_heads=8, n_retrieval=100)
+    print("case label 8192 pairs", flush=True)
+    got, ref = _run(cfg, k=100)
+    _check(got, ref, 100)
