@@ -3,7 +3,9 @@
 // argument returns without touching the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cmath>
 #include <cstring>
@@ -239,6 +241,37 @@ has_status persistent_grid(int& grid) {
     if ((p) && !aligned16(p)) return fail(HAS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
   } while (0)
 
+// HAS_DEBUG=1: the array contents the kernels rely on are copied to the
+// host (synchronising the stream) and checked before anything is launched.
+bool debug_checks() {
+  const char* e = std::getenv("HAS_DEBUG");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+has_status debug_check_arrays(const has_decode_dims* d, int pairs, const int32_t* i_dom, const uint8_t* labels,
+                              int label_pairs, void* stream) {
+  std::vector<int32_t> dom((size_t)pairs * d->n_dom);
+  std::vector<uint8_t> lab(labels ? (size_t)label_pairs : 0);
+  hipError_t e = hipMemcpyAsync(dom.data(), i_dom, dom.size() * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess && labels)
+    e = hipMemcpyAsync(lab.data(), labels, lab.size(), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "HAS_DEBUG copy");
+  const int hd = d->d_head / 2;
+  std::vector<uint8_t> seen(hd);
+  for (int p = 0; p < pairs; ++p) {
+    std::fill(seen.begin(), seen.end(), 0);
+    for (int i = 0; i < d->n_dom; ++i) {
+      const int f = dom[(size_t)p * d->n_dom + i];
+      if (f < 0 || f >= hd) return fail(HAS_ERR_INVALID_ARG, "i_dom[%d][%d] = %d outside [0, %d)", p, i, f, hd);
+      if (seen[f]++) return fail(HAS_ERR_INVALID_ARG, "i_dom[%d] repeats chunk %d", p, f);
+    }
+  }
+  for (size_t i = 0; i < lab.size(); ++i)
+    if (lab[i] > 1) return fail(HAS_ERR_INVALID_ARG, "labels[%zu] = %d is neither 0 nor 1", i, (int)lab[i]);
+  return HAS_OK;
+}
+
 has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, const void* q_index,
                       const void* k_cache, const void* v_cache, const void* k_dom, const int32_t* i_dom,
                       const uint8_t* labels, float* out, int32_t* idx_out, void* ws, size_t ws_bytes,
@@ -271,6 +304,11 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
   g.host_plan = (clsa && labels == nullptr && g.prefilter) ? 1 : 0;
   g.out = out;
   g.idx_out = idx_out;
+  if (debug_checks()) {
+    s = debug_check_arrays(dims, clsa ? dims->n_kv_heads : dims->n_layers * dims->n_kv_heads, i_dom, labels,
+                           dims->n_layers * dims->n_kv_heads, stream);
+    if (s != HAS_OK) return s;
+  }
   s = persistent_grid(g.grid);
   if (s != HAS_OK) return s;
   int dev = 0;
@@ -394,6 +432,10 @@ has_status kdom_pack(const has_decode_dims* dims, const void* k_cache, const int
   Layout L = make_layout(dims, false);
   L.g.k = k_cache;
   L.g.i_dom = i_dom;
+  if (debug_checks()) {
+    s = debug_check_arrays(dims, dims->n_layers * dims->n_kv_heads, i_dom, nullptr, 0, stream);
+    if (s != HAS_OK) return s;
+  }
   s = persistent_grid(L.g.grid);
   if (s != HAS_OK) return s;
   hipError_t e = has::launch_kdom_pack(L.g, k_dom, (hipStream_t)stream);

@@ -269,7 +269,9 @@ __device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
   for (int c = threadIdx.x; c < g.R; c += NT) {
     float v = 0.f;
     if (c < 2 * g.n_dom) {
-      const int f = dom[c >> 1], cc = c & 1;
+      // i_dom entries lie in [0, d/2) by contract; the clamp keeps an invalid
+      // one from reading outside the query row
+      const int f = min(max(dom[c >> 1], 0), hd - 1), cc = c & 1;
       const int chn = g.interleaved ? 2 * f + cc : f + cc * hd;
       float sum = 0.f;
       for (int h = 0; h < g.G; ++h) sum += Vec<E>::one(qg, (size_t)h * g.d + chn);
@@ -1560,7 +1562,7 @@ __global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd
         const int e = part * EPV + q;
         E v = E(0);
         if (e < 2 * g.n_dom) {
-          const int f = dom[e >> 1], cc = e & 1;
+          const int f = min(max(dom[e >> 1], 0), hd - 1), cc = e & 1;  // as in group_query_dom
           v = row[g.interleaved ? 2 * f + cc : f + cc * hd];
         }
         vals[q] = v;

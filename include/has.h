@@ -25,8 +25,17 @@
  *     HAS_ERR_HIP means a HIP call failed while enqueueing; outputs are then
  *     undefined.  has_last_error() gives a message (thread-local).
  *   - Array contents are not checked (finite values; i_dom entries distinct
- *     and in [0, d_head/2); labels in {0, 1}).
- *   - Threads may call the library concurrently on distinct streams.
+ *     and in [0, d_head/2); labels in {0, 1}), except when the environment
+ *     variable HAS_DEBUG is "1": then i_dom and labels are copied to the host
+ *     (synchronising `stream`) and checked before anything is launched, and
+ *     a violation returns HAS_ERR_INVALID_ARG.
+ *   - The decode entry points run the streaming groups' attention on a side
+ *     stream that the library creates, with two events, on its first decode
+ *     call on each device (kept until the process ends); the side stream is
+ *     ordered after the caller's stream and joined back into it before the
+ *     call's last kernel, so the caller sees one ordered sequence on `stream`.
+ *   - Threads may call the library concurrently on distinct streams (their
+ *     side-stream work is serialised).
  */
 #ifndef HAS_H_
 #define HAS_H_

@@ -272,3 +272,29 @@ def test_selection_path_boundaries(over):
     print(f"case boundaries {over}", flush=True)
     case = U.DeviceCase(cfg)
     _check_items(case, _all_items(cfg)[:cfg.n_kv_heads * 2], f"boundary {over}")
+
+
+def test_debug_checks_reject_bad_arrays(monkeypatch):
+    """HAS_DEBUG=1: i_dom out of range or repeated, or a label other than 0/1,
+    is rejected before anything is launched; valid arrays run unchanged."""
+    cfg = R.get_config("c1", ctx_len=3000, n_fac=200, batch=1)
+    case = U.DeviceCase(cfg)
+    ref_out, ref_idx, ws = case.run()
+    monkeypatch.setenv("HAS_DEBUG", "1")
+    out, idx, _ = case.run(ws=ws)
+    assert (out == ref_out).all() and (idx == ref_idx).all()
+    good_dom, good_lab = case.i_dom.clone(), case.labels.clone()
+    for what, fix in [("out of range", lambda: case.i_dom[0, 1].__setitem__(0, cfg.d_head // 2)),
+                      ("repeated", lambda: case.i_dom[0, 2].__setitem__(1, int(case.i_dom[0, 2, 0]))),
+                      ("label 2", lambda: case.labels[0].__setitem__(3, 2))]:
+        case.i_dom.copy_(good_dom)
+        case.labels.copy_(good_lab)
+        fix()
+        torch.cuda.synchronize()
+        with pytest.raises(H.HasError) as e:
+            case.run(ws=ws)
+        assert e.value.status == 1, what
+        with pytest.raises(H.HasError):
+            H.kdom_pack(case.kd_dims, case.k, case.i_dom, case.k_dom) if what != "label 2" else case.run(ws=ws)
+    case.i_dom.copy_(good_dom)
+    case.labels.copy_(good_lab)
