@@ -1636,6 +1636,10 @@ hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Streaming rows per call (over all (layer, sequence, group) items) from which
+// the streaming attention runs on the side stream.
+constexpr long long kSideStreamRows = 1LL << 20;
+
 hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   hipError_t e;
   const hipStream_t s = ss.main;
@@ -1651,7 +1655,11 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   // Streaming groups need nothing but the plan: their attention runs on the
   // side stream, overlapping the scoring and selection of retrieval groups.
   // (The shared-index mode without labels has none.)
-  const bool side = !(g.clsa && g.labels == nullptr);
+  // Streaming groups run on the side stream when their rows are worth
+  // overlapping with scoring; small steps (latency-bound) attend to them in
+  // the retrieval attention's launch instead and skip the event waits.
+  const bool any_stream = !(g.clsa && g.labels == nullptr);
+  const bool side = any_stream && (long long)n_att_items * g.n_srows >= kSideStreamRows;
   if (side) {
     if ((e = hipEventRecord(ss.fork, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ss.side, ss.fork, 0)) != hipSuccess) return e;
@@ -1719,13 +1727,21 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
-    g.attn_mode = 1;
+    // mode 1: retrieval units only; mode 0: retrieval and streaming units
+    const bool with_stream = any_stream && !side;
+    g.attn_mode = with_stream && !g.clsa_mfma ? 0 : 1;
     KTimer t("attention_fac", s);
     if (g.clsa_mfma) {
       attn_clsa_mfma_kernel<<<clampi((long long)g.Hkv * g.B * g.nch_f, 1, g.grid), NT, 0, s>>>(g);
       e = hipGetLastError();
+      if (e == hipSuccess && with_stream) {
+        Geo gs = g;
+        gs.attn_mode = 2;
+        e = launch_attn(gs, clampi(n_att_items * (long long)g.nch_s, 1, g.grid), s);
+      }
     } else {
-      e = launch_attn(g, clampi(n_att_items * (long long)g.nch_f, 1, g.grid), s);
+      const long long units = n_att_items * (long long)(g.nch_f + (with_stream ? g.nch_s : 0));
+      e = launch_attn(g, clampi(units, 1, g.grid), s);
     }
   }
   if (e != hipSuccess) return e;
