@@ -392,8 +392,13 @@ __global__ __launch_bounds__(NT) void tau_kernel(Geo g) {
 // 64/V-token slabs, the V lanes of a row reduce their partial dot products,
 // and lane L keeps the score of token (L % V) * 64/V + L / V, so each wave
 // writes 64 consecutive scores.
-template <typename E, int V, bool PF>
+// MODE 0: every score and a histogram (general path); 1: prefiltered, tau
+// from tau_kernel; 2: prefiltered, each unit derives tau from the sampled
+// keys itself (steps with few index items, where a separate launch costs
+// more than the redundant work), unit 0 of the item storing it.
+template <typename E, int V, int MODE>
 __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
+  constexpr bool PF = MODE != 0;
   constexpr int EPV = Vec<E>::N;
   constexpr int U = V >= 8 ? 2 : 16 / V;  // 64-token steps in flight per wave (16 loads per lane)
   __shared__ uint32_t s_hist[PF ? 1 : kHistBins];
@@ -424,7 +429,16 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
       const float* qb = g.qbar + (size_t)item * R + (lane % V) * EPV;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) qr[e] = qb[e];
-      tau = g.tau[item].x;
+      if constexpr (MODE == 2) {
+        __shared__ int s_w2[2 * NWAVE];
+        __shared__ uint32_t s_res2[2];
+        static_assert(kCandUnit * sizeof(uint2) >= kHistBins * sizeof(uint32_t), "tau histogram in s_cand");
+        const uint2 t2 = item_tau(g, item, reinterpret_cast<uint32_t*>(s_cand), s_w2, s_res2);
+        tau = t2.x;
+        if (ch == 0 && tid == 0) g.tau[item] = t2;  // for the final kernel
+      } else {
+        tau = g.tau[item].x;
+      }
       if (tid == 0) s_n = 0;
       __syncthreads();
     } else {
@@ -1592,15 +1606,15 @@ hipError_t launch_attn(const Geo& g, int grid, hipStream_t s) {
   return g.d == 128 ? launch_attn_g<float, 128>(g, grid, s) : launch_attn_g<float, 64>(g, grid, s);
 }
 
-template <typename E, bool PF>
+template <typename E, int MODE>
 hipError_t launch_tip_v(const Geo& g, int grid, hipStream_t s) {
   const int V = g.R * (int)sizeof(E) / 16;
   switch (V) {
-    case 1: tip_kernel<E, 1, PF><<<grid, NT, 0, s>>>(g); break;
-    case 2: tip_kernel<E, 2, PF><<<grid, NT, 0, s>>>(g); break;
-    case 4: tip_kernel<E, 4, PF><<<grid, NT, 0, s>>>(g); break;
-    case 8: tip_kernel<E, 8, PF><<<grid, NT, 0, s>>>(g); break;
-    case 16: tip_kernel<E, 16, PF><<<grid, NT, 0, s>>>(g); break;
+    case 1: tip_kernel<E, 1, MODE><<<grid, NT, 0, s>>>(g); break;
+    case 2: tip_kernel<E, 2, MODE><<<grid, NT, 0, s>>>(g); break;
+    case 4: tip_kernel<E, 4, MODE><<<grid, NT, 0, s>>>(g); break;
+    case 8: tip_kernel<E, 8, MODE><<<grid, NT, 0, s>>>(g); break;
+    case 16: tip_kernel<E, 16, MODE><<<grid, NT, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1639,6 +1653,9 @@ hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s) {
 // Streaming rows per call (over all (layer, sequence, group) items) from which
 // the streaming attention runs on the side stream.
 constexpr long long kSideStreamRows = 1LL << 20;
+// Prefiltered scoring units per call (index items x units per item) up to
+// which each unit derives tau itself instead of a separate launch.
+constexpr long long kTauInlineUnits = 512;
 
 hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   hipError_t e;
@@ -1674,6 +1691,7 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     if ((e = hipEventRecord(ss.join, ss.side)) != hipSuccess) return e;
   }
   const int grid_tip = clampi(n_idx_items * g.nch_t, 1, g.grid);
+  const bool tau_inline = n_idx_items * g.nch_tip <= kTauInlineUnits;
   const int grid_item = clampi(n_idx_items, 1, g.grid);
   if (g.prefilter) {
     {
@@ -1682,7 +1700,7 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
       e = g.bf16 ? launch_sample_v<uint16_t>(g, grid_sample, s) : launch_sample_v<float>(g, grid_sample, s);
     }
     if (e != hipSuccess) return e;
-    {
+    if (!tau_inline) {
       KTimer t("tau", s);
       tau_kernel<<<grid_item, NT, 0, s>>>(g);
     }
@@ -1690,7 +1708,10 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     {
       const int grid_tip_pf = clampi(n_idx_items * g.nch_tip, 1, g.grid);
       KTimer t("tip_score", s);
-      e = g.bf16 ? launch_tip_v<uint16_t, true>(g, grid_tip_pf, s) : launch_tip_v<float, true>(g, grid_tip_pf, s);
+      if (tau_inline)
+        e = g.bf16 ? launch_tip_v<uint16_t, 2>(g, grid_tip_pf, s) : launch_tip_v<float, 2>(g, grid_tip_pf, s);
+      else
+        e = g.bf16 ? launch_tip_v<uint16_t, 1>(g, grid_tip_pf, s) : launch_tip_v<float, 1>(g, grid_tip_pf, s);
     }
     if (e != hipSuccess) return e;
     {
@@ -1702,7 +1723,7 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   } else {
     {
       KTimer t("tip_score", s);
-      e = g.bf16 ? launch_tip_v<uint16_t, false>(g, grid_tip, s) : launch_tip_v<float, false>(g, grid_tip, s);
+      e = g.bf16 ? launch_tip_v<uint16_t, 0>(g, grid_tip, s) : launch_tip_v<float, 0>(g, grid_tip, s);
     }
     if (e != hipSuccess) return e;
     {
