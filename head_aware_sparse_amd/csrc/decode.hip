@@ -1669,12 +1669,11 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     plan_kernel<<<grid_plan, NT, 0, s>>>(g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // Streaming groups need nothing but the plan: their attention runs on the
-  // side stream, overlapping the scoring and selection of retrieval groups.
-  // (The shared-index mode without labels has none.)
-  // Streaming groups run on the side stream when their rows are worth
-  // overlapping with scoring; small steps (latency-bound) attend to them in
-  // the retrieval attention's launch instead and skip the event waits.
+  // Streaming groups need nothing but the plan.  When their rows are worth
+  // overlapping with scoring, their attention runs on the side stream beside
+  // the scoring and selection of retrieval groups; small (latency-bound)
+  // steps attend to them in the retrieval attention's launch instead and
+  // skip the event waits.  (The shared-index mode without labels has none.)
   const bool any_stream = !(g.clsa && g.labels == nullptr);
   const bool side = any_stream && (long long)n_att_items * g.n_srows >= kSideStreamRows;
   if (side) {

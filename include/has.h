@@ -29,11 +29,12 @@
  *     variable HAS_DEBUG is "1": then i_dom and labels are copied to the host
  *     (synchronising `stream`) and checked before anything is launched, and
  *     a violation returns HAS_ERR_INVALID_ARG.
- *   - The decode entry points run the streaming groups' attention on a side
- *     stream that the library creates, with two events, on its first decode
- *     call on each device (kept until the process ends); the side stream is
- *     ordered after the caller's stream and joined back into it before the
- *     call's last kernel, so the caller sees one ordered sequence on `stream`.
+ *   - The first decode call on each device creates a side stream and two
+ *     events (kept until the process ends).  When a call's streaming groups
+ *     attend to at least 2^20 cache rows in total, their attention runs on
+ *     that side stream, ordered after the caller's stream and joined back
+ *     into it before the call's last kernel, so the caller sees one ordered
+ *     sequence on `stream`.  Smaller calls enqueue everything on `stream`.
  *   - Threads may call the library concurrently on distinct streams (their
  *     side-stream work is serialised).
  */
