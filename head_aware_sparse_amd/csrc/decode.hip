@@ -1199,27 +1199,36 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
       for (int c = 0; c < CPL; ++c) qr[h][c] *= kScale;
     }
     __syncthreads();
-    // pass 1: logits (log2 domain) into s_z
-    for (int r0 = wave * RPW; r0 < nrows; r0 += AU * RPB) {
-      uint4 raw[AU];
-      int rr[AU];
+    // pass 1: logits (log2 domain) into s_z.  A ring of AU row groups per
+    // wave: each is reloaded with the group AU steps ahead as soon as it has
+    // been used, so AU - 1 loads stay in flight.  Rows past the end load the
+    // last row again (in bounds) and are ignored.
+    constexpr int kStep = AU * RPB;
+    auto row_ptr = [&](const E* base, int r) {
+      return base + (size_t)s_rows[min(r, nrows - 1)] * D + slot * CPL;
+    };
+    uint4 raw[AU];
+    if (nrows > 0) {
+      const int r0 = wave * RPW + rsub;
+#pragma unroll
+      for (int j = 0; j < AU; ++j) raw[j] = ld16_stream(row_ptr(kb, r0 + j * RPB));
+    }
+    for (int r0 = wave * RPW; r0 < nrows; r0 += kStep) {
 #pragma unroll
       for (int j = 0; j < AU; ++j) {
-        rr[j] = r0 + j * RPB + rsub;
-        raw[j] = rr[j] < nrows ? ld16_stream(kb + (size_t)s_rows[rr[j]] * D + slot * CPL)
-                               : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < AU; ++j) {
+        const int r = r0 + j * RPB + rsub;
         float kf[CPL];
         Vec<E>::cvt(raw[j], kf);
+        // the last step loads the first V row groups of pass 2 instead
+        const bool more = r0 + kStep < nrows;
+        raw[j] = ld16_stream(row_ptr(more ? kb : vb, more ? r + kStep : r - r0 + wave * RPW));
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float s = 0.f;
 #pragma unroll
           for (int c = 0; c < CPL; ++c) s += qr[h][c] * kf[c];
           s = group_sum<LPR>(s);
-          if (slot == h && rr[j] < nrows) s_z[h][rr[j]] = s;
+          if (slot == h && r < nrows) s_z[h][r] = s;
         }
       }
     }
@@ -1241,29 +1250,23 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
       }
     }
     __syncthreads();
-    // pass 2: acc += p v
+    // pass 2: acc += p v (the ring already holds the first V row groups)
     float acc[G][CPL];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) acc[h][c] = 0.f;
-    for (int r0 = wave * RPW; r0 < nrows; r0 += AU * RPB) {
-      uint4 raw[AU];
-      int rr[AU];
+    for (int r0 = wave * RPW; r0 < nrows; r0 += kStep) {
 #pragma unroll
       for (int j = 0; j < AU; ++j) {
-        rr[j] = r0 + j * RPB + rsub;
-        raw[j] = rr[j] < nrows ? ld16_stream(vb + (size_t)s_rows[rr[j]] * D + slot * CPL)
-                               : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < AU; ++j) {
-        if (rr[j] < nrows) {
-          float vf[CPL];
-          Vec<E>::cvt(raw[j], vf);
+        const int r = r0 + j * RPB + rsub;
+        float vf[CPL];
+        Vec<E>::cvt(raw[j], vf);
+        raw[j] = ld16_stream(row_ptr(vb, r + kStep));
+        if (r < nrows) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float p = s_z[h][rr[j]];
+            const float p = s_z[h][r];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) acc[h][c] += p * vf[c];
           }
