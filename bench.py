@@ -33,10 +33,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(cfg, labels):
+def algorithmic_bytes(cfg, labels, per_layer_gather=False):
     """Bytes the method must move per step (counted once): dominant key
     channels of retrieval items, selected K+V rows, sink+window K+V rows,
-    queries and outputs.  Scores, histograms and partials are not counted."""
+    queries and outputs.  Scores, histograms and partials are not counted.
+    per_layer_gather: the shared index is attended layer by layer, each layer
+    gathering the selected rows again."""
     import numpy as np
     es = 2 if cfg.bf16 else 4
     d, T = cfg.d_head, cfg.ctx_len
@@ -49,6 +51,8 @@ def algorithmic_bytes(cfg, labels):
         n_str_att = cfg.n_layers * n_idx - n_ret_att
         tip = n_idx * T * 2 * cfg.n_dom * es
         gather = n_idx * cfg.n_fac * row          # one gather serves every layer
+        if per_layer_gather:
+            gather *= cfg.n_layers
         stream = (n_srows * row * cfg.batch * cfg.n_kv_heads) if n_str_att else 0
     else:
         n_ret = int(np.asarray(labels).sum()) * cfg.batch
@@ -121,6 +125,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4"])
+    ap.add_argument("--clsa-mode", default="fused", choices=["fused", "sequential"],
+                    help="shared-index workload: one fused call, or one sparse_select plus one fac_attend per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-label", action="store_true")
     ap.add_argument("--cpu-sample", default="24,72", help="retrieval,streaming items timed on the CPU")
@@ -226,7 +232,21 @@ def main():
     labels = torch.from_numpy(np.ascontiguousarray(labels_np)).cuda()
 
     out = torch.empty((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), dtype=torch.float32, device="cuda")
-    if cfg.clsa:
+    sequential = cfg.clsa and args.clsa_mode == "sequential"
+    if sequential:
+        # the layer-by-layer form: the index once, then one attention call per layer
+        k0, v0, kd0, id0 = k[0], v[0], kd[0], i_dom[0]
+        d1 = H.DecodeDims(*[getattr(dims, f) for f, _ in dims._fields_])
+        d1.n_layers = 1
+        idx_t = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.n_fac), dtype=torch.int32, device="cuda")
+        ws_s = H.sparse_select(d1, q[0], kd0, id0, idx_t)
+        ws_a = H.fac_attend(d1, q[0], k0, v0, idx_t, out[0])
+
+        def step():
+            H.sparse_select(d1, q[0], kd0, id0, idx_t, ws=ws_s)
+            for n in range(cfg.n_layers):
+                H.fac_attend(d1, q[n], k0, v0, idx_t, out[n], ws=ws_a)
+    elif cfg.clsa:
         k0, v0, kd0, id0 = k[0], v[0], kd[0], i_dom[0]
         ws = H.shared_index_decode(dims, q, k0, v0, kd0, id0, out, labels=None)
 
@@ -251,6 +271,22 @@ def main():
     kt = H.timing_collect()
     H.timing_enable(False)
     kernels_ms = {n: t / c for n, (t, c) in kt.items()}
+    layer_ms = None
+    if sequential:
+        # per-layer attention time (events on the launch stream): the first
+        # layer gathers the selected rows from HBM, later layers find them in
+        # the memory-side cache
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(cfg.n_layers + 1)]
+        acc = np.zeros(cfg.n_layers)
+        for _ in range(n_prof):
+            H.sparse_select(d1, q[0], kd0, id0, idx_t, ws=ws_s)
+            evs[0].record()
+            for n in range(cfg.n_layers):
+                H.fac_attend(d1, q[n], k0, v0, idx_t, out[n], ws=ws_a)
+                evs[n + 1].record()
+            torch.cuda.synchronize()
+            acc += [evs[n].elapsed_time(evs[n + 1]) for n in range(cfg.n_layers)]
+        layer_ms = [round(x / n_prof, 5) for x in acc]
 
     # the timed region
     torch.cuda.synchronize()
@@ -265,7 +301,7 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
 
-    ab = algorithmic_bytes(cfg, None if cfg.clsa else labels_np)
+    ab = algorithmic_bytes(cfg, None if cfg.clsa else labels_np, per_layer_gather=sequential)
     tip_ms = kernels_ms["tip_score"]
     tip_gbps = ab["tip"] / (tip_ms * 1e-3) / 1e9
     n_scored = (cfg.batch * cfg.n_kv_heads if cfg.clsa else int(labels_np.sum()) * cfg.batch) * cfg.ctx_len
@@ -289,9 +325,11 @@ def main():
         "config": {"workload": {
             "c1": "single Llama-3-8B-shaped layer, batch 1, ctx 32768, 2 of 8 KV groups retrieval",
             "c2": "single Llama-3-8B-shaped layer, batch 16, ctx 32768, 2 of 8 KV groups retrieval",
-            "c3": "CLSA: 8 layers sharing one KV cache, batch 4, ctx 131072, one shared top-2048 index",
+            "c3": "CLSA: 8 layers sharing one KV cache, batch 4, ctx 131072, one shared top-2048 index" + (
+                  ", selected once then attended layer by layer (9 calls)" if sequential else ""),
             "c4": "32-layer Llama-3-8B-shaped sparse decode step, batch 4, ctx 131072, 64 of 256 (layer, KV "
                   "group) pairs retrieval"}[cfg.name],
+            "clsa_mode": args.clsa_mode if cfg.clsa else None,
             "name": cfg.name, "layers": cfg.n_layers, "batch": cfg.batch, "ctx_len": cfg.ctx_len,
             "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "d_head": cfg.d_head, "n_dom": cfg.n_dom,
             "n_fac": cfg.n_fac, "n_sink": cfg.n_sink, "window": cfg.window},
@@ -305,6 +343,8 @@ def main():
         "measured_copy_GBps": round(copy_gbps, 1),
         "label": label_info,
     }
+    if layer_ms is not None:
+        res["fac_attend_ms_per_layer"] = layer_ms
     if not args.no_cpu_baseline and not cfg.clsa:
         nr, ns = (int(x) for x in args.cpu_sample.split(","))
         log("timing the CPU oracle on a sample of the step")

@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     HAS_F32,
     DecodeDims,
     HasError,
+    fac_attend,
+    fac_attend_workspace,
     aoh_label,
     aoh_label_workspace,
     kdom_pack,
@@ -20,6 +22,8 @@ from .binding import (  # noqa: F401
     shared_index_workspace,
     sparse_decode_step,
     sparse_decode_workspace,
+    sparse_select,
+    sparse_select_workspace,
     status_string,
     timing_collect,
     timing_enable,

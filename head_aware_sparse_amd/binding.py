@@ -61,6 +61,14 @@ def lib():
         L.shared_index_workspace.restype = S
         L.shared_index_decode.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, S, P]
         L.shared_index_decode.restype = I
+        L.sparse_select_workspace.argtypes = [DP]
+        L.sparse_select_workspace.restype = S
+        L.sparse_select.argtypes = [DP, P, P, P, P, P, S, P]
+        L.sparse_select.restype = I
+        L.fac_attend_workspace.argtypes = [DP]
+        L.fac_attend_workspace.restype = S
+        L.fac_attend.argtypes = [DP, P, P, P, P, P, P, S, P]
+        L.fac_attend.restype = I
         L.aoh_label_workspace.argtypes = [I, I, I, I, I]
         L.aoh_label_workspace.restype = S
         L.aoh_label.argtypes = [I, I, I, I, I, I, P, P, I, ctypes.c_float, P, P, P, P, S, P]
@@ -128,6 +136,14 @@ def shared_index_workspace(dims):
     return int(lib().shared_index_workspace(ctypes.byref(dims)))
 
 
+def sparse_select_workspace(dims):
+    return int(lib().sparse_select_workspace(ctypes.byref(dims)))
+
+
+def fac_attend_workspace(dims):
+    return int(lib().fac_attend_workspace(ctypes.byref(dims)))
+
+
 def aoh_label_workspace(n_layers, n_q_heads, n_kv_heads, d_model, d_head):
     return int(lib().aoh_label_workspace(n_layers, n_q_heads, n_kv_heads, d_model, d_head))
 
@@ -192,6 +208,37 @@ def shared_index_decode(dims, q, k_cache, v_cache, k_dom, i_dom, out, q_index=No
     _check(lib().shared_index_decode(ctypes.byref(dims), _ptr(q), _ptr(q_index), _ptr(k_cache), _ptr(v_cache),
                                      _ptr(k_dom), _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _ptr(ws),
                                      ws.numel(), _stream(stream)))
+    return ws
+
+
+def sparse_select(dims, q_index, k_dom, i_dom, idx_out, ws=None, stream=None):
+    import torch
+    B, Hq, Hkv, T, d = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.ctx_len, dims.d_head
+    dt = _kv_torch_dtype(dims)
+    _dev(q_index, "q_index", dt, (B, Hq, d))
+    _dev(k_dom, "k_dom", dt, (B, Hkv, T, kdom_row_elems(dims)))
+    _dev(i_dom, "i_dom", torch.int32, (Hkv, dims.n_dom))
+    _dev(idx_out, "idx_out", torch.int32, (B, Hkv, dims.n_fac))
+    nbytes = sparse_select_workspace(dims)
+    ws = _workspace(nbytes, ws, q_index)
+    _check(lib().sparse_select(ctypes.byref(dims), _ptr(q_index), _ptr(k_dom), _ptr(i_dom), _ptr(idx_out),
+                               _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def fac_attend(dims, q, k_cache, v_cache, idx, out, ws=None, stream=None):
+    import torch
+    B, Hq, Hkv, T, d = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.ctx_len, dims.d_head
+    dt = _kv_torch_dtype(dims)
+    _dev(q, "q", dt, (B, Hq, d))
+    _dev(k_cache, "k_cache", dt, (B, Hkv, T, d))
+    _dev(v_cache, "v_cache", dt, (B, Hkv, T, d))
+    _dev(idx, "idx", torch.int32, (B, Hkv, dims.n_fac))
+    _dev(out, "out", torch.float32, (B, Hq, d))
+    nbytes = fac_attend_workspace(dims)
+    ws = _workspace(nbytes, ws, q)
+    _check(lib().fac_attend(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), _ptr(out),
+                            _ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
 

@@ -58,8 +58,10 @@ int kdom_elems(int n_dom, int dt) {
   return vecs * 16 / esize(dt);
 }
 
-// Validates a decode shape.  clsa selects the shared-index limits.
-has_status check_dims(const has_decode_dims* d, bool clsa) {
+// Validates a decode shape.  clsa selects the shared-index limits; a call
+// that ignores the streaming (n_sink, window) or dominant-chunk (n_dom,
+// rope_layout) fields says so and they are not checked.
+has_status check_dims(const has_decode_dims* d, bool clsa, bool uses_stream = true, bool uses_dom = true) {
   if (!d) return fail(HAS_ERR_INVALID_ARG, "dims is NULL");
   if (d->n_layers < 1 || d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
     return fail(HAS_ERR_INVALID_ARG, "n_layers, batch, n_q_heads and n_kv_heads must be >= 1");
@@ -76,13 +78,17 @@ has_status check_dims(const has_decode_dims* d, bool clsa) {
     return fail(HAS_ERR_UNSUPPORTED, "ctx_len %d above %d", d->ctx_len, has::kMaxTipChunks * 4096);
   if (d->n_fac < 1 || d->n_fac > d->ctx_len)
     return fail(HAS_ERR_INVALID_ARG, "n_fac %d outside [1, ctx_len=%d]", d->n_fac, d->ctx_len);
-  if (d->n_sink < 0 || d->window < 0) return fail(HAS_ERR_INVALID_ARG, "n_sink and window must be >= 0");
-  if ((long long)d->n_sink + d->window < 1) return fail(HAS_ERR_INVALID_ARG, "n_sink + window must be >= 1");
-  if (d->n_dom < 1 || d->n_dom > d->d_head / 2)
-    return fail(HAS_ERR_INVALID_ARG, "n_dom %d outside [1, d_head/2]", d->n_dom);
+  if (uses_stream) {
+    if (d->n_sink < 0 || d->window < 0) return fail(HAS_ERR_INVALID_ARG, "n_sink and window must be >= 0");
+    if ((long long)d->n_sink + d->window < 1) return fail(HAS_ERR_INVALID_ARG, "n_sink + window must be >= 1");
+  }
+  if (uses_dom) {
+    if (d->n_dom < 1 || d->n_dom > d->d_head / 2)
+      return fail(HAS_ERR_INVALID_ARG, "n_dom %d outside [1, d_head/2]", d->n_dom);
+    if (d->rope_layout != HAS_ROPE_ROTATE_HALF && d->rope_layout != HAS_ROPE_INTERLEAVED)
+      return fail(HAS_ERR_INVALID_ARG, "bad rope_layout");
+  }
   if (d->kv_dtype != HAS_F32 && d->kv_dtype != HAS_BF16) return fail(HAS_ERR_INVALID_ARG, "bad kv_dtype");
-  if (d->rope_layout != HAS_ROPE_ROTATE_HALF && d->rope_layout != HAS_ROPE_INTERLEAVED)
-    return fail(HAS_ERR_INVALID_ARG, "bad rope_layout");
   if ((long long)d->n_layers * d->n_kv_heads > has::kMaxPairs)
     return fail(HAS_ERR_UNSUPPORTED, "n_layers * n_kv_heads above %d", has::kMaxPairs);
   (void)clsa;
@@ -122,7 +128,9 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   while ((g.T + g.ct - 1) / g.ct > has::kMaxTipChunks && g.ct < 4096) g.ct *= 2;
   g.nch_t = (g.T + g.ct - 1) / g.ct;
   g.Ts = (g.T + 63) / 64 * 64;
-  g.clsa_mfma = clsa && g.bf16 && g.d == 128 && g.Lq * g.G <= 32;
+  // the matrix cores pay off once several layers' queries share each
+  // gathered row; a single layer's G heads go faster on the vector ALUs
+  g.clsa_mfma = clsa && g.bf16 && g.d == 128 && g.Lq >= 2 && g.Lq * g.G <= 32;
   g.cf = g.clsa_mfma ? has::kClsaRows : clampi(pow2_floor((long long)g.n_fac * n_att / 2048), 128, has::kMaxChunkRows);
   g.nch_f = (g.n_fac + g.cf - 1) / g.cf;
   g.s_end = g.n_sink < g.T ? g.n_sink : g.T;
@@ -269,6 +277,39 @@ has_status debug_check_arrays(const has_decode_dims* d, int pairs, const int32_t
   }
   for (size_t i = 0; i < lab.size(); ++i)
     if (lab[i] > 1) return fail(HAS_ERR_INVALID_ARG, "labels[%zu] = %d is neither 0 nor 1", i, (int)lab[i]);
+  return HAS_OK;
+}
+
+// One-layer shapes for sparse_select / fac_attend: fields the call does not
+// use are replaced by valid placeholders before the layout is built.
+has_status one_layer_dims(const has_decode_dims* dims, bool uses_dom, has_decode_dims& out) {
+  has_status s = check_dims(dims, true, false, uses_dom);
+  if (s != HAS_OK) return s;
+  if (dims->n_layers != 1) return fail(HAS_ERR_INVALID_ARG, "n_layers must be 1 (got %d)", dims->n_layers);
+  out = *dims;
+  out.n_sink = 1;
+  out.window = 0;
+  if (!uses_dom) {
+    out.n_dom = 1;
+    out.rope_layout = HAS_ROPE_ROTATE_HALF;
+  }
+  return HAS_OK;
+}
+
+// Workspace of fac_attend: the chunk partials only.
+size_t fac_attend_bytes(const Layout& L) {
+  const has::Geo& g = L.g;
+  return align_up((size_t)g.Lq * g.Hkv * g.B * g.nparts * g.G * (g.d + 4) * 4, 256);
+}
+
+has_status debug_check_idx(const has_decode_dims* d, const int32_t* idx, void* stream) {
+  std::vector<int32_t> h((size_t)d->batch * d->n_kv_heads * d->n_fac);
+  hipError_t e = hipMemcpyAsync(h.data(), idx, h.size() * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "HAS_DEBUG copy");
+  for (size_t i = 0; i < h.size(); ++i)
+    if (h[i] < 0 || h[i] >= d->ctx_len)
+      return fail(HAS_ERR_INVALID_ARG, "idx[%zu] = %d outside [0, %d)", i, h[i], d->ctx_len);
   return HAS_OK;
 }
 
@@ -467,6 +508,87 @@ has_status shared_index_decode(const has_decode_dims* dims, const void* q, const
                                void* stream) {
   return run_decode(dims, true, q, q_index, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out, ws, ws_bytes,
                     stream);
+}
+
+size_t sparse_select_workspace(const has_decode_dims* dims) {
+  has_decode_dims d1;
+  if (one_layer_dims(dims, true, d1) != HAS_OK) return 0;
+  return make_layout(&d1, true).bytes;
+}
+
+has_status sparse_select(const has_decode_dims* dims, const void* q_index, const void* k_dom,
+                         const int32_t* i_dom, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  has_decode_dims d1;
+  has_status s = one_layer_dims(dims, true, d1);
+  if (s != HAS_OK) return s;
+  REQUIRE_PTR(q_index, "q_index");
+  REQUIRE_PTR(k_dom, "k_dom");
+  REQUIRE_PTR(i_dom, "i_dom");
+  REQUIRE_PTR(idx_out, "idx_out");
+  Layout L = make_layout(&d1, true);
+  if (!ws) return fail(HAS_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned16(ws)) return fail(HAS_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  if (ws_bytes < L.bytes) return fail(HAS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, L.bytes);
+  carve(L, ws);
+  has::Geo& g = L.g;
+  g.q = q_index;
+  g.q_index = q_index;
+  g.kdom = k_dom;
+  g.i_dom = i_dom;
+  g.host_plan = g.prefilter;
+  g.idx_out = idx_out;
+  g.select_only = 1;
+  if (debug_checks()) {
+    s = debug_check_arrays(&d1, d1.n_kv_heads, i_dom, nullptr, 0, stream);
+    if (s != HAS_OK) return s;
+  }
+  s = persistent_grid(g.grid);
+  if (s != HAS_OK) return s;
+  // no streaming groups: the side stream is never used
+  const hipError_t e = has::launch_decode(g, has::StreamSet{(hipStream_t)stream, nullptr, nullptr, nullptr});
+  if (e != hipSuccess) return hip_fail(e, "sparse_select launch");
+  return ok();
+}
+
+size_t fac_attend_workspace(const has_decode_dims* dims) {
+  has_decode_dims d1;
+  if (one_layer_dims(dims, false, d1) != HAS_OK) return 0;
+  return fac_attend_bytes(make_layout(&d1, true));
+}
+
+has_status fac_attend(const has_decode_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* idx, float* out, void* ws, size_t ws_bytes, void* stream) {
+  has_decode_dims d1;
+  has_status s = one_layer_dims(dims, false, d1);
+  if (s != HAS_OK) return s;
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k_cache, "k_cache");
+  REQUIRE_PTR(v_cache, "v_cache");
+  REQUIRE_PTR(idx, "idx");
+  REQUIRE_PTR(out, "out");
+  Layout L = make_layout(&d1, true);
+  const size_t need = fac_attend_bytes(L);
+  if (!ws) return fail(HAS_ERR_WORKSPACE, "ws is NULL");
+  if (!aligned16(ws)) return fail(HAS_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  if (ws_bytes < need) return fail(HAS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, need);
+  has::Geo& g = L.g;
+  g.part = (float*)ws;
+  g.q = q;
+  g.k = k_cache;
+  g.v = v_cache;
+  g.idx = const_cast<int32_t*>(idx);  // read only: the attention kernels never write it
+  g.idx_bmajor = 1;
+  g.host_plan = 1;  // one layer, all groups retrieval
+  g.out = out;
+  if (debug_checks()) {
+    s = debug_check_idx(&d1, idx, stream);
+    if (s != HAS_OK) return s;
+  }
+  s = persistent_grid(g.grid);
+  if (s != HAS_OK) return s;
+  const hipError_t e = has::launch_fac_attend(g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fac_attend launch");
+  return ok();
 }
 
 size_t aoh_label_workspace(int n_layers, int n_q_heads, int n_kv_heads, int d_model, int d_head) {

@@ -1177,7 +1177,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
     __syncthreads();
     int nrows;
     if (fac) {
-      const int iitem = g.clsa ? gi * g.B + b : pa * g.B + b;
+      const int iitem = g.idx_bmajor ? b * g.Hkv + gi : (g.clsa ? gi * g.B + b : pa * g.B + b);
       const int32_t* ix = g.idx + (size_t)iitem * g.n_fac + (size_t)chunk * g.cf;
       nrows = min(g.cf, g.n_fac - chunk * g.cf);
       // indices come from select_c and are always in [0, T); the clamp only
@@ -1343,7 +1343,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
 
 // ------------------------------------------------------------------ CLSA attention
 // Shared-index retrieval attention on the matrix cores.  With one index per
-// (sequence, group) the N layers' G query heads -- QV = N*G <= 32 query
+// (sequence, group) the N >= 2 layers' G query heads -- QV = N*G <= 32 query
 // vectors -- all attend to the same gathered rows, a dense contraction:
 //   S[qv][row] = Q[qv][:] . K[row][:]       (bf16 MFMA 32x32x16, fp32 sums)
 //   P = softmax over the unit's rows per qv (fp32, in LDS)
@@ -1387,7 +1387,8 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
     const int chunk = j % g.nch_f;
     const int r2 = j / g.nch_f;
     const int b = r2 % g.B, gi = r2 / g.B;
-    const int32_t* ix = g.idx + ((size_t)gi * g.B + b) * g.n_fac + (size_t)chunk * g.cf;
+    const size_t iitem = g.idx_bmajor ? (size_t)b * g.Hkv + gi : (size_t)gi * g.B + b;
+    const int32_t* ix = g.idx + iitem * g.n_fac + (size_t)chunk * g.cf;
     const int nrows = min(g.cf, g.n_fac - chunk * g.cf);
     const size_t kvs = (size_t)b * g.Hkv + gi;
     const uint16_t* kb = (const uint16_t*)g.k + kvs * (size_t)g.T * D;
@@ -1749,6 +1750,7 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  if (g.select_only) return hipSuccess;
   {
     // mode 1: retrieval units only; mode 0: retrieval and streaming units
     const bool with_stream = any_stream && !side;
@@ -1769,6 +1771,30 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   }
   if (e != hipSuccess) return e;
   if (side && (e = hipStreamWaitEvent(s, ss.join, 0)) != hipSuccess) return e;
+  const long long n_out = n_att_items * g.G * g.d;
+  {
+    KTimer t("merge", s);
+    merge_kernel<<<clampi((n_out + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
+  }
+  return hipGetLastError();
+}
+
+// FAC attention of one layer over a caller's index (batch-major), then the
+// merge of the chunk partials.
+hipError_t launch_fac_attend(const Geo& g0, hipStream_t s) {
+  Geo g = g0;
+  g.attn_mode = 1;
+  const long long n_att_items = (long long)g.Hkv * g.B;
+  {
+    KTimer t("attention_fac", s);
+    if (g.clsa_mfma) {
+      attn_clsa_mfma_kernel<<<clampi(n_att_items * g.nch_f, 1, g.grid), NT, 0, s>>>(g);
+    } else {
+      const hipError_t e = launch_attn(g, clampi(n_att_items * g.nch_f, 1, g.grid), s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const long long n_out = n_att_items * g.G * g.d;
   {
     KTimer t("merge", s);

@@ -24,7 +24,7 @@ struct Geo {
   int R;            // k_dom row elements
   int bf16;         // kv dtype
   int clsa;         // 1: one index per (b, g) shared by Lq layers over one cache
-  int clsa_mfma;    // shared-index retrieval attention on the matrix cores (bf16, d 128, Lq*G <= 32)
+  int clsa_mfma;    // shared-index retrieval attention on the matrix cores (bf16, d 128, 2 <= Lq, Lq*G <= 32)
   int interleaved;  // rope pairing
   int host_plan;    // shared-index mode, no labels, prefiltered: the plan is implicit (no plan launch)
   // chunking
@@ -40,6 +40,8 @@ struct Geo {
   int bm_words;     // words of the per-item token bitmap (T / 32 rounded up)
   int grid;         // persistent grid size
   int attn_mode;    // attention launch: 1 = retrieval (FAC) units, 2 = streaming units
+  int select_only;  // stop after the selection (sparse_select)
+  int idx_bmajor;   // FAC reads a caller's index laid out [B][Hkv][n_fac] (fac_attend)
   // workspace
   int* plan;         // [4 + 3*kMaxPairs]: n_idx_pairs, n_att_ret, n_att_str, -, lists
   uint32_t* hist;    // [idx items][kHistBins]
@@ -90,5 +92,6 @@ struct StreamSet {
 
 hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s);
 hipError_t launch_decode(const Geo& g, const StreamSet& ss);
+hipError_t launch_fac_attend(const Geo& g, hipStream_t s);
 
 }  // namespace has

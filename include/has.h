@@ -181,6 +181,35 @@ has_status shared_index_decode(const has_decode_dims* dims, const void* q, const
                                const int32_t* i_dom, const uint8_t* labels, float* out,
                                int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
+/* sparse_select: the index alone -- the TIP scores and exact top-n_fac of
+ * sparse_decode_step's retrieval branch ([FASA] §2.B.1) -- for one layer
+ * over one cache, so that it can serve several fac_attend calls ([CLSA]
+ * "Cómo funciona CLSA": the index is computed once and later layers attend
+ * over it).  dims->n_layers must be 1; n_sink and window are not used.
+ * q_index [batch,n_q_heads,d_head]; k_dom [batch,n_kv_heads,ctx_len,
+ * kdom_row_elems] (kdom_pack with n_layers = 1); i_dom [n_kv_heads,n_dom];
+ * idx_out [batch,n_kv_heads,n_fac] int32 (required) receives each group's
+ * selection, ascending, ties to the lower token. */
+size_t sparse_select_workspace(const has_decode_dims* dims);
+has_status sparse_select(const has_decode_dims* dims, const void* q_index, const void* k_dom,
+                         const int32_t* i_dom, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* fac_attend: FAC attention of one layer over a given index ([FASA] §2.B.2):
+ *   out[b,h] = sum over the n_fac entries t of idx[b,g] of
+ *              softmax_t(q[b,h].k_t / sqrt(d_head)) v_t,     g = h / G,
+ * with full d_head rows of one cache; an entry repeated r times contributes
+ * its row r times.  One sparse_select followed by one fac_attend per layer,
+ * each with that layer's q, is the layer-by-layer form of the shared index
+ * ([CLSA]).  dims->n_layers must be 1; n_sink, window, n_dom and
+ * rope_layout are not used.  q [batch,n_q_heads,d_head] (kv_dtype); k_cache,
+ * v_cache [batch,n_kv_heads,ctx_len,d_head]; idx [batch,n_kv_heads,n_fac]
+ * int32 with entries in [0, ctx_len): an entry outside is clamped into that
+ * range, so no read leaves the cache (with HAS_DEBUG=1 it is rejected
+ * instead); out [batch,n_q_heads,d_head] f32. */
+size_t fac_attend_workspace(const has_decode_dims* dims);
+has_status fac_attend(const has_decode_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* idx, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------- diagnostics --
  * Per-kernel device time.  While enabled (process-wide), every kernel the
  * library launches is bracketed by HIP events recorded on the caller's

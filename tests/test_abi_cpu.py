@@ -104,3 +104,41 @@ def test_status_strings_and_row_elems():
     assert H.kdom_row_elems(_dims(n_dom=12)) == 32   # 24 bf16 -> padded to 4 vectors
     assert H.kdom_row_elems(_dims(n_dom=1)) == 8
     assert H.kdom_row_elems(_dims(n_dom=8, kv_dtype=H.HAS_F32)) == 16
+
+
+def test_select_and_attend_argument_checks():
+    """sparse_select / fac_attend take one layer; fields they do not use are
+    not validated (fac_attend ignores n_sink, window, n_dom, rope_layout)."""
+    P = ctypes.c_void_p
+    L = lib()
+
+    def select(d, ws=FAKE, ws_bytes=1 << 40, **o):
+        p = dict(qi=FAKE, kd=FAKE, idom=FAKE, idx=FAKE)
+        p.update(o)
+        return L.sparse_select(ctypes.byref(d), P(p["qi"]), P(p["kd"]), P(p["idom"]), P(p["idx"]),
+                               P(ws) if ws else None, ws_bytes, None)
+
+    def attend(d, ws=FAKE, ws_bytes=1 << 40, **o):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, idx=FAKE, out=FAKE)
+        p.update(o)
+        return L.fac_attend(ctypes.byref(d), P(p["q"]), P(p["k"]), P(p["v"]), P(p["idx"]), P(p["out"]),
+                            P(ws) if ws else None, ws_bytes, None)
+
+    d = _dims()
+    assert select(_dims(n_layers=2)) == 1 and "n_layers" in H.last_error()
+    assert attend(_dims(n_layers=2)) == 1
+    assert select(d, idx=None) == 1 and "idx_out" in H.last_error()
+    assert attend(d, idx=None) == 1
+    assert attend(d, q=FAKE + 4) == 1 and "aligned" in H.last_error()
+    assert select(_dims(n_dom=0)) == 1
+    assert select(d, ws=None) == 3
+    # unused fields: not validated, the call gets as far as the workspace check
+    assert select(_dims(n_sink=0, window=0), ws=None) == 3
+    assert attend(_dims(n_sink=0, window=0, n_dom=0, rope_layout=7), ws=None) == 3
+    need_s, need_a = H.sparse_select_workspace(d), H.fac_attend_workspace(d)
+    assert need_s > 0 and need_a > 0
+    assert select(d, ws_bytes=need_s - 1) == 3
+    assert attend(d, ws_bytes=need_a - 1) == 3
+    assert H.fac_attend_workspace(_dims(n_layers=2)) == 0
+    # the attention-only workspace holds the chunk partials alone
+    assert need_a < need_s

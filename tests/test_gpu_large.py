@@ -97,7 +97,7 @@ def test_c4_32_layers_128k_sampled():
 ], ids=["f32", "d64", "48qv", "ragged-mfma"])
 def test_clsa_attention_paths(over):
     """Shared-index mode on both attention paths (matrix cores for bf16,
-    d 128, N*G <= 32; vector ALUs otherwise), with one layer treating a group
+    d 128, 2 <= N, N*G <= 32; vector ALUs otherwise), with one layer treating a group
     as streaming."""
     cfg = R.get_config("c3", ctx_len=9000, batch=2, **{"n_fac": 700, **over})
     print(f"case clsa paths {over}", flush=True)
