@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--clsa-mode", default="fused", choices=["fused", "sequential"],
                     help="shared-index workload: one fused call, or one sparse_select plus one fac_attend per layer")
+    ap.add_argument("--ctx-len", type=int, default=None, help="override the workload's context length")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-label", action="store_true")
     ap.add_argument("--cpu-sample", default="24,72", help="retrieval,streaming items timed on the CPU")
@@ -150,7 +152,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    cfg = R.get_config(args.config)
+    over = {k: v for k, v in (("ctx_len", args.ctx_len), ("batch", args.batch)) if v is not None}
+    cfg = R.get_config(args.config, **over)
     log(f"config {cfg}")
     t0 = time.time()
     hi = R.HostInputs(cfg, with_weights=(cfg.d_model > 0 and not args.no_label))
@@ -323,12 +326,12 @@ def main():
         "dtype": "bf16" if cfg.bf16 else "f32",
         "data": "synthetic (seeded Philox4x32-10 inputs shaped like the pages' workloads)",
         "config": {"workload": {
-            "c1": "single Llama-3-8B-shaped layer, batch 1, ctx 32768, 2 of 8 KV groups retrieval",
-            "c2": "single Llama-3-8B-shaped layer, batch 16, ctx 32768, 2 of 8 KV groups retrieval",
-            "c3": "CLSA: 8 layers sharing one KV cache, batch 4, ctx 131072, one shared top-2048 index" + (
-                  ", selected once then attended layer by layer (9 calls)" if sequential else ""),
-            "c4": "32-layer Llama-3-8B-shaped sparse decode step, batch 4, ctx 131072, 64 of 256 (layer, KV "
-                  "group) pairs retrieval"}[cfg.name],
+            "c1": f"single Llama-3-8B-shaped layer, batch {cfg.batch}, ctx {cfg.ctx_len}, 2 of 8 KV groups retrieval",
+            "c2": f"single Llama-3-8B-shaped layer, batch {cfg.batch}, ctx {cfg.ctx_len}, 2 of 8 KV groups retrieval",
+            "c3": f"CLSA: 8 layers sharing one KV cache, batch {cfg.batch}, ctx {cfg.ctx_len}, one shared top-2048 "
+                  "index" + (", selected once then attended layer by layer (9 calls)" if sequential else ""),
+            "c4": f"32-layer Llama-3-8B-shaped sparse decode step, batch {cfg.batch}, ctx {cfg.ctx_len}, 64 of 256 "
+                  "(layer, KV group) pairs retrieval"}[cfg.name],
             "clsa_mode": args.clsa_mode if cfg.clsa else None,
             "name": cfg.name, "layers": cfg.n_layers, "batch": cfg.batch, "ctx_len": cfg.ctx_len,
             "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "d_head": cfg.d_head, "n_dom": cfg.n_dom,

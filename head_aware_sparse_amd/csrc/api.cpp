@@ -98,7 +98,7 @@ has_status check_dims(const has_decode_dims* d, bool clsa, bool uses_stream = tr
 struct Layout {
   has::Geo g;
   size_t off_plan, off_hist, off_info, off_cand, off_ngt, off_off, off_thr, off_scores, off_idx, off_part, off_skeys, off_tau,
-      off_bm, off_qbar;
+      off_qbar;
   size_t bytes;
 };
 
@@ -175,7 +175,6 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   L.off_part = take((size_t)n_att * g.nparts * g.G * (g.d + 4) * 4);
   L.off_skeys = take((size_t)n_idx * has::kSampleTokens * 4);
   L.off_tau = take((size_t)n_idx * 8);
-  L.off_bm = take((size_t)n_idx * g.bm_words * 4);
   L.off_qbar = take((size_t)n_idx * g.R * 4);
   L.bytes = o;
   return L;
@@ -196,7 +195,6 @@ void carve(Layout& L, void* ws) {
   g.part = (float*)(b + L.off_part);
   g.skeys = (uint32_t*)(b + L.off_skeys);
   g.tau = (uint2*)(b + L.off_tau);
-  g.bitmap = (uint32_t*)(b + L.off_bm);
   g.qbar = (float*)(b + L.off_qbar);
 }
 

@@ -310,6 +310,19 @@ __device__ __forceinline__ uint32_t wave_reduce_u(uint32_t x, Op op) {
   const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return op(r32[0], r32[1]);
 }
+// Inclusive prefix sum over the 64 lanes with DPP only: shifts by 1, 2, 4
+// and 8 within each 16-lane row (lanes shifted in from outside the row add
+// 0), then lane 15 of each row is added to the next row and lane 31 to rows
+// 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan_u(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
 __device__ __forceinline__ uint32_t wave_min_u(uint32_t x) {
   return wave_reduce_u(x, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
@@ -865,38 +878,41 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
 // final: per index item, the exact top-n_fac among the candidates (key >=
 // tau) held in LDS.  While the candidates load, they are counted in 2048
 // bins of (key - tau) >> sh, sh sized so the largest sampled key falls in the
-// top bin (larger keys are clamped into it).  When the bin holding the
-// n_fac-th candidate is not the clamped top bin and has at most kRankMax
-// members, one pass marks every candidate above it and lists its members,
-// and the members are ranked directly; otherwise the general radix threshold
-// decides.  If the candidates are fewer than n_fac or overflowed, the item
-// is rescored in full here and selected from its score row (exact either
-// way).  The selected tokens are marked in an LDS bitmap; a token's output
-// slot is the number of marked tokens before it, from per-word prefix
-// counts, which emits the selection in ascending order.
+// top bin (larger keys are clamped into it).  The cut (key*, token*) -- the
+// n_fac-th candidate in the order (key desc, token asc) -- comes from ranking
+// the members of the bin that holds it when that bin is not the clamped top
+// bin and has at most kRankMax members, else from the general radix
+// threshold.  The selected tokens are then compacted to the front of the
+// candidate buffer, marked in a token bitmap built in the rest of it, and
+// each is written to the slot given by the number of marked tokens before
+// it (per-word prefix counts), which emits the selection in ascending order.
+// If the candidates are fewer than n_fac or overflowed, the item is rescored
+// in full here and selected from its score row (exact either way).
 template <typename E>
 __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
-  __shared__ uint2 s_c[kCandFast];
-  __shared__ __attribute__((aligned(16))) uint32_t s_bm[kPrefilterMaxT / 32];
+  // candidates; later the selected tokens, the bitmap and the prefix counts
+  __shared__ __attribute__((aligned(16))) uint2 s_c[kCandFast];
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ float s_q[kMaxR];
   __shared__ int s_w[NWAVE];
   __shared__ uint32_t s_res[2];
   __shared__ uint2 s_list[kRankMax];
   __shared__ int s_m;
-  static_assert(kHistBins * sizeof(uint32_t) >= (kPrefilterMaxT / 32) * sizeof(uint16_t), "u16 prefix alias");
-  static_assert(kCandFast * sizeof(uint2) >= (kPrefilterMaxT / 32) * sizeof(uint32_t), "u32 prefix alias");
+  // bitmap words per thread for the prefix counts: a multiple of 4 (16-byte
+  // reads), so the bitmap spans NT * per words
+  const int per = ((g.bm_words + NT - 1) / NT + 3) & ~3;
+  constexpr int kSelWords = (kCandFast / 3 + 63) / 64 * 64;  // n_fac <= kCandFast / 3 on this path
+  constexpr int kPerMax = (kPrefilterMaxT / 32 / NT + 3) & ~3;
+  static_assert(kCandFast * sizeof(uint2) >= (kSelWords + NT * kPerMax) * sizeof(uint32_t) +
+                                                 NT * kPerMax * sizeof(uint16_t),
+                "selected tokens, bitmap and u16 prefixes fit the candidate buffer");
   static_assert(kCandFast / 3 < 65536, "prefiltered n_fac fits u16 prefixes");
   const int tid = threadIdx.x;
   const int n_items = n_idx_pairs(g) * g.B;
-  // bitmap words per thread for the prefix counts: a multiple of 4 (16-byte
-  // reads); NT * per <= kPrefilterMaxT / 32 as bm_words <= that
-  const int per = ((g.bm_words + NT - 1) / NT + 3) & ~3;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     __syncthreads();
     const uint32_t count = g.info[(size_t)item * 4 + 2];
     const uint2 th = g.tau[item];
-    for (int w = tid; w < NT * per; w += NT) s_bm[w] = 0u;
     for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
     if (tid == 0) s_m = 0;
     const int pidx = item / g.B, b = item - pidx * g.B;
@@ -904,37 +920,54 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
     const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
     int32_t* ix = g.idx + (size_t)item * g.n_fac;
     int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
-    auto mark = [&](uint32_t t) { atomicOr(&s_bm[t >> 5], 1u << (t & 31)); };
-    // writes every marked element of src to its slot; s_pre holds the
-    // per-word prefix counts (in LDS no longer needed)
-    auto emit = [&](const auto& src, auto* s_pre) {
-      const uint4* q4 = reinterpret_cast<const uint4*>(s_bm + tid * per);
-      int cnt = 0;
-      for (int v = 0; v < per / 4; ++v) {
-        const uint4 x = q4[v];
-        cnt += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
-      }
-      int tot;
-      uint32_t run = (uint32_t)block_excl_scan(cnt, s_w, tot);
-      for (int w = tid * per; w < (tid + 1) * per; ++w) {
-        s_pre[w] = run;  // < n_fac, which fits the prefix type
-        run += __popc(s_bm[w]);
-      }
+    // bitmap of NT * per words at bm, u16 prefix counts after it
+    auto clear_bitmap = [&](uint32_t* bm) {
+      for (int w = tid; w < NT * per; w += NT) bm[w] = 0u;
+    };
+    // exclusive prefix counts of the set bits, one u16 per bitmap word
+    // (< n_fac < 2^16).  Each wave scans a contiguous quarter of the bitmap,
+    // lane i on word i of each 64-word tile, so LDS accesses are
+    // conflict-free; a first pass sums the quarters for the wave offsets.
+    auto prefix = [&](const uint32_t* bm, uint16_t* pre) {
+      const int lane = tid & 63, wave = tid >> 6;
+      const int qw = NT * per / NWAVE;  // a multiple of 64 (per is a multiple of 4)
+      const uint32_t* wb = bm + wave * qw;
+      uint16_t* wp = pre + wave * qw;
+      uint32_t tot = 0;
+      for (int k = lane; k < qw; k += 64) tot += __popc(wb[k]);
+      tot = wave_reduce_u(tot, [](uint32_t x, uint32_t y) { return x + y; });
+      if (lane == 0) s_w[wave] = (int)tot;
       __syncthreads();
-      src.for_each([&](uint32_t, uint32_t t) {
-        const uint32_t word = s_bm[t >> 5], bit = 1u << (t & 31);
-        if (word & bit) {
-          const uint32_t pos = s_pre[t >> 5] + __popc(word & (bit - 1u));
-          ix[pos] = (int32_t)t;
-          if (ox) ox[pos] = (int32_t)t;
-        }
-      });
+      uint32_t carry = 0;
+      for (int w = 0; w < wave; ++w) carry += (uint32_t)s_w[w];
+      for (int k0 = 0; k0 < qw; k0 += 64) {
+        const uint32_t x = __popc(wb[k0 + lane]);
+        const uint32_t inc = wave_incl_scan_u(x);
+        wp[k0 + lane] = (uint16_t)(carry + inc - x);
+        carry += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      }
+    };
+    auto put = [&](const uint32_t* bm, const uint16_t* pre, uint32_t t) {
+      const uint32_t word = bm[t >> 5], bit = 1u << (t & 31);
+      const uint32_t pos = pre[t >> 5] + __popc(word & (bit - 1u));
+      if (pos < (uint32_t)g.n_fac) {  // always, with exactly n_fac marked
+        ix[pos] = (int32_t)t;
+        if (ox) ox[pos] = (int32_t)t;
+      }
     };
     if (count >= (uint32_t)g.n_fac && count <= (uint32_t)g.cand_cap) {
       const uint32_t tau = th.x;
       const uint32_t span = th.y > tau ? th.y - tau : 0u;
       const int bits = span ? 32 - __clz(span) : 0;
       const int sh = bits > 11 ? bits - 11 : 0;
+      // direct: the bitmap and its prefix counts fit after the candidates,
+      // and tokens are marked while the threshold is found; else the
+      // selected tokens are compacted first and the bitmap built behind them
+      const int cand_words = ((int)count * 2 + 3) & ~3;
+      const bool direct = (size_t)(cand_words + NT * per) * 4 + (size_t)NT * per * 2 <= sizeof(s_c);
+      uint32_t* bm = reinterpret_cast<uint32_t*>(s_c) + (direct ? cand_words : kSelWords);
+      uint16_t* pre = reinterpret_cast<uint16_t*>(bm + NT * per);
+      if (direct) clear_bitmap(bm);
       __syncthreads();
       // candidates -> LDS, two per 16-byte load, eight loads in flight,
       // counted by their first digit on the way
@@ -959,21 +992,27 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
       }
       __syncthreads();
       const LdsPairs src{s_c, (int)count};
+      auto mark = [&](uint32_t t) { atomicOr(&bm[t >> 5], 1u << (t & 31)); };
       int bin;
       uint32_t above;
       find_bin_top(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, bin, above);
       const uint32_t members = s_hist[bin];
       __syncthreads();
+      uint32_t kstar = 0, tstar = 0;
       if (bin < kHistBins - 1 && members <= (uint32_t)kRankMax) {
+        // every candidate in a higher bin has a larger key; within the bin a
+        // member is selected when fewer than need members precede it in
+        // (key desc, token asc), and the cut is the one preceded by need - 1
         const uint32_t ub = (uint32_t)bin;
         src.for_each([&](uint32_t k, uint32_t t) {
           const uint32_t d = min((k - tau) >> sh, (uint32_t)kHistBins - 1u);
-          if (d > ub) mark(t);
-          else if (d == ub) s_list[atomicAdd(&s_m, 1)] = make_uint2(k, t);
+          if (d > ub) {
+            if (direct) mark(t);
+          } else if (d == ub) {
+            s_list[atomicAdd(&s_m, 1)] = make_uint2(k, t);
+          }
         });
         __syncthreads();
-        // a member is selected when fewer than need members precede it in
-        // the order (key desc, token asc)
         const uint32_t need = (uint32_t)g.n_fac - above;
         const int m = s_m;
         for (int i = tid; i < m; i += NT) {
@@ -984,18 +1023,61 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
             const uint2 o = s_list[j];
             r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
           }
-          if (r < need) mark(me.y);
+          if (direct && r < need) mark(me.y);
+          if (r == need - 1) {
+            s_res[0] = me.x;
+            s_res[1] = me.y;
+          }
         }
+        __syncthreads();
+        kstar = s_res[0];
+        tstar = s_res[1];
       } else {
-        uint32_t kstar, tstar;
         exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
-        src.for_each([&](uint32_t k, uint32_t t) {
-          if (k > kstar || (k == kstar && t <= tstar)) mark(t);
-        });
+        if (direct)
+          src.for_each([&](uint32_t k, uint32_t t) {
+            if (k > kstar || (k == kstar && t <= tstar)) mark(t);
+          });
+      }
+      uint32_t* s_sel = reinterpret_cast<uint32_t*>(s_c);
+      int n_sel = 0;
+      if (!direct) {
+        // compact the selected tokens (n_fac of them) to the front of the
+        // buffer as u32.  Per chunk, every read precedes every write; a
+        // write lands below 4 bytes x (candidates read so far), under the
+        // next chunk's first read at 8 bytes x that.
+        __syncthreads();
+        if (tid == 0) s_m = 0;
+        __syncthreads();
+        for (int c0 = 0; c0 < (int)count; c0 += 8 * NT) {
+          uint2 r[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int i = c0 + j * NT + tid;
+            r[j] = i < (int)count ? s_c[i] : make_uint2(0u, 0xFFFFFFFFu);
+          }
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c0 + j * NT + tid < (int)count && (r[j].x > kstar || (r[j].x == kstar && r[j].y <= tstar)))
+              s_sel[atomicAdd(&s_m, 1)] = r[j].y;
+          __syncthreads();
+        }
+        n_sel = min(s_m, g.n_fac);  // == n_fac
+        clear_bitmap(bm);
+        __syncthreads();
+        for (int i = tid; i < n_sel; i += NT) mark(s_sel[i]);
       }
       __syncthreads();
-      // the histogram is free by then; n_fac < 2^16 here
-      emit(src, reinterpret_cast<uint16_t*>(s_hist));
+      prefix(bm, pre);
+      __syncthreads();
+      if (direct) {
+        src.for_each([&](uint32_t, uint32_t t) {
+          if (bm[t >> 5] & (1u << (t & 31))) put(bm, pre, t);
+        });
+      } else {
+        for (int i = tid; i < n_sel; i += NT) put(bm, pre, s_sel[i]);
+      }
     } else {
       const size_t slice = group_query_dom<E>(g, item, s_q);
       __syncthreads();
@@ -1007,11 +1089,19 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
       const ScoreScan src{sc, g.T};
       uint32_t kstar, tstar;
       exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+      uint32_t* bm = reinterpret_cast<uint32_t*>(s_c);
+      uint16_t* pre = reinterpret_cast<uint16_t*>(bm + NT * per);
+      clear_bitmap(bm);
+      __syncthreads();
       src.for_each([&](uint32_t k, uint32_t t) {
-        if (k > kstar || (k == kstar && t <= tstar)) mark(t);
+        if (k > kstar || (k == kstar && t <= tstar)) atomicOr(&bm[t >> 5], 1u << (t & 31));
       });
       __syncthreads();
-      emit(src, reinterpret_cast<uint32_t*>(s_c));
+      prefix(bm, pre);
+      __syncthreads();
+      src.for_each([&](uint32_t k, uint32_t t) {
+        if (k > kstar || (k == kstar && t <= tstar)) put(bm, pre, t);
+      });
     }
   }
 }

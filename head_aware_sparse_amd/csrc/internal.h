@@ -15,7 +15,7 @@ constexpr int kMaxTipChunks = 1024;  // score chunks per item
 constexpr int kMaxPairs = 8192;      // (layer, KV group) pairs per call
 constexpr int kCandFast = 16384;     // candidates per item on the prefiltered path (LDS)
 constexpr int kSampleTokens = 4096;  // tokens scored per item to place the prefilter
-constexpr int kPrefilterMaxT = 131072;  // token bitmap of the prefiltered path lives in LDS
+constexpr int kPrefilterMaxT = 524288;  // token bitmap of the prefiltered path fits the final kernel's LDS
 
 // One decode call, with the workspace carved.  Passed by value to kernels.
 struct Geo {
@@ -57,7 +57,6 @@ struct Geo {
   float* qbar;       // [idx items][R] group query in k_dom channel order (prefiltered path)
   int ct_tip;        // tokens per scoring unit on the prefiltered path
   int nch_tip;       // scoring units per item on the prefiltered path
-  uint32_t* bitmap;  // [idx items][bm_words] selected-token bitmap
   float* part;       // [att items][nparts][G][d + 4]: acc[d], m, l
   // inputs / outputs
   const void* q;

@@ -192,14 +192,15 @@ def test_interleaved_rope_pairing():
             U.check_out(out[l, b, g * G:(g + 1) * G], ref, f"interleaved out b{b} g{g}")
 
 
-def test_prefilter_fallback_too_few_candidates():
+@pytest.mark.parametrize("T", [32768, 262144])
+def test_prefilter_fallback_too_few_candidates(T):
     """Adversarial scores: the keys at the sampled token positions are scaled
     up 40x, so the sample places its threshold far above the true n_fac-th
     score and fewer than n_fac tokens pass; the selection must fall back to a
     full rescoring of the item and stay exact."""
     import numpy as np
-    cfg = R.get_config("c1", ctx_len=32768, batch=1)
-    print("case prefilter fallback", flush=True)
+    cfg = R.get_config("c1", ctx_len=T, batch=1)
+    print(f"case prefilter fallback T={T}", flush=True)
     hi = R.HostInputs(cfg, with_weights=False)
     T = cfg.ctx_len
     sampled = np.concatenate([np.arange(256) + (blk * (T - 256)) // 15 for blk in range(16)])
@@ -222,14 +223,15 @@ def test_prefilter_fallback_too_few_candidates():
     U.check_out(out[l, 0, g * cfg.group:(g + 1) * cfg.group], ref, "fallback out")
 
 
-@pytest.mark.parametrize("shared_q,levels", [(True, 1), (False, 2)], ids=["coarse-ties", "fine-ties"])
-def test_tied_scores_select_exactly(shared_q, levels):
+@pytest.mark.parametrize("shared_q,levels,T", [(True, 1, 32768), (False, 2, 32768), (False, 2, 262144)],
+                         ids=["coarse-ties", "fine-ties", "fine-ties-256k"])
+def test_tied_scores_select_exactly(shared_q, levels, T):
     """Integer-valued cache rows and queries make the TIP scores exact small
     multiples of 1/G with hundreds to thousands of tokens on each value, so
     the n_fac-th score is shared by many tokens (ties go to the lower index)
     and the bin that holds it is crowded: the selection must stay exact."""
-    cfg = R.get_config("c1", ctx_len=32768, batch=1)
-    print(f"case ties shared_q={shared_q} levels={levels}", flush=True)
+    cfg = R.get_config("c1", ctx_len=T, batch=1)
+    print(f"case ties shared_q={shared_q} levels={levels} T={T}", flush=True)
     hi = R.HostInputs(cfg, with_weights=False)
     (l, g) = R.planted_groups(cfg)[0]
     G = cfg.group
@@ -259,7 +261,7 @@ def test_tied_scores_select_exactly(shared_q, levels):
 
 
 @pytest.mark.parametrize("over", [
-    dict(ctx_len=150000, n_fac=2048, batch=1),   # above the prefiltered path's 131072-token limit
+    dict(ctx_len=150000, n_fac=2048, batch=1),   # prefiltered, a ragged last scoring unit
     dict(ctx_len=8191, n_fac=500, batch=2),      # just below its 8192-token minimum
     dict(ctx_len=32768, n_fac=6000, batch=1),    # 3 n_fac above its 16384 candidate slots
     dict(ctx_len=8192, n_fac=3000, batch=1),     # near its largest n_fac at its smallest T (prefiltered)
@@ -272,6 +274,21 @@ def test_selection_path_boundaries(over):
     print(f"case boundaries {over}", flush=True)
     case = U.DeviceCase(cfg)
     _check_items(case, _all_items(cfg)[:cfg.n_kv_heads * 2], f"boundary {over}")
+
+
+@pytest.mark.parametrize("T", [262144, 524288, 524289], ids=["T256k", "T512k-max-prefiltered", "T512k+1-general"])
+def test_long_context_selection(T):
+    """Long contexts (the 256K scale and the prefiltered path's 524288-token
+    limit, where the final kernel's token bitmap fills most of its candidate
+    buffer; one token more takes the general path): a retrieval and a
+    streaming group of one sequence against the oracle, the planted needles
+    selected."""
+    cfg = R.get_config("c1", ctx_len=T, batch=1, n_q_heads=8, n_kv_heads=2)
+    print(f"case long context T={T}", flush=True)
+    lab = np.array([[1, 0]], np.uint8)
+    case = U.DeviceCase(cfg, labels=lab)
+    out, idx = _check_items(case, [(0, 0, 0), (0, 0, 1)], f"T{T}")
+    assert np.isin(R.needle_positions(cfg, 0, 0, 0), idx[0, 0, 0]).all()
 
 
 def test_debug_checks_reject_bad_arrays(monkeypatch):
