@@ -127,6 +127,10 @@ def main():
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--clsa-mode", default="fused", choices=["fused", "sequential"],
                     help="shared-index workload: one fused call, or one sparse_select plus one fac_attend per layer")
+    ap.add_argument("--cache", default="full", choices=["full", "split"],
+                    help="split: streaming groups keep only sink + window rows (filled by kv_append)")
+    ap.add_argument("--no-split", action="store_true",
+                    help="with the full cache: skip the extra timing of the same step on the split cache")
     ap.add_argument("--ctx-len", type=int, default=None, help="override the workload's context length")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -236,7 +240,62 @@ def main():
 
     out = torch.empty((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), dtype=torch.float32, device="cuda")
     sequential = cfg.clsa and args.clsa_mode == "sequential"
-    if sequential:
+    split = args.cache == "split" and not cfg.clsa
+    cache_info = None
+
+    def build_split():
+        """The split cache, filled from the full one by one prefill append
+        (capacity 16 rows above the length, for the timed token appends)."""
+        lab_flat = labels_np.astype(bool).reshape(-1)
+        n_ret, n_str = int(lab_flat.sum()), int((~lab_flat).sum())
+        cap = cfg.ctx_len + 16
+        S = cfg.n_sink + cfg.window
+        mk = lambda *shape: torch.empty(shape, dtype=k.dtype, device="cuda")
+        sc = dict(k_ret=mk(n_ret, cfg.batch, cap, cfg.d_head), v_ret=mk(n_ret, cfg.batch, cap, cfg.d_head),
+                  k_dom_ret=mk(n_ret, cfg.batch, cap, H.kdom_row_elems(dims)),
+                  k_str=mk(n_str, cfg.batch, S, cfg.d_head), v_str=mk(n_str, cfg.batch, S, cfg.d_head))
+        H.timing_enable(True)
+        H.kv_append(dims, 0, k, v, i_dom, labels, sc["k_ret"], sc["v_ret"], sc["k_dom_ret"], sc["k_str"], sc["v_str"])
+        torch.cuda.synchronize()
+        pa = H.timing_collect()
+        H.timing_enable(False)
+        es = k.element_size()
+        info = {"layout": "split", "bytes": sum(t.numel() for t in sc.values()) * es,
+                "full_layout_bytes": (k.numel() + v.numel() + kd.numel()) * es,
+                "prefill_append_ms": round(pa["kv_append"][0], 4)}
+        return sc, info
+
+    def split_step_fn(sc):
+        ws_s = H.sparse_decode_step_split(dims, q, sc["k_ret"], sc["v_ret"], sc["k_dom_ret"], sc["k_str"],
+                                          sc["v_str"], i_dom, labels, out)
+
+        def f():
+            H.sparse_decode_step_split(dims, q, sc["k_ret"], sc["v_ret"], sc["k_dom_ret"], sc["k_str"], sc["v_str"],
+                                       i_dom, labels, out, ws=ws_s)
+        return f
+
+    kv_dtype = k.dtype
+
+    def token_append_ms(sc):
+        """One decoded token's append (the next position); it overwrites the
+        oldest window slot, so it runs after the decode timing."""
+        k1 = torch.randn((cfg.n_layers, cfg.batch, cfg.n_kv_heads, 1, cfg.d_head), device="cuda").to(kv_dtype)
+        v1 = torch.randn((cfg.n_layers, cfg.batch, cfg.n_kv_heads, 1, cfg.d_head), device="cuda").to(kv_dtype)
+        H.timing_enable(True)
+        for t in range(10):
+            H.kv_append(dims, cfg.ctx_len + t, k1, v1, i_dom, labels, sc["k_ret"], sc["v_ret"], sc["k_dom_ret"],
+                        sc["k_str"], sc["v_str"])
+        torch.cuda.synchronize()
+        ta = H.timing_collect()
+        H.timing_enable(False)
+        return round(ta["kv_append"][0] / ta["kv_append"][1], 5)
+
+    if split:
+        sc_main, cache_info = build_split()
+        del k, v, kd  # the split cache replaces the full one
+        torch.cuda.empty_cache()
+        step = split_step_fn(sc_main)
+    elif sequential:
         # the layer-by-layer form: the index once, then one attention call per layer
         k0, v0, kd0, id0 = k[0], v[0], kd[0], i_dom[0]
         d1 = H.DecodeDims(*[getattr(dims, f) for f, _ in dims._fields_])
@@ -304,6 +363,29 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
 
+    split_extra = None
+    if split:
+        cache_info["token_append_ms"] = token_append_ms(sc_main)
+    elif not cfg.clsa and not args.no_split:
+        # the same step on the split cache, which then replaces the full one
+        sc_x, split_extra = build_split()
+        del k, v, kd
+        torch.cuda.empty_cache()
+        f = split_step_fn(sc_x)
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        x0.record()
+        for _ in range(args.steps):
+            f()
+        x1.record()
+        torch.cuda.synchronize()
+        xms = x0.elapsed_time(x1) / args.steps
+        split_extra.update({"ms_per_step": round(xms, 5), "value": round(1e3 / xms, 2)})
+        split_extra["token_append_ms"] = token_append_ms(sc_x)
+        del sc_x
+        torch.cuda.empty_cache()
     ab = algorithmic_bytes(cfg, None if cfg.clsa else labels_np, per_layer_gather=sequential)
     tip_ms = kernels_ms["tip_score"]
     tip_gbps = ab["tip"] / (tip_ms * 1e-3) / 1e9
@@ -333,6 +415,7 @@ def main():
             "c4": f"32-layer Llama-3-8B-shaped sparse decode step, batch {cfg.batch}, ctx {cfg.ctx_len}, 64 of 256 "
                   "(layer, KV group) pairs retrieval"}[cfg.name],
             "clsa_mode": args.clsa_mode if cfg.clsa else None,
+            "cache": "split" if split else "full",
             "name": cfg.name, "layers": cfg.n_layers, "batch": cfg.batch, "ctx_len": cfg.ctx_len,
             "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "d_head": cfg.d_head, "n_dom": cfg.n_dom,
             "n_fac": cfg.n_fac, "n_sink": cfg.n_sink, "window": cfg.window},
@@ -348,6 +431,10 @@ def main():
     }
     if layer_ms is not None:
         res["fac_attend_ms_per_layer"] = layer_ms
+    if cache_info is not None:
+        res["cache"] = cache_info
+    if split_extra is not None:
+        res["split_cache"] = split_extra
     if not args.no_cpu_baseline and not cfg.clsa:
         nr, ns = (int(x) for x in args.cpu_sample.split(","))
         log("timing the CPU oracle on a sample of the step")

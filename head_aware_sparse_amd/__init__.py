@@ -15,12 +15,14 @@ from .binding import (  # noqa: F401
     aoh_label,
     aoh_label_workspace,
     kdom_pack,
+    kv_append,
     kdom_row_elems,
     last_error,
     library_path,
     shared_index_decode,
     shared_index_workspace,
     sparse_decode_step,
+    sparse_decode_step_split,
     sparse_decode_workspace,
     sparse_select,
     sparse_select_workspace,

@@ -61,6 +61,10 @@ def lib():
         L.shared_index_workspace.restype = S
         L.shared_index_decode.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, S, P]
         L.shared_index_decode.restype = I
+        L.kv_append.argtypes = [DP, I, I, I, P, P, P, P, P, P, P, P, P, P]
+        L.kv_append.restype = I
+        L.sparse_decode_step_split.argtypes = [DP, I, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.sparse_decode_step_split.restype = I
         L.sparse_select_workspace.argtypes = [DP]
         L.sparse_select_workspace.restype = S
         L.sparse_select.argtypes = [DP, P, P, P, P, P, S, P]
@@ -208,6 +212,76 @@ def shared_index_decode(dims, q, k_cache, v_cache, k_dom, i_dom, out, q_index=No
     _check(lib().shared_index_decode(ctypes.byref(dims), _ptr(q), _ptr(q_index), _ptr(k_cache), _ptr(v_cache),
                                      _ptr(k_dom), _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _ptr(ws),
                                      ws.numel(), _stream(stream)))
+    return ws
+
+
+_dummy = {}
+
+
+def _ptr_nonempty(t):
+    """A device pointer for t; a 16-byte placeholder when t is empty (no
+    pair of that kind: the kernels never touch it)."""
+    if t.numel() > 0:
+        return _ptr(t)
+    import torch
+    key = t.device
+    if key not in _dummy:
+        _dummy[key] = torch.zeros(16, dtype=torch.uint8, device=t.device)
+    return _ptr(_dummy[key])
+
+
+def _split_capacity(dims, k_ret, v_ret, k_dom_ret, k_str, v_str):
+    """Checks a split cache's tensors against dims; returns its capacity."""
+    B, Hkv, d = dims.batch, dims.n_kv_heads, dims.d_head
+    dt = _kv_torch_dtype(dims)
+    if k_ret.dim() != 4:
+        raise ValueError("k_ret must be [n_ret, batch, capacity, d_head]")
+    n_ret, cap = k_ret.shape[0], k_ret.shape[2]
+    if cap < 1:
+        raise ValueError("k_ret's capacity (dim 2) must be >= 1, also with no retrieval pair")
+    n_str = dims.n_layers * Hkv - n_ret
+    _dev(k_ret, "k_ret", dt, (n_ret, B, cap, d))
+    _dev(v_ret, "v_ret", dt, (n_ret, B, cap, d))
+    _dev(k_dom_ret, "k_dom_ret", dt, (n_ret, B, cap, kdom_row_elems(dims)))
+    _dev(k_str, "k_str", dt, (n_str, B, dims.n_sink + dims.window, d))
+    _dev(v_str, "v_str", dt, (n_str, B, dims.n_sink + dims.window, d))
+    return cap
+
+
+def kv_append(dims, pos, k_new, v_new, i_dom, labels, k_ret, v_ret, k_dom_ret, k_str, v_str, stream=None):
+    import torch
+    L, B, Hkv, d = dims.n_layers, dims.batch, dims.n_kv_heads, dims.d_head
+    dt = _kv_torch_dtype(dims)
+    if k_new.dim() != 5:
+        raise ValueError("k_new must be [n_layers, batch, n_kv_heads, n_new, d_head]")
+    n_new = k_new.shape[3]
+    _dev(k_new, "k_new", dt, (L, B, Hkv, n_new, d))
+    _dev(v_new, "v_new", dt, (L, B, Hkv, n_new, d))
+    _dev(i_dom, "i_dom", torch.int32, (L, Hkv, dims.n_dom))
+    _dev(labels, "labels", torch.uint8, (L, Hkv))
+    cap = _split_capacity(dims, k_ret, v_ret, k_dom_ret, k_str, v_str)
+    _check(lib().kv_append(ctypes.byref(dims), cap, pos, n_new, _ptr(k_new), _ptr(v_new), _ptr(i_dom), _ptr(labels),
+                           _ptr_nonempty(k_ret), _ptr_nonempty(v_ret), _ptr_nonempty(k_dom_ret),
+                           _ptr_nonempty(k_str), _ptr_nonempty(v_str), _stream(stream)))
+
+
+def sparse_decode_step_split(dims, q, k_ret, v_ret, k_dom_ret, k_str, v_str, i_dom, labels, out, idx_out=None,
+                             ws=None, stream=None):
+    import torch
+    L, B, Hq, Hkv, d = dims.n_layers, dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.d_head
+    dt = _kv_torch_dtype(dims)
+    _dev(q, "q", dt, (L, B, Hq, d))
+    _dev(i_dom, "i_dom", torch.int32, (L, Hkv, dims.n_dom))
+    _dev(labels, "labels", torch.uint8, (L, Hkv))
+    _dev(out, "out", torch.float32, (L, B, Hq, d))
+    _dev(idx_out, "idx_out", torch.int32, (L, B, Hkv, dims.n_fac))
+    cap = _split_capacity(dims, k_ret, v_ret, k_dom_ret, k_str, v_str)
+    nbytes = sparse_decode_workspace(dims)
+    ws = _workspace(nbytes, ws, q)
+    _check(lib().sparse_decode_step_split(ctypes.byref(dims), cap, _ptr(q), _ptr_nonempty(k_ret),
+                                          _ptr_nonempty(v_ret), _ptr_nonempty(k_dom_ret), _ptr_nonempty(k_str),
+                                          _ptr_nonempty(v_str), _ptr(i_dom), _ptr(labels),
+                                          _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
 

@@ -121,6 +121,7 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   g.bf16 = d->kv_dtype == HAS_BF16;
   g.clsa = clsa ? 1 : 0;
   g.interleaved = d->rope_layout == HAS_ROPE_INTERLEAVED;
+  g.tstride = d->ctx_len;
   const long long n_idx = (long long)(clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att = (long long)g.Lq * g.Hkv * g.B;
   // Score chunks: aim for ~1024 units over the worst-case item count.
@@ -311,12 +312,27 @@ has_status debug_check_idx(const has_decode_dims* d, const int32_t* idx, void* s
   return HAS_OK;
 }
 
+// The split cache of sparse_decode_step_split: slabs of `capacity` rows for
+// retrieval groups, rings of n_sink + window rows for streaming groups.
+struct SplitCache {
+  int capacity;
+  const void* k_str;
+  const void* v_str;
+};
+
 has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, const void* q_index,
                       const void* k_cache, const void* v_cache, const void* k_dom, const int32_t* i_dom,
                       const uint8_t* labels, float* out, int32_t* idx_out, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      void* stream, const SplitCache* sc = nullptr) {
   has_status s = check_dims(dims, clsa);
   if (s != HAS_OK) return s;
+  if (sc) {
+    if (sc->capacity < dims->ctx_len || sc->capacity > has::kMaxTipChunks * 4096)
+      return fail(HAS_ERR_INVALID_ARG, "capacity %d outside [ctx_len=%d, %d]", sc->capacity, dims->ctx_len,
+                  has::kMaxTipChunks * 4096);
+    REQUIRE_PTR(sc->k_str, "k_str");
+    REQUIRE_PTR(sc->v_str, "v_str");
+  }
   REQUIRE_PTR(q, "q");
   OPTIONAL_PTR(q_index, "q_index");
   REQUIRE_PTR(k_cache, "k_cache");
@@ -343,6 +359,13 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
   g.host_plan = (clsa && labels == nullptr && g.prefilter) ? 1 : 0;
   g.out = out;
   g.idx_out = idx_out;
+  if (sc) {
+    g.split = 1;
+    g.tstride = sc->capacity;
+    g.scap = dims->n_sink + dims->window;
+    g.k_str = sc->k_str;
+    g.v_str = sc->v_str;
+  }
   if (debug_checks()) {
     s = debug_check_arrays(dims, clsa ? dims->n_kv_heads : dims->n_layers * dims->n_kv_heads, i_dom, labels,
                            dims->n_layers * dims->n_kv_heads, stream);
@@ -493,6 +516,54 @@ has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const 
                               void* stream) {
   return run_decode(dims, false, q, nullptr, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out, ws,
                     ws_bytes, stream);
+}
+
+has_status sparse_decode_step_split(const has_decode_dims* dims, int capacity, const void* q, const void* k_ret,
+                                    const void* v_ret, const void* k_dom_ret, const void* k_str, const void* v_str,
+                                    const int32_t* i_dom, const uint8_t* labels, float* out, int32_t* idx_out,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  const SplitCache sc{capacity, k_str, v_str};
+  return run_decode(dims, false, q, nullptr, k_ret, v_ret, k_dom_ret, i_dom, labels, out, idx_out, ws, ws_bytes,
+                    stream, &sc);
+}
+
+has_status kv_append(const has_decode_dims* dims, int capacity, int pos, int n_new, const void* k_new,
+                     const void* v_new, const int32_t* i_dom, const uint8_t* labels, void* k_ret, void* v_ret,
+                     void* k_dom_ret, void* k_str, void* v_str, void* stream) {
+  if (!dims) return fail(HAS_ERR_INVALID_ARG, "dims is NULL");
+  // ctx_len and n_fac are not used: the capacity stands in for the length
+  has_decode_dims d = *dims;
+  d.ctx_len = capacity;
+  d.n_fac = 1;
+  has_status s = check_dims(&d, false);
+  if (s != HAS_OK) return s;
+  if (pos < 0 || n_new < 1 || (long long)pos + n_new > capacity)
+    return fail(HAS_ERR_INVALID_ARG, "positions [%d, %d + %d) outside [0, capacity=%d)", pos, pos, n_new, capacity);
+  REQUIRE_PTR(k_new, "k_new");
+  REQUIRE_PTR(v_new, "v_new");
+  REQUIRE_PTR(i_dom, "i_dom");
+  REQUIRE_PTR(labels, "labels");
+  REQUIRE_PTR(k_ret, "k_ret");
+  REQUIRE_PTR(v_ret, "v_ret");
+  REQUIRE_PTR(k_dom_ret, "k_dom_ret");
+  REQUIRE_PTR(k_str, "k_str");
+  REQUIRE_PTR(v_str, "v_str");
+  Layout L = make_layout(&d, false);
+  has::Geo& g = L.g;
+  g.i_dom = i_dom;
+  g.labels = labels;
+  g.tstride = capacity;
+  g.scap = d.n_sink + d.window;
+  if (debug_checks()) {
+    s = debug_check_arrays(&d, d.n_layers * d.n_kv_heads, i_dom, labels, d.n_layers * d.n_kv_heads, stream);
+    if (s != HAS_OK) return s;
+  }
+  s = persistent_grid(g.grid);
+  if (s != HAS_OK) return s;
+  const hipError_t e = has::launch_kv_append(g, pos, n_new, k_new, v_new, k_ret, v_ret, k_dom_ret, k_str, v_str,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return ok();
 }
 
 size_t shared_index_workspace(const has_decode_dims* dims) {

@@ -279,7 +279,7 @@ __device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
     }
     s_q[c] = v;
   }
-  return ((size_t)l * g.B + b) * g.Hkv + gi;
+  return g.split ? (size_t)pidx * g.B + b : ((size_t)l * g.B + b) * g.Hkv + gi;
 }
 
 // One token's TIP score by a single thread (row of R elements).
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
       const int pidx = item / g.B, b = item - pidx * g.B;
       const int pair = idx_pair(g, pidx);
       const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
-      slice = ((size_t)l * g.B + b) * g.Hkv + gi;
+      slice = g.split ? (size_t)pidx * g.B + b : ((size_t)l * g.B + b) * g.Hkv + gi;
       const float* qb = g.qbar + (size_t)item * R + (lane % V) * EPV;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) qr[e] = qb[e];
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
 #pragma unroll
       for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
     }
-    const E* kd = (const E*)g.kdom + slice * (size_t)g.T * R;
+    const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * R;
     float* sc = g.scores + (size_t)item * g.Ts;
     const int t0 = ch * ct, t1 = min(g.T, t0 + ct);
     for (int base = t0 + wave * 64; base < t1; base += NT * U) {
@@ -852,7 +852,7 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
     float qr[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
-    const E* kd = (const E*)g.kdom + slice * (size_t)g.T * R;
+    const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * R;
     const int start = (int)((long long)blk * (g.T - 256) / (kBlocks - 1));
     uint4 raw[V];
 #pragma unroll
@@ -1081,7 +1081,7 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
     } else {
       const size_t slice = group_query_dom<E>(g, item, s_q);
       __syncthreads();
-      const E* kd = (const E*)g.kdom + slice * (size_t)g.T * g.R;
+      const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * g.R;
       float* sc = g.scores + (size_t)item * g.Ts;
       for (int t = tid; t < g.T; t += NT) sc[t] = score_one<E>(kd + (size_t)t * g.R, s_q, g.R);
       __threadfence();
@@ -1261,9 +1261,12 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
     const int pair = fac ? ret_pair(g, pa) : str_pair(g, pa);
     const int lq = pair / g.Hkv, gi = pair - lq * g.Hkv;
     const int lkv = g.clsa ? 0 : lq;
-    const size_t kvs = ((size_t)lkv * g.B + b) * g.Hkv + gi;
-    const E* kb = (const E*)g.k + kvs * (size_t)g.T * D;
-    const E* vb = (const E*)g.v + kvs * (size_t)g.T * D;
+    // split cache: slab = list position x B + b, a streaming group's rows in its ring
+    const bool ring = g.split && !fac;
+    const size_t kvs = g.split ? (size_t)pa * g.B + b : ((size_t)lkv * g.B + b) * g.Hkv + gi;
+    const size_t rows_per = ring ? (size_t)g.scap : (size_t)g.tstride;
+    const E* kb = (const E*)(ring ? g.k_str : g.k) + kvs * rows_per * D;
+    const E* vb = (const E*)(ring ? g.v_str : g.v) + kvs * rows_per * D;
     __syncthreads();
     int nrows;
     if (fac) {
@@ -1277,7 +1280,9 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
       nrows = min(g.cs, g.n_srows - chunk * g.cs);
       for (int r = tid; r < nrows; r += NT) {
         const int v = chunk * g.cs + r;
-        s_rows[r] = v < g.s_end ? v : g.w_start + (v - g.s_end);
+        const int pos = v < g.s_end ? v : g.w_start + (v - g.s_end);
+        // ring slot of a position: the sink as is, the window modulo its size
+        s_rows[r] = !ring || pos < g.n_sink ? pos : g.n_sink + (pos - g.n_sink) % g.window;
       }
     }
     float qr[G][CPL];
@@ -1741,6 +1746,94 @@ hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s) {
     kdom_pack_kernel<uint16_t><<<grid, NT, 0, s>>>(g, (uint16_t*)k_dom);
   else
     kdom_pack_kernel<float><<<grid, NT, 0, s>>>(g, (float*)k_dom);
+  return hipGetLastError();
+}
+
+// kv_append ([AoH] §4: a streaming head keeps only the sink and the recent
+// window).  One unit = (layer, KV group, sequence, block of up to 256 new
+// rows).  A retrieval group's rows go to its slab at their positions, with
+// their dominant-chunk copy; a streaming group keeps the sink positions and
+// the last `window` positions of this call, the window in a ring (so no two
+// writes of one call share a slot).  A pair's slab is its rank among the
+// pairs of its label, counted from the labels before it.
+constexpr int kAppendRows = 256;
+
+template <typename E>
+__global__ __launch_bounds__(NT) void kv_append_kernel(Geo g, int pos0, int n_new, const E* k_new, const E* v_new,
+                                                       E* k_ret, E* v_ret, E* k_dom_ret, E* k_str, E* v_str) {
+  constexpr int EPV = Vec<E>::N;
+  __shared__ int s_w[NWAVE];
+  const int tid = threadIdx.x;
+  const int P = g.Lq * g.Hkv;
+  const int nb = (n_new + kAppendRows - 1) / kAppendRows;
+  const long long n_units = (long long)P * g.B * nb;
+  const int nvec = g.d / EPV, hd = g.d / 2;
+  for (long long u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int blk = (int)(u % nb);
+    const long long pb = u / nb;
+    const int b = (int)(pb % g.B), pair = (int)(pb / g.B);
+    const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
+    int cnt = 0;
+    for (int p = tid; p < pair; p += NT) cnt += label_at(g, p);
+    int before;
+    block_excl_scan(cnt, s_w, before);  // retrieval pairs before this one
+    const bool ret = label_at(g, pair);
+    const size_t slab = (size_t)(ret ? before : pair - before) * g.B + b;
+    const E* ks = k_new + ((((size_t)l * g.B + b) * g.Hkv + gi) * n_new) * g.d;
+    const E* vs = v_new + ((((size_t)l * g.B + b) * g.Hkv + gi) * n_new) * g.d;
+    const int r0 = blk * kAppendRows, r1 = min(n_new, r0 + kAppendRows);
+    if (ret) {
+      E* kd = k_ret + slab * g.tstride * g.d;
+      E* vd = v_ret + slab * g.tstride * g.d;
+      for (int e = tid; e < (r1 - r0) * nvec; e += NT) {
+        const int r = r0 + e / nvec, c = e - (e / nvec) * nvec;
+        const size_t src = (size_t)r * g.d + (size_t)c * EPV, dst = (size_t)(pos0 + r) * g.d + (size_t)c * EPV;
+        *reinterpret_cast<uint4*>(kd + dst) = ld16(ks + src);
+        *reinterpret_cast<uint4*>(vd + dst) = ld16(vs + src);
+      }
+      // dominant-chunk copy, element 2i+c = channel c of chunk i_dom[i] (zero padded)
+      const int32_t* dom = g.i_dom + (size_t)pair * g.n_dom;
+      E* dd = k_dom_ret + slab * g.tstride * g.R;
+      for (int e = tid; e < (r1 - r0) * g.R; e += NT) {
+        const int r = r0 + e / g.R, j = e - (e / g.R) * g.R;
+        E v = E(0);
+        if (j < 2 * g.n_dom) {
+          const int f = min(max(dom[j >> 1], 0), hd - 1), cc = j & 1;
+          v = ks[(size_t)r * g.d + (g.interleaved ? 2 * f + cc : f + cc * hd)];
+        }
+        dd[(size_t)(pos0 + r) * g.R + j] = v;
+      }
+    } else {
+      E* kd = k_str + slab * g.scap * g.d;
+      E* vd = v_str + slab * g.scap * g.d;
+      const int keep_from = pos0 + n_new - g.window;  // the last `window` positions of this call
+      for (int e = tid; e < (r1 - r0) * nvec; e += NT) {
+        const int r = r0 + e / nvec, c = e - (e / nvec) * nvec;
+        const int pos = pos0 + r;
+        if (pos >= g.n_sink && pos < keep_from) continue;
+        const int slot = pos < g.n_sink ? pos : g.n_sink + (pos - g.n_sink) % g.window;
+        const size_t src = (size_t)r * g.d + (size_t)c * EPV, dst = (size_t)slot * g.d + (size_t)c * EPV;
+        *reinterpret_cast<uint4*>(kd + dst) = ld16(ks + src);
+        *reinterpret_cast<uint4*>(vd + dst) = ld16(vs + src);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_kv_append(const Geo& g, int pos0, int n_new, const void* k_new, const void* v_new, void* k_ret,
+                            void* v_ret, void* k_dom_ret, void* k_str, void* v_str, hipStream_t s) {
+  const long long units = (long long)g.Lq * g.Hkv * g.B * ((n_new + kAppendRows - 1) / kAppendRows);
+  const int grid = clampi(units, 1, g.grid);
+  KTimer t("kv_append", s);
+  if (g.bf16)
+    kv_append_kernel<uint16_t><<<grid, NT, 0, s>>>(g, pos0, n_new, (const uint16_t*)k_new, (const uint16_t*)v_new,
+                                                   (uint16_t*)k_ret, (uint16_t*)v_ret, (uint16_t*)k_dom_ret,
+                                                   (uint16_t*)k_str, (uint16_t*)v_str);
+  else
+    kv_append_kernel<float><<<grid, NT, 0, s>>>(g, pos0, n_new, (const float*)k_new, (const float*)v_new,
+                                                (float*)k_ret, (float*)v_ret, (float*)k_dom_ret, (float*)k_str,
+                                                (float*)v_str);
   return hipGetLastError();
 }
 

@@ -42,6 +42,9 @@ struct Geo {
   int attn_mode;    // attention launch: 1 = retrieval (FAC) units, 2 = streaming units
   int select_only;  // stop after the selection (sparse_select)
   int idx_bmajor;   // FAC reads a caller's index laid out [B][Hkv][n_fac] (fac_attend)
+  int split;        // split cache: retrieval groups' slabs [n_ret][B][tstride], streaming groups' rings
+  int tstride;      // rows per cache (and k_dom) slab: T, or the split cache's capacity
+  int scap;         // split cache: rows per streaming ring slab (n_sink + window)
   // workspace
   int* plan;         // [4 + 3*kMaxPairs]: n_idx_pairs, n_att_ret, n_att_str, -, lists
   uint32_t* hist;    // [idx items][kHistBins]
@@ -64,6 +67,8 @@ struct Geo {
   const void* k;
   const void* v;
   const void* kdom;
+  const void* k_str;  // split cache: streaming groups' rings [n_str][B][scap][d]
+  const void* v_str;
   const int32_t* i_dom;
   const uint8_t* labels;
   float* out;
@@ -92,5 +97,9 @@ struct StreamSet {
 hipError_t launch_kdom_pack(const Geo& g, void* k_dom, hipStream_t s);
 hipError_t launch_decode(const Geo& g, const StreamSet& ss);
 hipError_t launch_fac_attend(const Geo& g, hipStream_t s);
+// Writes positions [pos0, pos0 + n_new) of new K/V rows ([L][B][Hkv][n_new][d])
+// into a split cache, with the dominant-chunk copy of retrieval groups' keys.
+hipError_t launch_kv_append(const Geo& g, int pos0, int n_new, const void* k_new, const void* v_new, void* k_ret,
+                            void* v_ret, void* k_dom_ret, void* k_str, void* v_str, hipStream_t s);
 
 }  // namespace has

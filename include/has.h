@@ -163,6 +163,41 @@ has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const 
                               const uint8_t* labels, float* out, int32_t* idx_out, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* Split cache ([AoH] §4: a streaming head only ever attends to the sink and
+ * the recent window, so it need not keep the rest of its cache).  With
+ * n_ret pairs (l, g) labelled retrieval and n_str = n_layers*n_kv_heads -
+ * n_ret labelled streaming, each kind numbered in increasing l*n_kv_heads+g:
+ *   k_ret, v_ret  [n_ret, batch, capacity, d_head]   full rows, row = position
+ *   k_dom_ret     [n_ret, batch, capacity, kdom_row_elems]
+ *   k_str, v_str  [n_str, batch, n_sink + window, d_head]
+ * A streaming group's row for position p sits in slot p when p < n_sink,
+ * else in slot n_sink + (p - n_sink) mod window (the window is a ring).
+ * The caller sizes the arrays from the labels; the library cannot check
+ * their extents.
+ *
+ * kv_append: writes positions [pos, pos + n_new) of new post-RoPE rows
+ * k_new, v_new [n_layers, batch, n_kv_heads, n_new, d_head] into a split
+ * cache: a retrieval group gets its rows and their dominant-chunk copy
+ * (as kdom_pack) at those positions; a streaming group keeps the positions
+ * below n_sink and the last `window` positions of the call.  One call per
+ * decoded token (n_new = 1) keeps the cache current; one call with pos = 0
+ * fills it from a prefill.  Calls must come in increasing position order
+ * for the rings to hold the latest window.  dims->ctx_len and n_fac are not
+ * used; 0 <= pos, 1 <= n_new, pos + n_new <= capacity <= 4194304. */
+has_status kv_append(const has_decode_dims* dims, int capacity, int pos, int n_new, const void* k_new,
+                     const void* v_new, const int32_t* i_dom, const uint8_t* labels, void* k_ret, void* v_ret,
+                     void* k_dom_ret, void* k_str, void* v_str, void* stream);
+
+/* sparse_decode_step_split: sparse_decode_step over a split cache holding
+ * positions 0..ctx_len-1 (ctx_len <= capacity): the same results, reading
+ * retrieval groups' rows and k_dom from their slabs and streaming groups'
+ * sink and window from their rings.  q, i_dom, labels, out and idx_out as
+ * in sparse_decode_step; the workspace is sparse_decode_workspace(dims). */
+has_status sparse_decode_step_split(const has_decode_dims* dims, int capacity, const void* q, const void* k_ret,
+                                    const void* v_ret, const void* k_dom_ret, const void* k_str, const void* v_str,
+                                    const int32_t* i_dom, const uint8_t* labels, float* out, int32_t* idx_out,
+                                    void* ws, size_t ws_bytes, void* stream);
+
 /* shared_index_decode: CLSA mode ([CLSA] "Cómo funciona CLSA").  The
  * dims->n_layers = N layers share ONE cache.  The index is computed once per
  * (b, g) by TIP + top-n_fac (as in sparse_decode_step) from the indexer

@@ -142,3 +142,36 @@ def test_select_and_attend_argument_checks():
     assert H.fac_attend_workspace(_dims(n_layers=2)) == 0
     # the attention-only workspace holds the chunk partials alone
     assert need_a < need_s
+
+
+def test_split_cache_argument_checks():
+    """kv_append and sparse_decode_step_split validate positions, capacity
+    and pointers on the host."""
+    P = ctypes.c_void_p
+    L = lib()
+
+    def append(d, cap=40000, pos=0, n_new=1, **o):
+        p = dict(kn=FAKE, vn=FAKE, idom=FAKE, lab=FAKE, kr=FAKE, vr=FAKE, kdr=FAKE, ks=FAKE, vs=FAKE)
+        p.update(o)
+        return L.kv_append(ctypes.byref(d), cap, pos, n_new, P(p["kn"]), P(p["vn"]), P(p["idom"]), P(p["lab"]),
+                           P(p["kr"]), P(p["vr"]), P(p["kdr"]), P(p["ks"]), P(p["vs"]), None)
+
+    def split(d, cap=40000, ws=None, **o):
+        p = dict(q=FAKE, kr=FAKE, vr=FAKE, kdr=FAKE, ks=FAKE, vs=FAKE, idom=FAKE, lab=FAKE, out=FAKE)
+        p.update(o)
+        return L.sparse_decode_step_split(ctypes.byref(d), cap, P(p["q"]), P(p["kr"]), P(p["vr"]), P(p["kdr"]),
+                                          P(p["ks"]), P(p["vs"]), P(p["idom"]), P(p["lab"]), P(p["out"]), None,
+                                          P(ws) if ws else None, 1 << 40, None)
+
+    d = _dims()
+    assert append(d, pos=-1) == 1
+    assert append(d, n_new=0) == 1
+    assert append(d, pos=39999, n_new=2) == 1 and "capacity" in H.last_error()
+    assert append(d, ks=None) == 1 and "k_str" in H.last_error()
+    assert append(d, kn=FAKE + 2) == 1
+    assert append(_dims(d_head=96)) == 2
+    assert append(_dims(n_sink=0, window=0)) == 1
+    assert split(d, cap=100) == 1 and "capacity" in H.last_error()
+    assert split(d, vs=None) == 1 and "v_str" in H.last_error()
+    assert split(d, lab=None) == 1
+    assert split(d) == 3  # arguments valid: stops at the NULL workspace

@@ -136,3 +136,27 @@ def test_max_pairs_8192():
     case = U.DeviceCase(cfg, labels=lab)
     items = [(l, 0, g) for l in (0, 1, 511, 512, 1022, 1023) for g in (0, 3, 7)]
     _check_items(case, items, "8192 pairs")
+
+
+def test_split_cache_32_layers_128k():
+    """The 32-layer, batch-4, 131072-token step on the split cache (192 of
+    256 (layer, group) pairs keep only 4 + 2048 rows): filled by one prefill
+    kv_append from the full cache, it gives exactly the full-cache results;
+    sampled items of each kind agree with the oracle."""
+    from tests.test_gpu_split_cache import _append, _check_contents, _decode_split, _empty_split, _pairs
+    cfg = R.get_config("c4")
+    print("case c4 split cache", flush=True)
+    case = U.DeviceCase(cfg)
+    out_f, idx_f, _ = case.run()
+    sc = _empty_split(case, cfg.ctx_len)
+    _append(case, sc, 0, case.k, case.v)
+    _check_contents(case, sc, cfg.ctx_len)
+    out_s, idx_s = _decode_split(case, sc, case.dims)
+    assert (idx_s == idx_f).all()
+    assert np.array_equal(out_s, out_f)
+    ret, strm = _pairs(case)
+    G = cfg.group
+    for p in (list(ret)[5], list(strm)[77]):
+        l, g = divmod(p, cfg.n_kv_heads)
+        ref, _, _ = U.oracle_item(cfg, case.hi, case.labels_np, l, 2, g)
+        U.check_out(out_s[l, 2, g * G:(g + 1) * G], ref, f"c4 split l{l} g{g}")
