@@ -127,8 +127,9 @@ def main():
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--clsa-mode", default="fused", choices=["fused", "sequential"],
                     help="shared-index workload: one fused call, or one sparse_select plus one fac_attend per layer")
-    ap.add_argument("--cache", default="full", choices=["full", "split"],
-                    help="split: streaming groups keep only sink + window rows (filled by kv_append)")
+    ap.add_argument("--cache", default="full", choices=["full", "split", "split-host"],
+                    help="split: streaming groups keep only sink + window rows (filled by kv_append); "
+                         "split-host: also the retrieval groups' K and V rows in pinned host memory (FASA-M)")
     ap.add_argument("--no-split", action="store_true",
                     help="with the full cache: skip the extra timing of the same step on the split cache")
     ap.add_argument("--ctx-len", type=int, default=None, help="override the workload's context length")
@@ -240,18 +241,20 @@ def main():
 
     out = torch.empty((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), dtype=torch.float32, device="cuda")
     sequential = cfg.clsa and args.clsa_mode == "sequential"
-    split = args.cache == "split" and not cfg.clsa
+    split = args.cache in ("split", "split-host") and not cfg.clsa
     cache_info = None
 
-    def build_split():
+    def build_split(host_rows=False):
         """The split cache, filled from the full one by one prefill append
-        (capacity 16 rows above the length, for the timed token appends)."""
+        (capacity 16 rows above the length, for the timed token appends);
+        host_rows: the retrieval K and V rows in pinned host memory."""
         lab_flat = labels_np.astype(bool).reshape(-1)
         n_ret, n_str = int(lab_flat.sum()), int((~lab_flat).sum())
         cap = cfg.ctx_len + 16
         S = cfg.n_sink + cfg.window
         mk = lambda *shape: torch.empty(shape, dtype=k.dtype, device="cuda")
-        sc = dict(k_ret=mk(n_ret, cfg.batch, cap, cfg.d_head), v_ret=mk(n_ret, cfg.batch, cap, cfg.d_head),
+        mkr = (lambda *shape: torch.empty(shape, dtype=k.dtype, pin_memory=True)) if host_rows else mk
+        sc = dict(k_ret=mkr(n_ret, cfg.batch, cap, cfg.d_head), v_ret=mkr(n_ret, cfg.batch, cap, cfg.d_head),
                   k_dom_ret=mk(n_ret, cfg.batch, cap, H.kdom_row_elems(dims)),
                   k_str=mk(n_str, cfg.batch, S, cfg.d_head), v_str=mk(n_str, cfg.batch, S, cfg.d_head))
         H.timing_enable(True)
@@ -260,7 +263,9 @@ def main():
         pa = H.timing_collect()
         H.timing_enable(False)
         es = k.element_size()
-        info = {"layout": "split", "bytes": sum(t.numel() for t in sc.values()) * es,
+        host_b = (sc["k_ret"].numel() + sc["v_ret"].numel()) * es if host_rows else 0
+        info = {"layout": "split-host" if host_rows else "split", "bytes": sum(t.numel() for t in sc.values()) * es,
+                "host_bytes": host_b,
                 "full_layout_bytes": (k.numel() + v.numel() + kd.numel()) * es,
                 "prefill_append_ms": round(pa["kv_append"][0], 4)}
         return sc, info
@@ -291,7 +296,7 @@ def main():
         return round(ta["kv_append"][0] / ta["kv_append"][1], 5)
 
     if split:
-        sc_main, cache_info = build_split()
+        sc_main, cache_info = build_split(host_rows=args.cache == "split-host")
         del k, v, kd  # the split cache replaces the full one
         torch.cuda.empty_cache()
         step = split_step_fn(sc_main)
@@ -415,7 +420,7 @@ def main():
             "c4": f"32-layer Llama-3-8B-shaped sparse decode step, batch {cfg.batch}, ctx {cfg.ctx_len}, 64 of 256 "
                   "(layer, KV group) pairs retrieval"}[cfg.name],
             "clsa_mode": args.clsa_mode if cfg.clsa else None,
-            "cache": "split" if split else "full",
+            "cache": args.cache if split else "full",
             "name": cfg.name, "layers": cfg.n_layers, "batch": cfg.batch, "ctx_len": cfg.ctx_len,
             "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "d_head": cfg.d_head, "n_dom": cfg.n_dom,
             "n_fac": cfg.n_fac, "n_sink": cfg.n_sink, "window": cfg.window},

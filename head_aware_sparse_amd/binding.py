@@ -240,8 +240,14 @@ def _split_capacity(dims, k_ret, v_ret, k_dom_ret, k_str, v_str):
     if cap < 1:
         raise ValueError("k_ret's capacity (dim 2) must be >= 1, also with no retrieval pair")
     n_str = dims.n_layers * Hkv - n_ret
-    _dev(k_ret, "k_ret", dt, (n_ret, B, cap, d))
-    _dev(v_ret, "v_ret", dt, (n_ret, B, cap, d))
+    for t, name in ((k_ret, "k_ret"), (v_ret, "v_ret")):  # device, or pinned host memory
+        if t.device.type == "cpu" and t.numel() > 0 and not t.is_pinned():
+            raise ValueError(f"{name} on the host must be pinned memory")
+        if t.device.type == "cpu":
+            if not t.is_contiguous() or t.dtype != dt or tuple(t.shape) != (n_ret, B, cap, d):
+                raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {(n_ret, B, cap, d)}")
+        else:
+            _dev(t, name, dt, (n_ret, B, cap, d))
     _dev(k_dom_ret, "k_dom_ret", dt, (n_ret, B, cap, kdom_row_elems(dims)))
     _dev(k_str, "k_str", dt, (n_str, B, dims.n_sink + dims.window, d))
     _dev(v_str, "v_str", dt, (n_str, B, dims.n_sink + dims.window, d))

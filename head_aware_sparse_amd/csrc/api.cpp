@@ -312,6 +312,32 @@ has_status debug_check_idx(const has_decode_dims* d, const int32_t* idx, void* s
   return HAS_OK;
 }
 
+// The retrieval rows of a split cache (k_ret, v_ret) may live in pinned host
+// memory (FASA §2.C, FASA-M: only the dominant-key copy stays in HBM); the
+// kernels then reach them over the host link through their device-visible
+// address.  Anything but device or pinned host memory is refused: a kernel
+// touching pageable or unresident memory would fault.
+has_status row_store(const void* p, const char* name, const void*& dev) {
+  hipPointerAttribute_t a{};
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // an unregistered pointer: clear the error it leaves
+    return fail(HAS_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", name);
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    dev = p;
+    return HAS_OK;
+  }
+  if (a.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    const hipError_t e2 = hipHostGetDevicePointer(&d, const_cast<void*>(p), 0);
+    if (e2 != hipSuccess) return hip_fail(e2, "hipHostGetDevicePointer");
+    dev = d;
+    return HAS_OK;
+  }
+  return fail(HAS_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", name);
+}
+
 // The split cache of sparse_decode_step_split: slabs of `capacity` rows for
 // retrieval groups, rings of n_sink + window rows for streaming groups.
 struct SplitCache {
@@ -370,6 +396,10 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
     s = debug_check_arrays(dims, clsa ? dims->n_kv_heads : dims->n_layers * dims->n_kv_heads, i_dom, labels,
                            dims->n_layers * dims->n_kv_heads, stream);
     if (s != HAS_OK) return s;
+  }
+  if (sc) {
+    if ((s = row_store(k_cache, "k_ret", g.k)) != HAS_OK) return s;
+    if ((s = row_store(v_cache, "v_ret", g.v)) != HAS_OK) return s;
   }
   s = persistent_grid(g.grid);
   if (s != HAS_OK) return s;
@@ -558,10 +588,13 @@ has_status kv_append(const has_decode_dims* dims, int capacity, int pos, int n_n
     s = debug_check_arrays(&d, d.n_layers * d.n_kv_heads, i_dom, labels, d.n_layers * d.n_kv_heads, stream);
     if (s != HAS_OK) return s;
   }
+  const void *k_dev = nullptr, *v_dev = nullptr;
+  if ((s = row_store(k_ret, "k_ret", k_dev)) != HAS_OK) return s;
+  if ((s = row_store(v_ret, "v_ret", v_dev)) != HAS_OK) return s;
   s = persistent_grid(g.grid);
   if (s != HAS_OK) return s;
-  const hipError_t e = has::launch_kv_append(g, pos, n_new, k_new, v_new, k_ret, v_ret, k_dom_ret, k_str, v_str,
-                                             (hipStream_t)stream);
+  const hipError_t e = has::launch_kv_append(g, pos, n_new, k_new, v_new, const_cast<void*>(k_dev),
+                                             const_cast<void*>(v_dev), k_dom_ret, k_str, v_str, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   return ok();
 }

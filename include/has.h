@@ -11,8 +11,9 @@
  *          Once"), section "Cómo funciona CLSA".
  *
  * Conventions for every entry point:
- *   - Every array argument is a DEVICE pointer to contiguous row-major data,
- *     aligned to 16 bytes, owned by the caller.  The library never allocates
+ *   - Every array argument is a DEVICE pointer to contiguous row-major data
+ *     (one exception, stated at the split cache), aligned to 16 bytes, owned
+ *     by the caller.  The library never allocates
  *     or frees memory and never synchronises the stream.
  *   - `stream` is a hipStream_t (NULL = the default stream); all device work
  *     is enqueued on it, in order, and is asynchronous to the host.
@@ -173,7 +174,13 @@ has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const 
  * A streaming group's row for position p sits in slot p when p < n_sink,
  * else in slot n_sink + (p - n_sink) mod window (the window is a ring).
  * The caller sizes the arrays from the labels; the library cannot check
- * their extents.
+ * their extents.  k_ret and v_ret may instead live in pinned host memory
+ * (hipHostMalloc): the memory-saving variant of [FASA] §2.C (FASA-M), where
+ * only the dominant-key copy k_dom_ret stays in HBM and the selected rows
+ * are read over the host link.  The library maps them to their
+ * device-visible address; memory that is neither device memory nor pinned
+ * host memory is rejected (HAS_ERR_INVALID_ARG).  Every other array is
+ * device memory.
  *
  * kv_append: writes positions [pos, pos + n_new) of new post-RoPE rows
  * k_new, v_new [n_layers, batch, n_kv_heads, n_new, d_head] into a split

@@ -159,3 +159,52 @@ def test_token_by_token_append_across_the_ring_wrap():
                                       case.hi.rows("v", l, 0, g)[:T], case.hi.i_dom[l, g],
                                       bool(case.labels_np[l, g]))
         U.check_out(out_s[l, 0, g * G:(g + 1) * G], ref, f"token-by-token l{l} g{g}")
+
+
+def test_host_resident_rows_fasa_m():
+    """The retrieval groups' full K and V rows in pinned host memory, only the
+    dominant-key copy (and the streaming rings) in HBM: appends and decode
+    read and write them over the host link and give exactly the results of
+    the all-device split cache.  Pageable host memory is refused before any
+    launch."""
+    cfg = R.get_config("c1", ctx_len=12000, batch=2, n_layers=2)
+    print("case FASA-M host rows", flush=True)
+    case = U.DeviceCase(cfg, labels=_labels(cfg, 5))
+    T0 = cfg.ctx_len - 2
+    dev = _empty_split(case, cfg.ctx_len + 8)
+    host = dict(dev)
+    host["k_ret"] = torch.zeros(dev["k_ret"].shape, dtype=dev["k_ret"].dtype, pin_memory=True)
+    host["v_ret"] = torch.zeros(dev["v_ret"].shape, dtype=dev["v_ret"].dtype, pin_memory=True)
+    host["k_dom_ret"] = torch.zeros_like(dev["k_dom_ret"])
+    host["k_str"] = torch.zeros_like(dev["k_str"])
+    host["v_str"] = torch.zeros_like(dev["v_str"])
+    for sc in (dev, host):
+        _append(case, sc, 0, case.k[:, :, :, :T0].contiguous(), case.v[:, :, :, :T0].contiguous())
+        for pos in (T0, T0 + 1):
+            _append(case, sc, pos, case.k[:, :, :, pos:pos + 1].contiguous(), case.v[:, :, :, pos:pos + 1].contiguous())
+    torch.cuda.synchronize()
+    assert (host["k_ret"].view(torch.int16) == dev["k_ret"].cpu().view(torch.int16)).all()
+    out_d, idx_d = _decode_split(case, dev, case.dims)
+    out_h, idx_h = _decode_split(case, host, case.dims)
+    assert (idx_h == idx_d).all()
+    assert np.array_equal(out_h, out_d)
+    pageable = dict(host)
+    pageable["v_ret"] = torch.zeros(dev["v_ret"].shape, dtype=dev["v_ret"].dtype)  # not pinned
+    with pytest.raises((ValueError, H.HasError)):
+        _decode_split(case, pageable, case.dims)
+    # the library's own check, past the binding: a pageable host pointer is
+    # refused before anything is launched
+    import ctypes
+    from head_aware_sparse_amd.binding import lib
+    P = ctypes.c_void_p
+    out = torch.full((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), 7.0, device="cuda")
+    ws = torch.empty(H.sparse_decode_workspace(case.dims), dtype=torch.uint8, device="cuda")
+    r = lib().sparse_decode_step_split(ctypes.byref(case.dims), dev["k_ret"].shape[2], P(case.q.data_ptr()),
+                                       P(host["k_ret"].data_ptr()), P(pageable["v_ret"].data_ptr()),
+                                       P(dev["k_dom_ret"].data_ptr()), P(dev["k_str"].data_ptr()),
+                                       P(dev["v_str"].data_ptr()), P(case.i_dom.data_ptr()),
+                                       P(case.labels.data_ptr()), P(out.data_ptr()), None, P(ws.data_ptr()),
+                                       ws.numel(), None)
+    assert r == 1 and "v_ret" in H.last_error()
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
