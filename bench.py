@@ -33,12 +33,13 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(cfg, labels, per_layer_gather=False):
+def algorithmic_bytes(cfg, labels, per_layer_gather=False, per_head=False):
     """Bytes the method must move per step (counted once): dominant key
     channels of retrieval items, selected K+V rows, sink+window K+V rows,
     queries and outputs.  Scores, histograms and partials are not counted.
     per_layer_gather: the shared index is attended layer by layer, each layer
-    gathering the selected rows again."""
+    gathering the selected rows again.  per_head: every query head scores and
+    gathers for itself (G times the rows of a retrieval group)."""
     import numpy as np
     es = 2 if cfg.bf16 else 4
     d, T = cfg.d_head, cfg.ctx_len
@@ -57,8 +58,9 @@ def algorithmic_bytes(cfg, labels, per_layer_gather=False):
     else:
         n_ret = int(np.asarray(labels).sum()) * cfg.batch
         n_str = cfg.n_layers * cfg.batch * cfg.n_kv_heads - n_ret
-        tip = n_ret * T * 2 * cfg.n_dom * es
-        gather = n_ret * cfg.n_fac * row
+        rep = cfg.n_q_heads // cfg.n_kv_heads if per_head else 1
+        tip = rep * n_ret * T * 2 * cfg.n_dom * es
+        gather = rep * n_ret * cfg.n_fac * row
         stream = n_str * n_srows * row
     qo = cfg.n_layers * cfg.batch * cfg.n_q_heads * d * (es + 4)
     return {"tip": tip, "gather": gather, "stream": stream, "q_out": qo, "total": tip + gather + stream + qo}
@@ -130,6 +132,8 @@ def main():
     ap.add_argument("--cache", default="full", choices=["full", "split", "split-host"],
                     help="split: streaming groups keep only sink + window rows (filled by kv_append); "
                          "split-host: also the retrieval groups' K and V rows in pinned host memory (FASA-M)")
+    ap.add_argument("--select", default="group", choices=["group", "per-head"],
+                    help="per-head: every query head selects its own tokens (the ablation of the group-mean TIP)")
     ap.add_argument("--no-split", action="store_true",
                     help="with the full cache: skip the extra timing of the same step on the split cache")
     ap.add_argument("--ctx-len", type=int, default=None, help="override the workload's context length")
@@ -241,7 +245,8 @@ def main():
 
     out = torch.empty((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), dtype=torch.float32, device="cuda")
     sequential = cfg.clsa and args.clsa_mode == "sequential"
-    split = args.cache in ("split", "split-host") and not cfg.clsa
+    per_head = args.select == "per-head" and not cfg.clsa
+    split = args.cache in ("split", "split-host") and not cfg.clsa and not per_head
     cache_info = None
 
     def build_split(host_rows=False):
@@ -319,6 +324,11 @@ def main():
 
         def step():
             H.shared_index_decode(dims, q, k0, v0, kd0, id0, out, labels=None, ws=ws)
+    elif per_head:
+        ws = H.sparse_decode_step_per_head(dims, q, k, v, kd, i_dom, labels, out)
+
+        def step():
+            H.sparse_decode_step_per_head(dims, q, k, v, kd, i_dom, labels, out, ws=ws)
     else:
         ws = H.sparse_decode_step(dims, q, k, v, kd, i_dom, labels, out)
 
@@ -371,7 +381,7 @@ def main():
     split_extra = None
     if split:
         cache_info["token_append_ms"] = token_append_ms(sc_main)
-    elif not cfg.clsa and not args.no_split:
+    elif not cfg.clsa and not args.no_split and not per_head:
         # the same step on the split cache, which then replaces the full one
         sc_x, split_extra = build_split()
         del k, v, kd
@@ -391,10 +401,12 @@ def main():
         split_extra["token_append_ms"] = token_append_ms(sc_x)
         del sc_x
         torch.cuda.empty_cache()
-    ab = algorithmic_bytes(cfg, None if cfg.clsa else labels_np, per_layer_gather=sequential)
+    ab = algorithmic_bytes(cfg, None if cfg.clsa else labels_np, per_layer_gather=sequential, per_head=per_head)
     tip_ms = kernels_ms["tip_score"]
     tip_gbps = ab["tip"] / (tip_ms * 1e-3) / 1e9
     n_scored = (cfg.batch * cfg.n_kv_heads if cfg.clsa else int(labels_np.sum()) * cfg.batch) * cfg.ctx_len
+    if per_head:
+        n_scored *= cfg.group
     key = f"tip_score_{cfg.name}"
     roofline = {"kernel": "tip_score", "bound": "hbm", "achieved": round(tip_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(tip_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(key),
@@ -421,6 +433,7 @@ def main():
                   "(layer, KV group) pairs retrieval"}[cfg.name],
             "clsa_mode": args.clsa_mode if cfg.clsa else None,
             "cache": args.cache if split else "full",
+            "select": "per-head" if per_head else "group",
             "name": cfg.name, "layers": cfg.n_layers, "batch": cfg.batch, "ctx_len": cfg.ctx_len,
             "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "d_head": cfg.d_head, "n_dom": cfg.n_dom,
             "n_fac": cfg.n_fac, "n_sink": cfg.n_sink, "window": cfg.window},

@@ -21,7 +21,9 @@ from .binding import (  # noqa: F401
     library_path,
     shared_index_decode,
     shared_index_workspace,
+    sparse_decode_per_head_workspace,
     sparse_decode_step,
+    sparse_decode_step_per_head,
     sparse_decode_step_split,
     sparse_decode_workspace,
     sparse_select,

@@ -61,6 +61,10 @@ def lib():
         L.shared_index_workspace.restype = S
         L.shared_index_decode.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, S, P]
         L.shared_index_decode.restype = I
+        L.sparse_decode_per_head_workspace.argtypes = [DP]
+        L.sparse_decode_per_head_workspace.restype = S
+        L.sparse_decode_step_per_head.argtypes = [DP, P, P, P, P, P, P, P, P, P, S, P]
+        L.sparse_decode_step_per_head.restype = I
         L.kv_append.argtypes = [DP, I, I, I, P, P, P, P, P, P, P, P, P, P]
         L.kv_append.restype = I
         L.sparse_decode_step_split.argtypes = [DP, I, P, P, P, P, P, P, P, P, P, P, P, S, P]
@@ -189,6 +193,32 @@ def sparse_decode_step(dims, q, k_cache, v_cache, k_dom, i_dom, labels, out, idx
     _check(lib().sparse_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_dom),
                                     _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(),
                                     _stream(stream)))
+    return ws
+
+
+def sparse_decode_per_head_workspace(dims):
+    return int(lib().sparse_decode_per_head_workspace(ctypes.byref(dims)))
+
+
+def sparse_decode_step_per_head(dims, q, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out=None, ws=None,
+                                stream=None):
+    import torch
+    L, B, Hq, Hkv, T, d = (dims.n_layers, dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.ctx_len,
+                           dims.d_head)
+    dt = _kv_torch_dtype(dims)
+    _dev(q, "q", dt, (L, B, Hq, d))
+    _dev(k_cache, "k_cache", dt, (L, B, Hkv, T, d))
+    _dev(v_cache, "v_cache", dt, (L, B, Hkv, T, d))
+    _dev(k_dom, "k_dom", dt, (L, B, Hkv, T, kdom_row_elems(dims)))
+    _dev(i_dom, "i_dom", torch.int32, (L, Hkv, dims.n_dom))
+    _dev(labels, "labels", torch.uint8, (L, Hkv))
+    _dev(out, "out", torch.float32, (L, B, Hq, d))
+    _dev(idx_out, "idx_out", torch.int32, (L, B, Hq, dims.n_fac))
+    nbytes = sparse_decode_per_head_workspace(dims)
+    ws = _workspace(nbytes, ws, q)
+    _check(lib().sparse_decode_step_per_head(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(k_dom), _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out),
+                                             _ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
 

@@ -122,6 +122,7 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   g.clsa = clsa ? 1 : 0;
   g.interleaved = d->rope_layout == HAS_ROPE_INTERLEAVED;
   g.tstride = d->ctx_len;
+  g.kv_div = 1;
   const long long n_idx = (long long)(clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att = (long long)g.Lq * g.Hkv * g.B;
   // Score chunks: aim for ~1024 units over the worst-case item count.
@@ -349,7 +350,7 @@ struct SplitCache {
 has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, const void* q_index,
                       const void* k_cache, const void* v_cache, const void* k_dom, const int32_t* i_dom,
                       const uint8_t* labels, float* out, int32_t* idx_out, void* ws, size_t ws_bytes,
-                      void* stream, const SplitCache* sc = nullptr) {
+                      void* stream, const SplitCache* sc = nullptr, int kv_div = 1) {
   has_status s = check_dims(dims, clsa);
   if (s != HAS_OK) return s;
   if (sc) {
@@ -392,9 +393,11 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
     g.k_str = sc->k_str;
     g.v_str = sc->v_str;
   }
+  g.kv_div = kv_div;
   if (debug_checks()) {
-    s = debug_check_arrays(dims, clsa ? dims->n_kv_heads : dims->n_layers * dims->n_kv_heads, i_dom, labels,
-                           dims->n_layers * dims->n_kv_heads, stream);
+    const int kv_heads = dims->n_kv_heads / kv_div;
+    s = debug_check_arrays(dims, clsa ? kv_heads : dims->n_layers * kv_heads, i_dom, labels,
+                           dims->n_layers * kv_heads, stream);
     if (s != HAS_OK) return s;
   }
   if (sc) {
@@ -546,6 +549,25 @@ has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const 
                               void* stream) {
   return run_decode(dims, false, q, nullptr, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out, ws,
                     ws_bytes, stream);
+}
+
+size_t sparse_decode_per_head_workspace(const has_decode_dims* dims) {
+  if (check_dims(dims, false) != HAS_OK) return 0;
+  has_decode_dims v = *dims;
+  v.n_kv_heads = dims->n_q_heads;  // one index group per query head
+  return make_layout(&v, false).bytes;
+}
+
+has_status sparse_decode_step_per_head(const has_decode_dims* dims, const void* q, const void* k_cache,
+                                       const void* v_cache, const void* k_dom, const int32_t* i_dom,
+                                       const uint8_t* labels, float* out, int32_t* idx_out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  has_status s = check_dims(dims, false);
+  if (s != HAS_OK) return s;
+  has_decode_dims v = *dims;
+  v.n_kv_heads = dims->n_q_heads;
+  return run_decode(&v, false, q, nullptr, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out, ws, ws_bytes,
+                    stream, nullptr, dims->n_q_heads / dims->n_kv_heads);
 }
 
 has_status sparse_decode_step_split(const has_decode_dims* dims, int capacity, const void* q, const void* k_ret,

@@ -154,8 +154,20 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Index groups are the KV groups, or with kv_div > 1 the query heads (each
+// selecting its own tokens): (layer, index group) pairs and cache slabs map
+// to the KV group that holds the rows, i_dom and the label.
+__device__ __forceinline__ int kv_pair(const Geo& g, int pair) {
+  if (g.kv_div == 1) return pair;
+  const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
+  return l * (g.Hkv / g.kv_div) + gi / g.kv_div;
+}
+__device__ __forceinline__ size_t kv_slice(const Geo& g, int l, int b, int gi) {
+  return ((size_t)l * g.B + b) * (g.Hkv / g.kv_div) + gi / g.kv_div;
+}
+
 __device__ __forceinline__ int label_at(const Geo& g, int pair) {
-  return g.labels ? (g.labels[pair] != 0) : 1;
+  return g.labels ? (g.labels[kv_pair(g, pair)] != 0) : 1;
 }
 
 // Plan accessors: index pairs (one selection each), retrieval and streaming
@@ -264,7 +276,7 @@ __device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
     qg = (const E*)(g.q_index ? g.q_index : g.q) + ((size_t)b * g.Hq + gi * g.G) * g.d;
   else
     qg = (const E*)g.q + (((size_t)l * g.B + b) * g.Hq + gi * g.G) * g.d;
-  const int32_t* dom = g.i_dom + (size_t)pair * g.n_dom;
+  const int32_t* dom = g.i_dom + (size_t)kv_pair(g, pair) * g.n_dom;
   const int hd = g.d / 2;
   for (int c = threadIdx.x; c < g.R; c += NT) {
     float v = 0.f;
@@ -279,7 +291,7 @@ __device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
     }
     s_q[c] = v;
   }
-  return g.split ? (size_t)pidx * g.B + b : ((size_t)l * g.B + b) * g.Hkv + gi;
+  return g.split ? (size_t)pidx * g.B + b : kv_slice(g, l, b, gi);
 }
 
 // One token's TIP score by a single thread (row of R elements).
@@ -438,7 +450,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
       const int pidx = item / g.B, b = item - pidx * g.B;
       const int pair = idx_pair(g, pidx);
       const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
-      slice = g.split ? (size_t)pidx * g.B + b : ((size_t)l * g.B + b) * g.Hkv + gi;
+      slice = g.split ? (size_t)pidx * g.B + b : kv_slice(g, l, b, gi);
       const float* qb = g.qbar + (size_t)item * R + (lane % V) * EPV;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) qr[e] = qb[e];
@@ -1263,7 +1275,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
     const int lkv = g.clsa ? 0 : lq;
     // split cache: slab = list position x B + b, a streaming group's rows in its ring
     const bool ring = g.split && !fac;
-    const size_t kvs = g.split ? (size_t)pa * g.B + b : ((size_t)lkv * g.B + b) * g.Hkv + gi;
+    const size_t kvs = g.split ? (size_t)pa * g.B + b : kv_slice(g, lkv, b, gi);
     const size_t rows_per = ring ? (size_t)g.scap : (size_t)g.tstride;
     const E* kb = (const E*)(ring ? g.k_str : g.k) + kvs * rows_per * D;
     const E* vb = (const E*)(ring ? g.v_str : g.v) + kvs * rows_per * D;

@@ -164,6 +164,23 @@ has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const 
                               const uint8_t* labels, float* out, int32_t* idx_out, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* sparse_decode_step_per_head: the per-query-head selection variant, to
+ * ablate the group-mean TIP above ([FASA] §2.B.1 scores with one head's
+ * query; with G heads per KV group, sparse_decode_step scores with their mean
+ * and the group shares one index).  Here every query head h of a retrieval
+ * group selects its own n_fac tokens from its own scores
+ *   s_t = sum over f in i_dom[l,g] of the chunk-f part of q[l,b,h] . k_t
+ * (ties to the lower t) and attends over them; streaming groups as in
+ * sparse_decode_step.  Arguments as in sparse_decode_step except idx_out
+ * [n_layers,batch,n_q_heads,n_fac] (-1 rows for heads of streaming groups),
+ * and n_layers * n_q_heads <= 8192.  It scores and gathers G times the rows
+ * of sparse_decode_step. */
+size_t sparse_decode_per_head_workspace(const has_decode_dims* dims);
+has_status sparse_decode_step_per_head(const has_decode_dims* dims, const void* q, const void* k_cache,
+                                       const void* v_cache, const void* k_dom, const int32_t* i_dom,
+                                       const uint8_t* labels, float* out, int32_t* idx_out, void* ws,
+                                       size_t ws_bytes, void* stream);
+
 /* Split cache ([AoH] §4: a streaming head only ever attends to the sink and
  * the recent window, so it need not keep the rest of its cache).  With
  * n_ret pairs (l, g) labelled retrieval and n_str = n_layers*n_kv_heads -
