@@ -122,7 +122,8 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   g.clsa = clsa ? 1 : 0;
   g.interleaved = d->rope_layout == HAS_ROPE_INTERLEAVED;
   g.tstride = d->ctx_len;
-  g.kv_div = 1;
+  g.kv_shift = 0;
+  g.hkv_kv = g.Hkv;
   const long long n_idx = (long long)(clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att = (long long)g.Lq * g.Hkv * g.B;
   // Score chunks: aim for ~1024 units over the worst-case item count.
@@ -393,7 +394,9 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
     g.k_str = sc->k_str;
     g.v_str = sc->v_str;
   }
-  g.kv_div = kv_div;
+  // kv_div is the group size G, a power of two
+  g.kv_shift = kv_div == 8 ? 3 : kv_div == 4 ? 2 : kv_div == 2 ? 1 : 0;
+  g.hkv_kv = g.Hkv >> g.kv_shift;
   if (debug_checks()) {
     const int kv_heads = dims->n_kv_heads / kv_div;
     s = debug_check_arrays(dims, clsa ? kv_heads : dims->n_layers * kv_heads, i_dom, labels,

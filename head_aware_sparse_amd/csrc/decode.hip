@@ -154,16 +154,16 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Index groups are the KV groups, or with kv_div > 1 the query heads (each
+// Index groups are the KV groups, or with kv_shift > 0 the query heads (each
 // selecting its own tokens): (layer, index group) pairs and cache slabs map
 // to the KV group that holds the rows, i_dom and the label.
 __device__ __forceinline__ int kv_pair(const Geo& g, int pair) {
-  if (g.kv_div == 1) return pair;
+  if (g.kv_shift == 0) return pair;
   const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
-  return l * (g.Hkv / g.kv_div) + gi / g.kv_div;
+  return l * g.hkv_kv + (gi >> g.kv_shift);
 }
 __device__ __forceinline__ size_t kv_slice(const Geo& g, int l, int b, int gi) {
-  return ((size_t)l * g.B + b) * (g.Hkv / g.kv_div) + gi / g.kv_div;
+  return ((size_t)l * g.B + b) * g.hkv_kv + (gi >> g.kv_shift);
 }
 
 __device__ __forceinline__ int label_at(const Geo& g, int pair) {
@@ -900,16 +900,24 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
 // it (per-word prefix counts), which emits the selection in ascending order.
 // If the candidates are fewer than n_fac or overflowed, the item is rescored
 // in full here and selected from its score row (exact either way).
-template <typename E>
+// LONG = false (T <= kShortMaxT): the bitmap has an LDS array of its own, so
+// it always fits beside the candidates and the compacting path is compiled
+// out; LONG = true: the bitmap goes in the candidate buffer.
+constexpr int kShortMaxT = 131072;
+
+template <typename E, bool LONG>
 __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
-  // candidates; later the selected tokens, the bitmap and the prefix counts
+  // candidates; for LONG, later the selected tokens, the bitmap and the prefix counts
   __shared__ __attribute__((aligned(16))) uint2 s_c[kCandFast];
-  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t s_bm[LONG ? 4 : kShortMaxT / 32];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
   __shared__ float s_q[kMaxR];
   __shared__ int s_w[NWAVE];
   __shared__ uint32_t s_res[2];
   __shared__ uint2 s_list[kRankMax];
   __shared__ int s_m;
+  // !LONG: the prefix counts (u16) reuse the histogram, free by then
+  static_assert(kHistBins * sizeof(uint32_t) >= kShortMaxT / 32 * sizeof(uint16_t), "u16 prefixes in s_hist");
   // bitmap words per thread for the prefix counts: a multiple of 4 (16-byte
   // reads), so the bitmap spans NT * per words
   const int per = ((g.bm_words + NT - 1) / NT + 3) & ~3;
@@ -976,9 +984,10 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
       // and tokens are marked while the threshold is found; else the
       // selected tokens are compacted first and the bitmap built behind them
       const int cand_words = ((int)count * 2 + 3) & ~3;
-      const bool direct = (size_t)(cand_words + NT * per) * 4 + (size_t)NT * per * 2 <= sizeof(s_c);
-      uint32_t* bm = reinterpret_cast<uint32_t*>(s_c) + (direct ? cand_words : kSelWords);
-      uint16_t* pre = reinterpret_cast<uint16_t*>(bm + NT * per);
+      const bool direct =
+          !LONG || (size_t)(cand_words + NT * per) * 4 + (size_t)NT * per * 2 <= sizeof(s_c);
+      uint32_t* bm = !LONG ? s_bm : reinterpret_cast<uint32_t*>(s_c) + (direct ? cand_words : kSelWords);
+      uint16_t* pre = !LONG ? reinterpret_cast<uint16_t*>(s_hist) : reinterpret_cast<uint16_t*>(bm + NT * per);
       if (direct) clear_bitmap(bm);
       __syncthreads();
       // candidates -> LDS, two per 16-byte load, eight loads in flight,
@@ -1101,8 +1110,8 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
       const ScoreScan src{sc, g.T};
       uint32_t kstar, tstar;
       exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
-      uint32_t* bm = reinterpret_cast<uint32_t*>(s_c);
-      uint16_t* pre = reinterpret_cast<uint16_t*>(bm + NT * per);
+      uint32_t* bm = !LONG ? s_bm : reinterpret_cast<uint32_t*>(s_c);
+      uint16_t* pre = !LONG ? reinterpret_cast<uint16_t*>(s_hist) : reinterpret_cast<uint16_t*>(bm + NT * per);
       clear_bitmap(bm);
       __syncthreads();
       src.for_each([&](uint32_t k, uint32_t t) {
@@ -1914,8 +1923,13 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     if (e != hipSuccess) return e;
     {
       KTimer t("select_final", s);
-      if (g.bf16) final_kernel<uint16_t><<<grid_item, NT, 0, s>>>(g);
-      else final_kernel<float><<<grid_item, NT, 0, s>>>(g);
+      if (g.T <= kShortMaxT) {
+        if (g.bf16) final_kernel<uint16_t, false><<<grid_item, NT, 0, s>>>(g);
+        else final_kernel<float, false><<<grid_item, NT, 0, s>>>(g);
+      } else {
+        if (g.bf16) final_kernel<uint16_t, true><<<grid_item, NT, 0, s>>>(g);
+        else final_kernel<float, true><<<grid_item, NT, 0, s>>>(g);
+      }
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {

@@ -45,7 +45,8 @@ struct Geo {
   int split;        // split cache: retrieval groups' slabs [n_ret][B][tstride], streaming groups' rings
   int tstride;      // rows per cache (and k_dom) slab: T, or the split cache's capacity
   int scap;         // split cache: rows per streaming ring slab (n_sink + window)
-  int kv_div;       // index groups per KV group: 1, or G when every query head selects its own tokens
+  int kv_shift;     // log2(index groups per KV group): 0, or log2 G when every query head selects its own tokens
+  int hkv_kv;       // KV groups per layer (Hkv >> kv_shift)
   // workspace
   int* plan;         // [4 + 3*kMaxPairs]: n_idx_pairs, n_att_ret, n_att_str, -, lists
   uint32_t* hist;    // [idx items][kHistBins]
