@@ -267,9 +267,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(Geo g) {
 // Group query of an index item in k_dom channel order (zero padded) into
 // s_q[R]; returns the item's cache slice.  Callers synchronise around it.
 template <typename E>
-__device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
-  const int pidx = item / g.B, b = item - pidx * g.B;
-  const int pair = idx_pair(g, pidx);
+__device__ size_t group_query_dom_at(const Geo& g, int pidx, int pair, int b, float* s_q) {
   const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
   const E* qg;
   if (g.clsa)
@@ -292,6 +290,11 @@ __device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
     s_q[c] = v;
   }
   return g.split ? (size_t)pidx * g.B + b : kv_slice(g, l, b, gi);
+}
+template <typename E>
+__device__ size_t group_query_dom(const Geo& g, int item, float* s_q) {
+  const int pidx = item / g.B, b = item - pidx * g.B;
+  return group_query_dom_at<E>(g, pidx, idx_pair(g, pidx), b, s_q);
 }
 
 // One token's TIP score by a single thread (row of R elements).
@@ -844,22 +847,69 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
 // spread blocks of 256; one unit = (item, block), each wave scoring 64 tokens
 // with the same lane layout as tip_kernel.  Block 0 also stores the item's
 // group query for the scoring pass.
-template <typename E, int V>
+// PLAN (steps without the side stream): no plan launch precedes; every
+// workgroup lists the retrieval pairs from the labels in LDS, workgroup 0
+// writes the plan for the later launches, and the grid fills the -1 index
+// rows of streaming groups.
+template <typename E, int V, bool PLAN>
 __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
   constexpr int EPV = Vec<E>::N;
   constexpr int kBlocks = kSampleTokens / 256;
   __shared__ float s_q[kMaxR];
+  __shared__ uint16_t s_ret[PLAN ? kMaxPairs : 1];
+  __shared__ int s_w[NWAVE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = V * EPV;
-  const int n_units = n_idx_pairs(g) * g.B * kBlocks;
+  int n_idx;
+  if constexpr (PLAN) {
+    const int P = g.Lq * g.Hkv;
+    const int per = (P + NT - 1) / NT;
+    const int p0 = min(P, tid * per), p1 = min(P, p0 + per);
+    int cnt = 0;
+    for (int p = p0; p < p1; ++p) cnt += label_at(g, p);
+    int n_ret;
+    const int excl = block_excl_scan(cnt, s_w, n_ret);
+    int* lists = g.plan + 4;
+    int r = excl, st = p0 - excl;
+    for (int p = p0; p < p1; ++p) {
+      if (label_at(g, p)) {
+        s_ret[r] = (uint16_t)p;
+        if (blockIdx.x == 0) lists[r] = lists[kMaxPairs + r] = p;
+        ++r;
+      } else {
+        if (blockIdx.x == 0) lists[2 * kMaxPairs + st] = p;
+        ++st;
+      }
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+      g.plan[0] = n_ret;
+      g.plan[1] = n_ret;
+      g.plan[2] = P - n_ret;
+      g.plan[3] = 0;
+    }
+    n_idx = n_ret;
+    if (g.idx_out) {
+      const size_t tot = (size_t)g.Lq * g.B * g.Hkv * g.n_fac;
+      for (size_t i = (size_t)blockIdx.x * NT + tid; i < tot; i += (size_t)gridDim.x * NT) {
+        const size_t it = i / (size_t)g.n_fac;
+        const int gi = (int)(it % g.Hkv), l = (int)(it / ((size_t)g.Hkv * g.B));
+        if (!label_at(g, l * g.Hkv + gi)) g.idx_out[i] = -1;
+      }
+    }
+    __syncthreads();
+  } else {
+    n_idx = n_idx_pairs(g);
+  }
+  const int n_units = n_idx * g.B * kBlocks;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const int item = u / kBlocks, blk = u - item * kBlocks;
+    const int pidx = item / g.B, b = item - pidx * g.B;
     __syncthreads();
-    const size_t slice = group_query_dom<E>(g, item, s_q);
+    const size_t slice = group_query_dom_at<E>(g, pidx, PLAN ? (int)s_ret[pidx] : idx_pair(g, pidx), b, s_q);
     __syncthreads();
     if (blk == 0) {
       for (int c = tid; c < R; c += NT) g.qbar[(size_t)item * R + c] = s_q[c];
-      if (g.host_plan && tid < 4) g.info[(size_t)item * 4 + tid] = 0u;  // else the plan clears them
+      if ((PLAN || g.host_plan) && tid < 4) g.info[(size_t)item * 4 + tid] = 0u;  // else the plan clears them
     }
     float qr[EPV];
 #pragma unroll
@@ -1740,18 +1790,22 @@ hipError_t launch_tip_v(const Geo& g, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E>
-hipError_t launch_sample_v(const Geo& g, int grid, hipStream_t s) {
+template <typename E, bool PLAN>
+hipError_t launch_sample_p(const Geo& g, int grid, hipStream_t s) {
   const int V = g.R * (int)sizeof(E) / 16;
   switch (V) {
-    case 1: sample_kernel<E, 1><<<grid, NT, 0, s>>>(g); break;
-    case 2: sample_kernel<E, 2><<<grid, NT, 0, s>>>(g); break;
-    case 4: sample_kernel<E, 4><<<grid, NT, 0, s>>>(g); break;
-    case 8: sample_kernel<E, 8><<<grid, NT, 0, s>>>(g); break;
-    case 16: sample_kernel<E, 16><<<grid, NT, 0, s>>>(g); break;
+    case 1: sample_kernel<E, 1, PLAN><<<grid, NT, 0, s>>>(g); break;
+    case 2: sample_kernel<E, 2, PLAN><<<grid, NT, 0, s>>>(g); break;
+    case 4: sample_kernel<E, 4, PLAN><<<grid, NT, 0, s>>>(g); break;
+    case 8: sample_kernel<E, 8, PLAN><<<grid, NT, 0, s>>>(g); break;
+    case 16: sample_kernel<E, 16, PLAN><<<grid, NT, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+template <typename E>
+hipError_t launch_sample_v(const Geo& g, int grid, hipStream_t s, bool plan) {
+  return plan ? launch_sample_p<E, true>(g, grid, s) : launch_sample_p<E, false>(g, grid, s);
 }
 
 int clampi(long long v, int lo, int hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); }
@@ -1872,7 +1926,12 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   const long long n_idx_items = (long long)(g.clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att_items = (long long)g.Lq * g.Hkv * g.B;
   const int grid_plan = clampi((n_idx_items * kHistBins / 4 + NT - 1) / NT, 1, g.grid);
-  if (!g.host_plan) {
+  const bool any_stream = !(g.clsa && g.labels == nullptr);
+  const bool side = any_stream && (long long)n_att_items * g.n_srows >= kSideStreamRows;
+  // Without the side stream (which forks right after the plan), the sampling
+  // launch builds the plan itself and the plan launch is saved.
+  const bool fuse_plan = g.prefilter && !side && !g.host_plan && !g.clsa;
+  if (!g.host_plan && !fuse_plan) {
     KTimer t("plan", s);
     plan_kernel<<<grid_plan, NT, 0, s>>>(g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1882,8 +1941,6 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   // the scoring and selection of retrieval groups; small (latency-bound)
   // steps attend to them in the retrieval attention's launch instead and
   // skip the event waits.  (The shared-index mode without labels has none.)
-  const bool any_stream = !(g.clsa && g.labels == nullptr);
-  const bool side = any_stream && (long long)n_att_items * g.n_srows >= kSideStreamRows;
   if (side) {
     if ((e = hipEventRecord(ss.fork, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ss.side, ss.fork, 0)) != hipSuccess) return e;
@@ -1904,7 +1961,8 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     {
       KTimer t("sample", s);
       const int grid_sample = clampi(n_idx_items * (kSampleTokens / 256), 1, g.grid);
-      e = g.bf16 ? launch_sample_v<uint16_t>(g, grid_sample, s) : launch_sample_v<float>(g, grid_sample, s);
+      e = g.bf16 ? launch_sample_v<uint16_t>(g, grid_sample, s, fuse_plan)
+                 : launch_sample_v<float>(g, grid_sample, s, fuse_plan);
     }
     if (e != hipSuccess) return e;
     if (!tau_inline) {
