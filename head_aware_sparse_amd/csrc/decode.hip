@@ -1475,7 +1475,9 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
 }
 
 // ------------------------------------------------------------------ merge
-__global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
+// Merge of the chunk partials, one thread per output element (small steps:
+// more threads in flight than the vector form).
+__global__ __launch_bounds__(NT) void merge_scalar_kernel(Geo g) {
   const size_t total = (size_t)g.Lq * g.B * g.Hkv * g.G * g.d;
   const int dd = g.d + 4;
   for (size_t e = (size_t)blockIdx.x * NT + threadIdx.x; e < total; e += (size_t)gridDim.x * NT) {
@@ -1490,8 +1492,6 @@ __global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
     const int np = label_at(g, lq * g.Hkv + gi) ? g.nch_f : g.nch_s;
     const float* pp = g.part + (a * g.nparts * g.G + h) * (size_t)dd;
     const size_t stride = (size_t)g.G * dd;
-    // single pass, online log-sum-exp; partial loads are independent of the
-    // running state, so unrolling keeps several in flight
     float M = -INFINITY, L = 0.f, O = 0.f;
 #pragma unroll 8
     for (int s = 0; s < np; ++s) {
@@ -1504,6 +1504,47 @@ __global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
       M = Mn;
     }
     g.out[(((size_t)lq * g.B + b) * g.Hq + (size_t)gi * g.G + h) * g.d + c] = O / L;
+  }
+}
+
+__global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
+  // (large steps) one thread per 4 channels of one head of one attention item: d/4 and G
+  // are powers of two, so the thread's (item, head, channel block) come from
+  // shifts; the partials and the output move as 16-byte vectors
+  const int sh_c = g.d == 128 ? 5 : 4;                   // log2(d / 4)
+  const int sh_h = g.G == 8 ? 3 : g.G == 4 ? 2 : g.G == 2 ? 1 : 0;
+  const int sh_i = sh_c + sh_h;                          // log2(G * d / 4)
+  const long long total = ((long long)g.Lq * g.B * g.Hkv) << sh_i;
+  const int dd = g.d + 4;
+  for (long long e = (long long)blockIdx.x * NT + threadIdx.x; e < total; e += (long long)gridDim.x * NT) {
+    const int a = (int)(e >> sh_i);
+    const int rem = (int)(e & ((1 << sh_i) - 1));
+    const int h = rem >> sh_c, c = (rem & ((1 << sh_c) - 1)) * 4;
+    const int gi = a % g.Hkv, lb = a / g.Hkv;
+    const int b = lb % g.B, lq = lb / g.B;
+    const int np = label_at(g, lq * g.Hkv + gi) ? g.nch_f : g.nch_s;
+    const float* pp = g.part + ((size_t)a * g.nparts * g.G + h) * (size_t)dd;
+    const size_t stride = (size_t)g.G * dd;
+    // single pass, online log-sum-exp; partial loads are independent of the
+    // running state, so unrolling keeps several in flight
+    float M = -INFINITY, L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int s = 0; s < np; ++s) {
+      const float* q = pp + s * stride;
+      const float ms = q[g.d], ls = q[g.d + 1];
+      const float4 as = *reinterpret_cast<const float4*>(q + c);
+      const float Mn = fmaxf(M, ms);
+      const float f_old = exp2f(M - Mn), f_new = exp2f(ms - Mn);
+      L = L * f_old + ls * f_new;
+      O.x = O.x * f_old + as.x * f_new;
+      O.y = O.y * f_old + as.y * f_new;
+      O.z = O.z * f_old + as.z * f_new;
+      O.w = O.w * f_old + as.w * f_new;
+      M = Mn;
+    }
+    *reinterpret_cast<float4*>(g.out + (((size_t)lq * g.B + b) * g.Hq + (size_t)gi * g.G + h) * g.d + c) =
+        make_float4(O.x / L, O.y / L, O.z / L, O.w / L);
   }
 }
 
@@ -1918,6 +1959,9 @@ constexpr long long kSideStreamRows = 1LL << 20;
 // Prefiltered scoring units per call (index items x units per item) up to
 // which each unit derives tau itself instead of a separate launch.
 constexpr long long kTauInlineUnits = 512;
+// Output elements per call from which the merge moves 4 per thread in
+// 16-byte vectors; below, one per thread keeps more threads in flight.
+constexpr long long kMergeVecOutputs = 1LL << 18;
 
 hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   hipError_t e;
@@ -2041,7 +2085,10 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   const long long n_out = n_att_items * g.G * g.d;
   {
     KTimer t("merge", s);
-    merge_kernel<<<clampi((n_out + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
+    if (n_out >= kMergeVecOutputs)  // 4 outputs per thread
+      merge_kernel<<<clampi((n_out / 4 + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
+    else
+      merge_scalar_kernel<<<clampi((n_out + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
   }
   return hipGetLastError();
 }
@@ -2065,7 +2112,10 @@ hipError_t launch_fac_attend(const Geo& g0, hipStream_t s) {
   const long long n_out = n_att_items * g.G * g.d;
   {
     KTimer t("merge", s);
-    merge_kernel<<<clampi((n_out + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
+    if (n_out >= kMergeVecOutputs)  // 4 outputs per thread
+      merge_kernel<<<clampi((n_out / 4 + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
+    else
+      merge_scalar_kernel<<<clampi((n_out + NT - 1) / NT, 1, g.grid), NT, 0, s>>>(g);
   }
   return hipGetLastError();
 }
