@@ -145,6 +145,10 @@ struct Vec<uint16_t> {  // bf16 bits
   }
 };
 
+// s_waitcnt immediate (gfx9 encoding) that waits for every vector memory
+// operation: vmcnt 0, expcnt and lgkmcnt at their maxima.
+constexpr int kWaitVm0 = 0x0F70;
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Streaming (read-once) 16-byte load: nontemporal, so the cache rows and the
@@ -478,50 +482,96 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
     const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * R;
     float* sc = g.scores + (size_t)item * g.Ts;
     const int t0 = ch * ct, t1 = min(g.T, t0 + ct);
-    for (int base = t0 + wave * 64; base < t1; base += NT * U) {
-      uint4 raw[U][V];
+    // the score of the token this lane keeps, from the V 16-byte pieces of a 64-token step
+    auto score = [&](const float (&kv)[V][EPV]) {
+      float mine = 0.f;
 #pragma unroll
-      for (int j = 0; j < U; ++j)
+      for (int i = 0; i < V; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) s += qr[e] * kv[i][e];
+        s = group_sum<V>(s);
+        if ((lane % V) == i) mine = s;
+      }
+      return mine;
+    };
+    auto cvt_step = [&](const uint4 (&raw)[V], float (&kv)[V][EPV]) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) Vec<E>::cvt(raw[i], kv[i]);
+    };
+    if constexpr (PF) {
+      // A ring of UR steps per wave: a step's pieces are reloaded with the step
+      // UR ahead as soon as they are converted, so (UR - 1) V loads stay in
+      // flight while a step is scored and its candidates are staged.  Steps
+      // past the end load the unit's last row (in bounds) and select nothing.
+      // The rare direct appends wait for their store, so no store is pending
+      // beside the ring's loads.
+      constexpr int UR = U;
+      const int wbase0 = t0 + wave * 64;
+      auto ld_step = [&](uint4 (&raw)[V], int base) {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-          const int tok = base + j * NT + i * (64 / V) + lane / V;
-          raw[j][i] = tok < t1 ? ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV) : make_uint4(0, 0, 0, 0);
+          const int tok = min(base + i * (64 / V) + lane / V, t1 - 1);
+          raw[i] = ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV);
         }
+      };
+      uint4 ring[UR][V];
+      // issued in ring order (the scheduler may not reorder them), so each
+      // step's wait leaves the later steps' loads in flight
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        float mine = 0.f;
+      for (int j = 0; j < UR; ++j) {
+        ld_step(ring[j], wbase0 + j * NT);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int base = wbase0; base < t1; base += NT * UR) {
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-          float kv[EPV];
-          Vec<E>::cvt(raw[j][i], kv);
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) s += qr[e] * kv[e];
-          s = group_sum<V>(s);
-          if ((lane % V) == i) mine = s;
-        }
-        const int tok = base + j * NT + (lane % V) * (64 / V) + lane / V;
-        if constexpr (PF) {
+        for (int j = 0; j < UR; ++j) {
+          const int sb = base + j * NT;
+          float kv[V][EPV];
+          cvt_step(ring[j], kv);
+          ld_step(ring[j], sb + NT * UR);
+          const float mine = score(kv);
+          const int tok = sb + (lane % V) * (64 / V) + lane / V;
           const uint32_t key = f2key(mine);
           const bool cand = tok < t1 && key >= tau;
           const uint64_t m = __ballot(cand);
           if (m) {
-            int wbase = 0;
-            if (lane == 0) wbase = atomicAdd(&s_n, __popcll(m));
-            wbase = __builtin_amdgcn_readfirstlane(wbase);
+            int wb = 0;
+            if (lane == 0) wb = atomicAdd(&s_n, __popcll(m));
+            wb = __builtin_amdgcn_readfirstlane(wb);
             if (cand) {
-              const int at = wbase + mbcnt(m);
+              const int at = wb + mbcnt(m);
               if (at < kCandUnit) {
                 s_cand[at] = make_uint2(key, (uint32_t)tok);
               } else {  // dense unit: append directly (rare)
                 const uint32_t gpos = atomicAdd(&g.info[(size_t)item * 4 + 2], 1u);
                 if (gpos < (uint32_t)g.cand_cap) g.cand[(size_t)item * g.cand_cap + gpos] = make_uint2(key, (uint32_t)tok);
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
               }
             }
           }
-        } else if (tok < t1) {
-          sc[tok] = mine;
-          atomicAdd(&s_hist[f2key(mine) >> 21], 1u);
+        }
+      }
+    } else {
+      for (int base = t0 + wave * 64; base < t1; base += NT * U) {
+        uint4 raw[U][V];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            const int tok = base + j * NT + i * (64 / V) + lane / V;
+            raw[j][i] = tok < t1 ? ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV) : make_uint4(0, 0, 0, 0);
+          }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          float kv[V][EPV];
+          cvt_step(raw[j], kv);
+          const float mine = score(kv);
+          const int tok = base + j * NT + (lane % V) * (64 / V) + lane / V;
+          if (tok < t1) {
+            sc[tok] = mine;
+            atomicAdd(&s_hist[f2key(mine) >> 21], 1u);
+          }
         }
       }
     }
@@ -534,6 +584,8 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
       uint2* cd = g.cand + (size_t)item * g.cand_cap;
       for (int i = tid; i < n; i += NT)
         if (cbase + (uint32_t)i < (uint32_t)g.cand_cap) cd[cbase + i] = s_cand[i];
+      // no store pending when the next unit's ring starts
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     } else {
       uint32_t* gh = g.hist + (size_t)item * kHistBins;
       for (int i = tid; i < kHistBins; i += NT) {
