@@ -1416,6 +1416,10 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) qr[h][c] *= kScale;
     }
+    // nothing of the unit's set-up (the query, the row indices, the last
+    // unit's partial stores) stays pending: the ring's waits then count only
+    // row loads, and registers freed by the query need no wait later
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     // pass 1: logits (log2 domain) into s_z.  A ring of AU row groups per
     // wave: each is reloaded with the group AU steps ahead as soon as it has
@@ -1481,14 +1485,18 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
         float vf[CPL];
         Vec<E>::cvt(raw[j], vf);
         raw[j] = ld16_stream(row_ptr(vb, r + kStep));
-        if (r < nrows) {
+        // rows past the end weigh 0 (no branch, so the conversion stays
+        // ahead of the reload and the ring's registers are not copied)
+        const bool live = r < nrows;
+        const int rr = live ? r : 0;
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float p = s_z[h][r];
+        for (int h = 0; h < G; ++h) {
+          const float z = s_z[h][rr];
+          const float p = live ? z : 0.f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[h][c] += p * vf[c];
-          }
+          for (int c = 0; c < CPL; ++c) acc[h][c] += p * vf[c];
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the ring order: each step waits for its own loads only
       }
     }
     // sum over the row groups of the wave (lanes LPR, 2 LPR, ... apart)
