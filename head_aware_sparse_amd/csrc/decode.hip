@@ -98,7 +98,9 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Exclusive prefix over the workgroup (NT threads) and the total.
+// Exclusive prefix over the workgroup (BT threads; s_w holds BT / 64) and the
+// total.
+template <int BT = NT>
 __device__ int block_excl_scan(int v, int* s_w, int& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   int x = v;
@@ -110,7 +112,7 @@ __device__ int block_excl_scan(int v, int* s_w, int& total) {
   if (lane == 63) s_w[wave] = x;
   __syncthreads();
   int base = 0, tot = 0;
-  for (int w = 0; w < NWAVE; ++w) {
+  for (int w = 0; w < BT / 64; ++w) {
     const int t = s_w[w];
     base += (w < wave) ? t : 0;
     tot += t;
@@ -188,15 +190,16 @@ __device__ __forceinline__ int str_pair(const Geo& g, int i) { return g.plan[4 +
 // Finds, over s_hist[0..nbins) read from the top bin down, the bin where the
 // running count first reaches `need` (1 <= need <= total).  Returns the bin
 // and the count strictly above it, identical in every thread.
+template <int BT = NT>
 __device__ void find_bin_top(const uint32_t* s_hist, int nbins, uint32_t need, int* s_w,
                              uint32_t* s_res, int& bin, uint32_t& above) {
-  const int per = nbins / NT;  // nbins is a multiple of NT
+  const int per = nbins / BT;  // nbins is a multiple of BT
   const int tid = threadIdx.x;
   const int hi = nbins - tid * per;  // this thread owns bins [hi - per, hi)
   uint32_t seg = 0;
   for (int i = 1; i <= per; ++i) seg += s_hist[hi - i];
   int total;
-  const uint32_t before = (uint32_t)block_excl_scan((int)seg, s_w, total);
+  const uint32_t before = (uint32_t)block_excl_scan<BT>((int)seg, s_w, total);
   if (before < need && need <= before + seg) {
     uint32_t run = before;
     for (int i = 1; i <= per; ++i) {
@@ -699,9 +702,9 @@ struct CandSource {
   }
 };
 
-template <class Src, class Pred, class Dig>
+template <int BT = NT, class Src, class Pred, class Dig>
 __device__ void histogram(const Src& src, uint32_t* s_hist, int nbins, Pred pred, Dig dig) {
-  for (int i = threadIdx.x; i < nbins; i += NT) s_hist[i] = 0;
+  for (int i = threadIdx.x; i < nbins; i += BT) s_hist[i] = 0;
   __syncthreads();
   src.for_each([&](uint32_t key, uint32_t tok) {
     if (pred(key, tok)) atomicAdd(&s_hist[dig(key, tok)], 1u);
@@ -713,46 +716,50 @@ __device__ void histogram(const Src& src, uint32_t* s_hist, int nbins, Pred pred
 // visits each element once, in the calling thread's strided share; reads are
 // issued four at a time so their latencies overlap.
 
-// (key, token) pairs held in LDS.
-struct LdsPairs {
+// (key, token) pairs held in LDS (BT threads).
+template <int BT = NT>
+struct LdsPairsT {
   const uint2* p;
   int n;
   template <class F>
   __device__ __forceinline__ void for_each(F f) const {
     int i = threadIdx.x;
-    for (; i + 3 * NT < n; i += 4 * NT) {
-      const uint2 a = p[i], b = p[i + NT], c = p[i + 2 * NT], d = p[i + 3 * NT];
+    for (; i + 3 * BT < n; i += 4 * BT) {
+      const uint2 a = p[i], b = p[i + BT], c = p[i + 2 * BT], d = p[i + 3 * BT];
       f(a.x, a.y);
       f(b.x, b.y);
       f(c.x, c.y);
       f(d.x, d.y);
     }
-    for (; i < n; i += NT) f(p[i].x, p[i].y);
+    for (; i < n; i += BT) f(p[i].x, p[i].y);
   }
 };
+using LdsPairs = LdsPairsT<>;
 
-// Every token of an item's score row.
-struct ScoreScan {
+// Every token of an item's score row (BT threads).
+template <int BT = NT>
+struct ScoreScanT {
   const float* sc;
   int T;
   template <class F>
   __device__ __forceinline__ void for_each(F f) const {
     int t = threadIdx.x;
-    for (; t + 3 * NT < T; t += 4 * NT) {
-      const float a = sc[t], b = sc[t + NT], c = sc[t + 2 * NT], d = sc[t + 3 * NT];
+    for (; t + 3 * BT < T; t += 4 * BT) {
+      const float a = sc[t], b = sc[t + BT], c = sc[t + 2 * BT], d = sc[t + 3 * BT];
       f(f2key(a), (uint32_t)t);
-      f(f2key(b), (uint32_t)(t + NT));
-      f(f2key(c), (uint32_t)(t + 2 * NT));
-      f(f2key(d), (uint32_t)(t + 3 * NT));
+      f(f2key(b), (uint32_t)(t + BT));
+      f(f2key(c), (uint32_t)(t + 2 * BT));
+      f(f2key(d), (uint32_t)(t + 3 * BT));
     }
-    for (; t < T; t += NT) f(f2key(sc[t]), (uint32_t)t);
+    for (; t < T; t += BT) f(f2key(sc[t]), (uint32_t)t);
   }
 };
+using ScoreScan = ScoreScanT<>;
 
 // Workgroup min and max of the keys of src (every thread gets both).
-template <class Src>
+template <int BT = NT, class Src>
 __device__ void key_range(const Src& src, uint32_t* s_res, uint32_t& lo, uint32_t& hi) {
-  __shared__ uint32_t s_lo[NWAVE], s_hi[NWAVE];
+  __shared__ uint32_t s_lo[BT / 64], s_hi[BT / 64];
   uint32_t a = 0xFFFFFFFFu, b = 0u;
   src.for_each([&](uint32_t k, uint32_t) {
     a = min(a, k);
@@ -769,7 +776,7 @@ __device__ void key_range(const Src& src, uint32_t* s_res, uint32_t& lo, uint32_
   __syncthreads();
   lo = s_lo[0];
   hi = s_hi[0];
-  for (int w = 1; w < NWAVE; ++w) {
+  for (int w = 1; w < BT / 64; ++w) {
     lo = min(lo, s_lo[w]);
     hi = max(hi, s_hi[w]);
   }
@@ -781,7 +788,7 @@ constexpr int kRankMax = 256;  // bin size resolved by direct ranking
 // The element of rank need-1 (0-based) in the order (key desc, token asc)
 // among the elements whose key satisfies ((key - lo) >> sh) == pre; there
 // are at most kRankMax of them.  Each counts the members ordered before it.
-template <class Src>
+template <int BT = NT, class Src>
 __device__ void rank_in_bin(const Src& src, uint32_t lo, int sh, uint32_t pre, uint32_t need, uint32_t* s_res,
                             uint32_t& kstar, uint32_t& tstar) {
   __shared__ uint2 s_list[kRankMax];
@@ -793,7 +800,7 @@ __device__ void rank_in_bin(const Src& src, uint32_t lo, int sh, uint32_t pre, u
   });
   __syncthreads();
   const int m = s_m;
-  for (int i = threadIdx.x; i < m; i += NT) {
+  for (int i = threadIdx.x; i < m; i += BT) {
     const uint2 me = s_list[i];
     uint32_t r = 0;
 #pragma unroll 8
@@ -820,11 +827,11 @@ __device__ void rank_in_bin(const Src& src, uint32_t lo, int sh, uint32_t pre, u
 // digits run out at key*, and the need-th smallest token among the elements
 // equal to key* follows: directly when all of them are selected, else by
 // three more 10-bit digits.
-template <class Src>
+template <int BT = NT, class Src>
 __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist, int* s_w, uint32_t* s_res,
                                 uint32_t& kstar, uint32_t& tstar) {
   uint32_t lo, hi;
-  key_range(src, s_res, lo, hi);
+  key_range<BT>(src, s_res, lo, hi);
   const uint32_t span = hi - lo;
   int rem = span ? 32 - __clz(span) : 0;  // bits of (key - lo) still open
   uint32_t pre = 0;
@@ -832,21 +839,21 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
     const int w = rem < 11 ? rem : 11;
     rem -= w;
     const int sh = rem;
-    const int nbins = (1 << w) < NT ? NT : (1 << w);
+    const int nbins = (1 << w) < BT ? BT : (1 << w);
     const uint32_t p = pre;
     const int up = sh + w;
-    histogram(src, s_hist, nbins,
+    histogram<BT>(src, s_hist, nbins,
               [=](uint32_t k, uint32_t) { return up >= 32 ? true : (((k - lo) >> up) == p); },
               [=](uint32_t k, uint32_t) { return ((k - lo) >> sh) & ((1u << w) - 1u); });
     int bin;
     uint32_t above;
-    find_bin_top(s_hist, nbins, need, s_w, s_res, bin, above);
+    find_bin_top<BT>(s_hist, nbins, need, s_w, s_res, bin, above);
     const uint32_t members = s_hist[bin];
     __syncthreads();
     need -= above;
     pre = (pre << w) | (uint32_t)bin;
     if (rem > 0 && members <= (uint32_t)kRankMax) {
-      rank_in_bin(src, lo, sh, pre, need, s_res, kstar, tstar);
+      rank_in_bin<BT>(src, lo, sh, pre, need, s_res, kstar, tstar);
       return;
     }
   }
@@ -854,7 +861,8 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
   tstar = 0;
   const uint32_t ks = kstar;
   // how many elements carry kstar, and the largest such token
-  __shared__ uint32_t s_eq[2 * NWAVE];
+  constexpr int BW = BT / 64;
+  __shared__ uint32_t s_eq[2 * BW];
   uint32_t n_eq = 0, t_max = 0;
   src.for_each([&](uint32_t k, uint32_t t) {
     if (k == ks) {
@@ -868,14 +876,14 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
   __syncthreads();
   if (lane == 0) {
     s_eq[wave] = n_eq;
-    s_eq[NWAVE + wave] = t_max;
+    s_eq[BW + wave] = t_max;
   }
   __syncthreads();
   n_eq = 0;
   t_max = 0;
-  for (int w = 0; w < NWAVE; ++w) {
+  for (int w = 0; w < BW; ++w) {
     n_eq += s_eq[w];
-    t_max = max(t_max, s_eq[NWAVE + w]);
+    t_max = max(t_max, s_eq[BW + w]);
   }
   if (need == n_eq) {
     tstar = t_max;
@@ -883,11 +891,11 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
     uint32_t tpre = 0;
     for (int shift = 20; shift >= 0; shift -= 10) {
       const uint32_t hmask = (shift == 20) ? 0u : (0xFFFFFFFFu << (shift + 10));
-      histogram(src, s_hist, 1024, [=](uint32_t k, uint32_t t) { return k == ks && (t & hmask) == tpre; },
+      histogram<BT>(src, s_hist, 1024, [=](uint32_t k, uint32_t t) { return k == ks && (t & hmask) == tpre; },
                 [=](uint32_t, uint32_t t) { return 1023u - ((t >> shift) & 0x3FFu); });
       int bin;
       uint32_t above;
-      find_bin_top(s_hist, 1024, need, s_w, s_res, bin, above);
+      find_bin_top<BT>(s_hist, 1024, need, s_w, s_res, bin, above);
       need -= above;
       tpre |= (1023u - (uint32_t)bin) << shift;
     }
@@ -1006,27 +1014,31 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
 // it always fits beside the candidates and the compacting path is compiled
 // out; LONG = true: the bitmap goes in the candidate buffer.
 constexpr int kShortMaxT = 131072;
+// One item per workgroup of kFinalThreads: the kernel's LDS admits one
+// workgroup per CU, so it brings sixteen waves.
+constexpr int kFinalThreads = 1024;
 
 template <typename E, bool LONG>
-__global__ __launch_bounds__(NT) void final_kernel(Geo g) {
+__global__ __launch_bounds__(kFinalThreads) void final_kernel(Geo g) {
+  constexpr int BT = kFinalThreads, BW = BT / 64;
   // candidates; for LONG, later the selected tokens, the bitmap and the prefix counts
   __shared__ __attribute__((aligned(16))) uint2 s_c[kCandFast];
   __shared__ __attribute__((aligned(16))) uint32_t s_bm[LONG ? 4 : kShortMaxT / 32];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
   __shared__ float s_q[kMaxR];
-  __shared__ int s_w[NWAVE];
+  __shared__ int s_w[BW];
   __shared__ uint32_t s_res[2];
   __shared__ uint2 s_list[kRankMax];
   __shared__ int s_m;
   // !LONG: the prefix counts (u16) reuse the histogram, free by then
   static_assert(kHistBins * sizeof(uint32_t) >= kShortMaxT / 32 * sizeof(uint16_t), "u16 prefixes in s_hist");
   // bitmap words per thread for the prefix counts: a multiple of 4 (16-byte
-  // reads), so the bitmap spans NT * per words
-  const int per = ((g.bm_words + NT - 1) / NT + 3) & ~3;
+  // reads), so the bitmap spans BT * per words
+  const int per = ((g.bm_words + BT - 1) / BT + 3) & ~3;
   constexpr int kSelWords = (kCandFast / 3 + 63) / 64 * 64;  // n_fac <= kCandFast / 3 on this path
-  constexpr int kPerMax = (kPrefilterMaxT / 32 / NT + 3) & ~3;
-  static_assert(kCandFast * sizeof(uint2) >= (kSelWords + NT * kPerMax) * sizeof(uint32_t) +
-                                                 NT * kPerMax * sizeof(uint16_t),
+  constexpr int kPerMax = (kPrefilterMaxT / 32 / BT + 3) & ~3;
+  static_assert(kCandFast * sizeof(uint2) >= (kSelWords + BT * kPerMax) * sizeof(uint32_t) +
+                                                 BT * kPerMax * sizeof(uint16_t),
                 "selected tokens, bitmap and u16 prefixes fit the candidate buffer");
   static_assert(kCandFast / 3 < 65536, "prefiltered n_fac fits u16 prefixes");
   const int tid = threadIdx.x;
@@ -1035,16 +1047,16 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
     __syncthreads();
     const uint32_t count = g.info[(size_t)item * 4 + 2];
     const uint2 th = g.tau[item];
-    for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+    for (int i = tid; i < kHistBins; i += BT) s_hist[i] = 0u;
     if (tid == 0) s_m = 0;
     const int pidx = item / g.B, b = item - pidx * g.B;
     const int pair = idx_pair(g, pidx);
     const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
     int32_t* ix = g.idx + (size_t)item * g.n_fac;
     int32_t* ox = g.idx_out ? g.idx_out + (((size_t)l * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
-    // bitmap of NT * per words at bm, u16 prefix counts after it
+    // bitmap of BT * per words at bm, u16 prefix counts after it
     auto clear_bitmap = [&](uint32_t* bm) {
-      for (int w = tid; w < NT * per; w += NT) bm[w] = 0u;
+      for (int w = tid; w < BT * per; w += BT) bm[w] = 0u;
     };
     // exclusive prefix counts of the set bits, one u16 per bitmap word
     // (< n_fac < 2^16).  Each wave scans a contiguous quarter of the bitmap,
@@ -1052,7 +1064,7 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
     // conflict-free; a first pass sums the quarters for the wave offsets.
     auto prefix = [&](const uint32_t* bm, uint16_t* pre) {
       const int lane = tid & 63, wave = tid >> 6;
-      const int qw = NT * per / NWAVE;  // a multiple of 64 (per is a multiple of 4)
+      const int qw = BT * per / BW;  // a multiple of 64 (per is a multiple of 4)
       const uint32_t* wb = bm + wave * qw;
       uint16_t* wp = pre + wave * qw;
       uint32_t tot = 0;
@@ -1087,22 +1099,22 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
       // selected tokens are compacted first and the bitmap built behind them
       const int cand_words = ((int)count * 2 + 3) & ~3;
       const bool direct =
-          !LONG || (size_t)(cand_words + NT * per) * 4 + (size_t)NT * per * 2 <= sizeof(s_c);
+          !LONG || (size_t)(cand_words + BT * per) * 4 + (size_t)BT * per * 2 <= sizeof(s_c);
       uint32_t* bm = !LONG ? s_bm : reinterpret_cast<uint32_t*>(s_c) + (direct ? cand_words : kSelWords);
-      uint16_t* pre = !LONG ? reinterpret_cast<uint16_t*>(s_hist) : reinterpret_cast<uint16_t*>(bm + NT * per);
+      uint16_t* pre = !LONG ? reinterpret_cast<uint16_t*>(s_hist) : reinterpret_cast<uint16_t*>(bm + BT * per);
       if (direct) clear_bitmap(bm);
       __syncthreads();
       // candidates -> LDS, two per 16-byte load, eight loads in flight,
       // counted by their first digit on the way
       const uint4* c4 = reinterpret_cast<const uint4*>(g.cand + (size_t)item * g.cand_cap);
       const int n4 = (int)(count + 1) / 2;
-      for (int i0 = tid; i0 < n4; i0 += 8 * NT) {
+      for (int i0 = tid; i0 < n4; i0 += 8 * BT) {
         uint4 r[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = i0 + j * NT < n4 ? c4[i0 + j * NT] : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < 8; ++j) r[j] = i0 + j * BT < n4 ? c4[i0 + j * BT] : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int i = i0 + j * NT;
+          const int i = i0 + j * BT;
           if (i < n4) {
             s_c[2 * i] = make_uint2(r[j].x, r[j].y);
             atomicAdd(&s_hist[min((r[j].x - tau) >> sh, (uint32_t)kHistBins - 1u)], 1u);
@@ -1114,11 +1126,11 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
         }
       }
       __syncthreads();
-      const LdsPairs src{s_c, (int)count};
+      const LdsPairsT<BT> src{s_c, (int)count};
       auto mark = [&](uint32_t t) { atomicOr(&bm[t >> 5], 1u << (t & 31)); };
       int bin;
       uint32_t above;
-      find_bin_top(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, bin, above);
+      find_bin_top<BT>(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, bin, above);
       const uint32_t members = s_hist[bin];
       __syncthreads();
       uint32_t kstar = 0, tstar = 0;
@@ -1138,7 +1150,7 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
         __syncthreads();
         const uint32_t need = (uint32_t)g.n_fac - above;
         const int m = s_m;
-        for (int i = tid; i < m; i += NT) {
+        for (int i = tid; i < m; i += BT) {
           const uint2 me = s_list[i];
           uint32_t r = 0;
 #pragma unroll 8
@@ -1156,7 +1168,7 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
         kstar = s_res[0];
         tstar = s_res[1];
       } else {
-        exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+        exact_threshold<BT>(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
         if (direct)
           src.for_each([&](uint32_t k, uint32_t t) {
             if (k > kstar || (k == kstar && t <= tstar)) mark(t);
@@ -1172,24 +1184,24 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
         __syncthreads();
         if (tid == 0) s_m = 0;
         __syncthreads();
-        for (int c0 = 0; c0 < (int)count; c0 += 8 * NT) {
+        for (int c0 = 0; c0 < (int)count; c0 += 8 * BT) {
           uint2 r[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const int i = c0 + j * NT + tid;
+            const int i = c0 + j * BT + tid;
             r[j] = i < (int)count ? s_c[i] : make_uint2(0u, 0xFFFFFFFFu);
           }
           __syncthreads();
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if (c0 + j * NT + tid < (int)count && (r[j].x > kstar || (r[j].x == kstar && r[j].y <= tstar)))
+            if (c0 + j * BT + tid < (int)count && (r[j].x > kstar || (r[j].x == kstar && r[j].y <= tstar)))
               s_sel[atomicAdd(&s_m, 1)] = r[j].y;
           __syncthreads();
         }
         n_sel = min(s_m, g.n_fac);  // == n_fac
         clear_bitmap(bm);
         __syncthreads();
-        for (int i = tid; i < n_sel; i += NT) mark(s_sel[i]);
+        for (int i = tid; i < n_sel; i += BT) mark(s_sel[i]);
       }
       __syncthreads();
       prefix(bm, pre);
@@ -1199,21 +1211,21 @@ __global__ __launch_bounds__(NT) void final_kernel(Geo g) {
           if (bm[t >> 5] & (1u << (t & 31))) put(bm, pre, t);
         });
       } else {
-        for (int i = tid; i < n_sel; i += NT) put(bm, pre, s_sel[i]);
+        for (int i = tid; i < n_sel; i += BT) put(bm, pre, s_sel[i]);
       }
     } else {
       const size_t slice = group_query_dom<E>(g, item, s_q);
       __syncthreads();
       const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * g.R;
       float* sc = g.scores + (size_t)item * g.Ts;
-      for (int t = tid; t < g.T; t += NT) sc[t] = score_one<E>(kd + (size_t)t * g.R, s_q, g.R);
+      for (int t = tid; t < g.T; t += BT) sc[t] = score_one<E>(kd + (size_t)t * g.R, s_q, g.R);
       __threadfence();
       __syncthreads();
-      const ScoreScan src{sc, g.T};
+      const ScoreScanT<BT> src{sc, g.T};
       uint32_t kstar, tstar;
-      exact_threshold(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+      exact_threshold<BT>(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
       uint32_t* bm = !LONG ? s_bm : reinterpret_cast<uint32_t*>(s_c);
-      uint16_t* pre = !LONG ? reinterpret_cast<uint16_t*>(s_hist) : reinterpret_cast<uint16_t*>(bm + NT * per);
+      uint16_t* pre = !LONG ? reinterpret_cast<uint16_t*>(s_hist) : reinterpret_cast<uint16_t*>(bm + BT * per);
       clear_bitmap(bm);
       __syncthreads();
       src.for_each([&](uint32_t k, uint32_t t) {
@@ -2086,11 +2098,11 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     {
       KTimer t("select_final", s);
       if (g.T <= kShortMaxT) {
-        if (g.bf16) final_kernel<uint16_t, false><<<grid_item, NT, 0, s>>>(g);
-        else final_kernel<float, false><<<grid_item, NT, 0, s>>>(g);
+        if (g.bf16) final_kernel<uint16_t, false><<<grid_item, kFinalThreads, 0, s>>>(g);
+        else final_kernel<float, false><<<grid_item, kFinalThreads, 0, s>>>(g);
       } else {
-        if (g.bf16) final_kernel<uint16_t, true><<<grid_item, NT, 0, s>>>(g);
-        else final_kernel<float, true><<<grid_item, NT, 0, s>>>(g);
+        if (g.bf16) final_kernel<uint16_t, true><<<grid_item, kFinalThreads, 0, s>>>(g);
+        else final_kernel<float, true><<<grid_item, kFinalThreads, 0, s>>>(g);
       }
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
