@@ -2041,7 +2041,13 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   Geo g = g0;
   const long long n_idx_items = (long long)(g.clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att_items = (long long)g.Lq * g.Hkv * g.B;
-  const int grid_plan = clampi((n_idx_items * kHistBins / 4 + NT - 1) / NT, 1, g.grid);
+  // the plan launch clears per-item histograms (general path) or counters
+  // (prefiltered) and fills the -1 index rows of streaming groups; its grid
+  // covers that work, no more
+  const long long plan_work =
+      g.prefilter ? std::max(n_idx_items, g.idx_out && !g.clsa ? (long long)g.Lq * g.B * g.Hkv * g.n_fac : 0LL)
+                  : n_idx_items * kHistBins / 4;
+  const int grid_plan = clampi((plan_work + NT - 1) / NT, 1, g.grid);
   const bool any_stream = !(g.clsa && g.labels == nullptr);
   const bool side = any_stream && (long long)n_att_items * g.n_srows >= kSideStreamRows;
   // Without the side stream (which forks right after the plan), the sampling
