@@ -1657,6 +1657,7 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_v[ROWS][kClsaPad];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[32][kClsaPad];
   __shared__ float s_ml[32][2];
+  __shared__ uint8_t s_lab[32];  // per query vector: its layer attends (retrieval label)
   uint16_t (*s_k)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(s_kp);
   float (*s_p)[kPPad] = reinterpret_cast<float (*)[kPPad]>(s_kp);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1673,37 +1674,47 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
     const uint16_t* kb = (const uint16_t*)g.k + kvs * (size_t)g.T * D;
     const uint16_t* vb = (const uint16_t*)g.v + kvs * (size_t)g.T * D;
     __syncthreads();
-    // gather rows (16 bytes per element e = row * 16 + part), zero padding rows
-    for (int e0 = tid; e0 < ROWS * 16; e0 += 8 * NT) {
-      uint4 rk[8], rv[8];
+    // Query vectors qv = n * G + h first (zero rows past QV), then the row
+    // indices, then every K and V element of the tile (16 bytes per element
+    // e = row * 16 + part): all loads are unconditional (rows past the end
+    // and query rows past QV read the last valid one, then store zeros), so
+    // each group is issued whole and the three latencies are paid once each.
+    static_assert(32 * 16 == 2 * NT, "two query elements per thread");
+    static_assert(ROWS * 16 == 8 * NT, "eight tile elements per thread");
+    uint4 qreg[2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * NT, r = e >> 4;
-        rk[u] = rv[u] = make_uint4(0, 0, 0, 0);
-        if (r < nrows) {
-          // indices come from the selection and lie in [0, T); the clamp only
-          // keeps a corrupted workspace from turning into out-of-range reads
-          const int row = min(max(ix[r], 0), g.T - 1);
-          rk[u] = ld16_stream(kb + (size_t)row * D + (e & 15) * 8);
-          rv[u] = ld16_stream(vb + (size_t)row * D + (e & 15) * 8);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * NT, r = e >> 4;
-        *reinterpret_cast<uint4*>(&s_k[r][(e & 15) * 8]) = rk[u];
-        *reinterpret_cast<uint4*>(&s_v[r][(e & 15) * 8]) = rv[u];
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + i * NT, qv = min(e >> 4, QV - 1), part = e & 15;
+      const int n = qv / g.G, h = qv - n * g.G;
+      qreg[i] = ld16((const uint16_t*)g.q + (((size_t)n * g.B + b) * g.Hq + (size_t)gi * g.G + h) * D + part * 8);
     }
-    // query vectors qv = n * G + h (zero rows past QV)
-    for (int e = tid; e < 32 * 16; e += NT) {
-      const int qv = e >> 4, part = e & 15;
-      uint4 v4 = make_uint4(0, 0, 0, 0);
-      if (qv < QV) {
-        const int n = qv / g.G, h = qv - n * g.G;
-        v4 = ld16((const uint16_t*)g.q + (((size_t)n * g.B + b) * g.Hq + (size_t)gi * g.G + h) * D + part * 8);
-      }
-      *reinterpret_cast<uint4*>(&s_q[qv][part * 8]) = v4;
+    int rowi[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // indices come from the selection and lie in [0, T); the clamp only
+      // keeps a corrupted workspace from turning into out-of-range reads
+      const int r = min((tid + u * NT) >> 4, nrows - 1);
+      rowi[u] = min(max(ix[r], 0), g.T - 1);
+    }
+    uint4 rk[8], rv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + u * NT;
+      rk[u] = ld16_stream(kb + (size_t)rowi[u] * D + (e & 15) * 8);
+      rv[u] = ld16_stream(vb + (size_t)rowi[u] * D + (e & 15) * 8);
+    }
+    if (tid < 32) s_lab[tid] = tid < QV ? (uint8_t)label_at(g, (tid / g.G) * g.Hkv + gi) : (uint8_t)0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + i * NT;
+      *reinterpret_cast<uint4*>(&s_q[e >> 4][(e & 15) * 8]) = (e >> 4) < QV ? qreg[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + u * NT, r = e >> 4;
+      const bool live = r < nrows;
+      *reinterpret_cast<uint4*>(&s_k[r][(e & 15) * 8]) = live ? rk[u] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&s_v[r][(e & 15) * 8]) = live ? rv[u] : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
     // S = Q K^T for row block `wave`, then (the K tile being free) into s_p
@@ -1789,23 +1800,19 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qv = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (qv < QV) {
+        if (s_lab[qv]) {  // 0 past QV
           const int n = qv / g.G, h = qv - n * g.G;
-          if (label_at(g, n * g.Hkv + gi)) {
-            const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
-            g.part[(((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4) + dcol] = o[r];
-          }
+          const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
+          g.part[(((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4) + dcol] = o[r];
         }
       }
     }
-    if (tid < QV) {
+    if (tid < QV && s_lab[tid]) {
       const int n = tid / g.G, h = tid - n * g.G;
-      if (label_at(g, n * g.Hkv + gi)) {
-        const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
-        float* pp = g.part + (((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4);
-        pp[D] = s_ml[tid][0];
-        pp[D + 1] = s_ml[tid][1];
-      }
+      const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
+      float* pp = g.part + (((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4);
+      pp[D] = s_ml[tid][0];
+      pp[D + 1] = s_ml[tid][1];
     }
   }
 }
