@@ -50,8 +50,10 @@ def algorithmic_bytes(cfg, labels, per_layer_gather=False, per_head=False):
     channels of retrieval items, selected K+V rows, sink+window K+V rows,
     queries and outputs.  Scores, histograms and partials are not counted.
     per_layer_gather: the shared index is attended layer by layer, each layer
-    gathering the selected rows again.  per_head: every query head scores and
-    gathers for itself (G times the rows of a retrieval group)."""
+    gathering the selected rows again.  per_head: every query head selects
+    and gathers for itself (G times the selected rows of a retrieval group);
+    the group's dominant key channels are still needed once, as its G heads
+    score against the same rows."""
     import numpy as np
     es = 2 if cfg.bf16 else 4
     d, T = cfg.d_head, cfg.ctx_len
@@ -71,7 +73,7 @@ def algorithmic_bytes(cfg, labels, per_layer_gather=False, per_head=False):
         n_ret = int(np.asarray(labels).sum()) * cfg.batch
         n_str = cfg.n_layers * cfg.batch * cfg.n_kv_heads - n_ret
         rep = cfg.n_q_heads // cfg.n_kv_heads if per_head else 1
-        tip = rep * n_ret * T * 2 * cfg.n_dom * es
+        tip = n_ret * T * 2 * cfg.n_dom * es
         gather = rep * n_ret * cfg.n_fac * row
         stream = n_str * n_srows * row
     qo = cfg.n_layers * cfg.batch * cfg.n_q_heads * d * (es + 4)

@@ -124,6 +124,7 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   g.tstride = d->ctx_len;
   g.kv_shift = 0;
   g.hkv_kv = g.Hkv;
+  g.sgrp = 1;
   const long long n_idx = (long long)(clsa ? g.Hkv : g.Lq * g.Hkv) * g.B;
   const long long n_att = (long long)g.Lq * g.Hkv * g.B;
   // Score chunks: aim for ~1024 units over the worst-case item count.

@@ -431,72 +431,90 @@ __global__ __launch_bounds__(NT) void tau_kernel(Geo g) {
 // from tau_kernel; 2: prefiltered, each unit derives tau from the sampled
 // keys itself (steps with few index items, where a separate launch costs
 // more than the redundant work), unit 0 of the item storing it.
-template <typename E, int V, int MODE>
+// HG > 1 (prefiltered with a tau launch, per-query-head selection): the HG
+// index items of one KV group's heads share a unit, so the group's dominant
+// key rows are read once and scored against HG queries, each head with its
+// own threshold and candidate list.
+template <typename E, int V, int MODE, int HG = 1>
 __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
   constexpr bool PF = MODE != 0;
+  static_assert(HG == 1 || MODE == 1, "heads share units only with a tau launch");
   constexpr int EPV = Vec<E>::N;
   constexpr int U = V >= 8 ? 2 : 16 / V;  // 64-token steps in flight per wave (16 loads per lane)
   __shared__ uint32_t s_hist[PF ? 1 : kHistBins];
-  constexpr int kCandUnit = 2048;  // candidates staged in LDS per unit; the rest go straight out
-  __shared__ uint2 s_cand[PF ? kCandUnit : 1];
+  // candidates staged in LDS per unit and head; the rest go straight out
+  constexpr int kCandUnit = HG == 1 ? 2048 : 1536;
+  __shared__ uint2 s_cand[PF ? HG : 1][PF ? kCandUnit : 1];
   __shared__ float s_q[V * EPV];
-  __shared__ int s_n;
-  __shared__ uint32_t s_base;
+  __shared__ int s_n[HG];
+  __shared__ uint32_t s_base[HG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = PF ? g.nch_tip : g.nch_t;
   const int ct = PF ? g.ct_tip : g.ct;
-  const int n_units = n_idx_pairs(g) * g.B * nch;
+  const int n_units = n_idx_pairs(g) / HG * g.B * nch;
   if constexpr (!PF)
     for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0;
   const int R = V * EPV;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int item = u / nch, ch = u - item * nch;
+    const int unit_item = u / nch, ch = u - unit_item * nch;
     __syncthreads();
-    float qr[EPV];
+    float qr[HG][EPV];
+    int item[HG];  // index items of the unit (the heads' items when HG > 1)
     size_t slice;
-    uint32_t tau = 0u;
+    uint32_t tau[HG];
     if constexpr (PF) {
-      // the sample pass stored the group query; each lane reads its slice
-      const int pidx = item / g.B, b = item - pidx * g.B;
-      const int pair = idx_pair(g, pidx);
+      // the sample pass stored each item's group query; each lane reads its slice
+      const int pg = unit_item / g.B, b = unit_item - pg * g.B;
+      const int pidx0 = pg * HG;  // the heads of a KV group are consecutive index pairs
+      const int pair = idx_pair(g, pidx0);
       const int l = pair / g.Hkv, gi = pair - l * g.Hkv;
-      slice = g.split ? (size_t)pidx * g.B + b : kv_slice(g, l, b, gi);
-      const float* qb = g.qbar + (size_t)item * R + (lane % V) * EPV;
+      slice = g.split ? (size_t)pidx0 * g.B + b : kv_slice(g, l, b, gi);
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) qr[e] = qb[e];
+      for (int h = 0; h < HG; ++h) {
+        item[h] = (pidx0 + h) * g.B + b;
+        const float* qb = g.qbar + (size_t)item[h] * R + (lane % V) * EPV;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) qr[h][e] = qb[e];
+      }
       if constexpr (MODE == 2) {
         __shared__ int s_w2[2 * NWAVE];
         __shared__ uint32_t s_res2[2];
         static_assert(kCandUnit * sizeof(uint2) >= kHistBins * sizeof(uint32_t), "tau histogram in s_cand");
-        const uint2 t2 = item_tau(g, item, reinterpret_cast<uint32_t*>(s_cand), s_w2, s_res2);
-        tau = t2.x;
-        if (ch == 0 && tid == 0) g.tau[item] = t2;  // for the final kernel
+        const uint2 t2 = item_tau(g, item[0], reinterpret_cast<uint32_t*>(&s_cand[0][0]), s_w2, s_res2);
+        tau[0] = t2.x;
+        if (ch == 0 && tid == 0) g.tau[item[0]] = t2;  // for the final kernel
       } else {
-        tau = g.tau[item].x;
+#pragma unroll
+        for (int h = 0; h < HG; ++h) tau[h] = g.tau[item[h]].x;
       }
-      if (tid == 0) s_n = 0;
+      if (tid < HG) s_n[tid] = 0;
       __syncthreads();
     } else {
-      slice = group_query_dom<E>(g, item, s_q);
+      item[0] = unit_item;
+      tau[0] = 0u;
+      slice = group_query_dom<E>(g, unit_item, s_q);
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
+      for (int e = 0; e < EPV; ++e) qr[0][e] = s_q[(lane % V) * EPV + e];
     }
     const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * R;
-    float* sc = g.scores + (size_t)item * g.Ts;
+    float* sc = g.scores + (size_t)item[0] * g.Ts;
     const int t0 = ch * ct, t1 = min(g.T, t0 + ct);
-    // the score of the token this lane keeps, from the V 16-byte pieces of a 64-token step
-    auto score = [&](const float (&kv)[V][EPV]) {
-      float mine = 0.f;
+    // the scores (one per head) of the token this lane keeps, from the V
+    // 16-byte pieces of a 64-token step
+    auto score = [&](const float (&kv)[V][EPV], float (&mine)[HG]) {
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        float s = 0.f;
+      for (int h = 0; h < HG; ++h) mine[h] = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) s += qr[e] * kv[i][e];
-        s = group_sum<V>(s);
-        if ((lane % V) == i) mine = s;
-      }
-      return mine;
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int h = 0; h < HG; ++h) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) s += qr[h][e] * kv[i][e];
+          s = group_sum<V>(s);
+          if ((lane % V) == i) mine[h] = s;
+        }
     };
     auto cvt_step = [&](const uint4 (&raw)[V], float (&kv)[V][EPV]) {
 #pragma unroll
@@ -533,23 +551,28 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
           float kv[V][EPV];
           cvt_step(ring[j], kv);
           ld_step(ring[j], sb + NT * UR);
-          const float mine = score(kv);
+          float mine[HG];
+          score(kv, mine);
           const int tok = sb + (lane % V) * (64 / V) + lane / V;
-          const uint32_t key = f2key(mine);
-          const bool cand = tok < t1 && key >= tau;
-          const uint64_t m = __ballot(cand);
-          if (m) {
-            int wb = 0;
-            if (lane == 0) wb = atomicAdd(&s_n, __popcll(m));
-            wb = __builtin_amdgcn_readfirstlane(wb);
-            if (cand) {
-              const int at = wb + mbcnt(m);
-              if (at < kCandUnit) {
-                s_cand[at] = make_uint2(key, (uint32_t)tok);
-              } else {  // dense unit: append directly (rare)
-                const uint32_t gpos = atomicAdd(&g.info[(size_t)item * 4 + 2], 1u);
-                if (gpos < (uint32_t)g.cand_cap) g.cand[(size_t)item * g.cand_cap + gpos] = make_uint2(key, (uint32_t)tok);
-                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+          for (int h = 0; h < HG; ++h) {
+            const uint32_t key = f2key(mine[h]);
+            const bool cand = tok < t1 && key >= tau[h];
+            const uint64_t m = __ballot(cand);
+            if (m) {
+              int wb = 0;
+              if (lane == 0) wb = atomicAdd(&s_n[h], __popcll(m));
+              wb = __builtin_amdgcn_readfirstlane(wb);
+              if (cand) {
+                const int at = wb + mbcnt(m);
+                if (at < kCandUnit) {
+                  s_cand[h][at] = make_uint2(key, (uint32_t)tok);
+                } else {  // dense unit: append directly (rare)
+                  const uint32_t gpos = atomicAdd(&g.info[(size_t)item[h] * 4 + 2], 1u);
+                  if (gpos < (uint32_t)g.cand_cap)
+                    g.cand[(size_t)item[h] * g.cand_cap + gpos] = make_uint2(key, (uint32_t)tok);
+                  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                }
               }
             }
           }
@@ -569,28 +592,32 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
         for (int j = 0; j < U; ++j) {
           float kv[V][EPV];
           cvt_step(raw[j], kv);
-          const float mine = score(kv);
+          float mine[HG];
+          score(kv, mine);
           const int tok = base + j * NT + (lane % V) * (64 / V) + lane / V;
           if (tok < t1) {
-            sc[tok] = mine;
-            atomicAdd(&s_hist[f2key(mine) >> 21], 1u);
+            sc[tok] = mine[0];
+            atomicAdd(&s_hist[f2key(mine[0]) >> 21], 1u);
           }
         }
       }
     }
     __syncthreads();
     if constexpr (PF) {
-      const int n = min(s_n, kCandUnit);
-      if (tid == 0) s_base = atomicAdd(&g.info[(size_t)item * 4 + 2], (uint32_t)n);
+      if (tid < HG) s_base[tid] = atomicAdd(&g.info[(size_t)item[tid] * 4 + 2], (uint32_t)min(s_n[tid], kCandUnit));
       __syncthreads();
-      const uint32_t cbase = s_base;
-      uint2* cd = g.cand + (size_t)item * g.cand_cap;
-      for (int i = tid; i < n; i += NT)
-        if (cbase + (uint32_t)i < (uint32_t)g.cand_cap) cd[cbase + i] = s_cand[i];
+#pragma unroll
+      for (int h = 0; h < HG; ++h) {
+        const int n = min(s_n[h], kCandUnit);
+        const uint32_t cbase = s_base[h];
+        uint2* cd = g.cand + (size_t)item[h] * g.cand_cap;
+        for (int i = tid; i < n; i += NT)
+          if (cbase + (uint32_t)i < (uint32_t)g.cand_cap) cd[cbase + i] = s_cand[h][i];
+      }
       // no store pending when the next unit's ring starts
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     } else {
-      uint32_t* gh = g.hist + (size_t)item * kHistBins;
+      uint32_t* gh = g.hist + (size_t)item[0] * kHistBins;
       for (int i = tid; i < kHistBins; i += NT) {
         const uint32_t c = s_hist[i];
         if (c) {
@@ -1383,8 +1410,11 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
   __shared__ float s_ml[G][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane % LPR, rsub = lane / LPR;
+  // sgrp > 1 (per-head selection): a streaming unit serves the sgrp = G
+  // consecutive head pairs of one KV group (G here is that group size, the
+  // index groups hold one head each), so the group's rows are read once
   const int n_ret = g.attn_mode == 2 ? 0 : n_ret_pairs(g);
-  const int n_str = g.attn_mode == 1 ? 0 : n_str_pairs(g);
+  const int n_str = g.attn_mode == 1 ? 0 : n_str_pairs(g) / g.sgrp;
   const int n_fac_units = n_ret * g.B * g.nch_f;
   const int n_units = n_fac_units + n_str * g.B * g.nch_s;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
@@ -1393,12 +1423,12 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
     const int nchunk = fac ? g.nch_f : g.nch_s;
     const int item = uu / nchunk, chunk = uu - item * nchunk;
     const int pa = item / g.B, b = item - pa * g.B;
-    const int pair = fac ? ret_pair(g, pa) : str_pair(g, pa);
+    const int pair = fac ? ret_pair(g, pa) : str_pair(g, pa * g.sgrp);
     const int lq = pair / g.Hkv, gi = pair - lq * g.Hkv;
     const int lkv = g.clsa ? 0 : lq;
     // split cache: slab = list position x B + b, a streaming group's rows in its ring
     const bool ring = g.split && !fac;
-    const size_t kvs = g.split ? (size_t)pa * g.B + b : kv_slice(g, lkv, b, gi);
+    const size_t kvs = g.split ? (size_t)(pa * (fac ? 1 : g.sgrp)) * g.B + b : kv_slice(g, lkv, b, gi);
     const size_t rows_per = ring ? (size_t)g.scap : (size_t)g.tstride;
     const E* kb = (const E*)(ring ? g.k_str : g.k) + kvs * rows_per * D;
     const E* vb = (const E*)(ring ? g.v_str : g.v) + kvs * rows_per * D;
@@ -1421,7 +1451,9 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
       }
     }
     float qr[G][CPL];
-    const E* qp = (const E*)g.q + (((size_t)lq * g.B + b) * g.Hq + (size_t)gi * G) * D + slot * CPL;
+    // the unit's first query head: index groups of G heads, or of one head each (sgrp > 1)
+    const int qh0 = g.sgrp > 1 ? gi : gi * G;
+    const E* qp = (const E*)g.q + (((size_t)lq * g.B + b) * g.Hq + (size_t)qh0) * D + slot * CPL;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       Vec<E>::cvt(ld16(qp + (size_t)h * D), qr[h]);
@@ -1530,18 +1562,22 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
         for (int c = 0; c < CPL; ++c) s_red[wave][h][slot * CPL + c] = acc[h][c];
     }
     __syncthreads();
+    // head h's partial: item a + h / g.G (heads past an index group's g.G
+    // belong to the next item when sgrp > 1), slot h % g.G
     const size_t a = ((size_t)lq * g.B + b) * g.Hkv + gi;
-    float* pp = g.part + ((a * g.nparts + chunk) * G) * (size_t)(D + 4);
+    auto part_of = [&](int h) {
+      return g.part + (((a + (size_t)(h / g.G)) * g.nparts + chunk) * g.G + (size_t)(h % g.G)) * (size_t)(D + 4);
+    };
     for (int e = tid; e < G * D; e += NT) {
       const int h = e / D, c = e - h * D;
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < NWAVE; ++w) s += s_red[w][h][c];
-      pp[(size_t)h * (D + 4) + c] = s;
+      part_of(h)[c] = s;
     }
     if (tid < G) {
-      pp[(size_t)tid * (D + 4) + D] = s_ml[tid][0];
-      pp[(size_t)tid * (D + 4) + D + 1] = s_ml[tid][1];
+      part_of(tid)[D] = s_ml[tid][0];
+      part_of(tid)[D + 1] = s_ml[tid][1];
     }
   }
 }
@@ -1880,7 +1916,7 @@ __global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd
 
 template <typename E, int D>
 hipError_t launch_attn_g(const Geo& g, int grid, hipStream_t s) {
-  switch (g.G) {
+  switch (g.G * g.sgrp) {
     case 1: attn_kernel<E, D, 1><<<grid, NT, 0, s>>>(g); break;
     case 2: attn_kernel<E, D, 2><<<grid, NT, 0, s>>>(g); break;
     case 4: attn_kernel<E, D, 4><<<grid, NT, 0, s>>>(g); break;
@@ -1905,6 +1941,19 @@ hipError_t launch_tip_v(const Geo& g, int grid, hipStream_t s) {
     case 4: tip_kernel<E, 4, MODE><<<grid, NT, 0, s>>>(g); break;
     case 8: tip_kernel<E, 8, MODE><<<grid, NT, 0, s>>>(g); break;
     case 16: tip_kernel<E, 16, MODE><<<grid, NT, 0, s>>>(g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Prefiltered scoring with a tau launch when every query head selects its
+// own tokens: the hg heads of a KV group share each unit (bf16 caches).
+template <int V>
+hipError_t launch_tip_heads(const Geo& g, int hg, int grid, hipStream_t s) {
+  switch (hg) {
+    case 2: tip_kernel<uint16_t, V, 1, 2><<<grid, NT, 0, s>>>(g); break;
+    case 4: tip_kernel<uint16_t, V, 1, 4><<<grid, NT, 0, s>>>(g); break;
+    case 8: tip_kernel<uint16_t, V, 1, 8><<<grid, NT, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -2076,7 +2125,8 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     {
       Geo gs = g;
       gs.attn_mode = 2;
-      const int grid_s = clampi(n_att_items * (long long)g.nch_s, 1, g.grid);
+      gs.sgrp = 1 << g.kv_shift;  // per-head selection: the group's heads share its rows
+      const int grid_s = clampi(n_att_items / gs.sgrp * (long long)g.nch_s, 1, g.grid);
       KTimer t("attention_stream", ss.side);
       e = launch_attn(gs, grid_s, ss.side);
     }
@@ -2100,9 +2150,15 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
-      const int grid_tip_pf = clampi(n_idx_items * g.nch_tip, 1, g.grid);
+      const int hg = 1 << g.kv_shift;
+      const int V = g.R * (g.bf16 ? 2 : 4) / 16;
+      const bool share = !tau_inline && hg > 1 && g.bf16 && (V == 2 || V == 4 || V == 8);
+      const int grid_tip_pf = clampi(n_idx_items / (share ? hg : 1) * g.nch_tip, 1, g.grid);
       KTimer t("tip_score", s);
-      if (tau_inline)
+      if (share)
+        e = V == 2 ? launch_tip_heads<2>(g, hg, grid_tip_pf, s)
+                   : V == 4 ? launch_tip_heads<4>(g, hg, grid_tip_pf, s) : launch_tip_heads<8>(g, hg, grid_tip_pf, s);
+      else if (tau_inline)
         e = g.bf16 ? launch_tip_v<uint16_t, 2>(g, grid_tip_pf, s) : launch_tip_v<float, 2>(g, grid_tip_pf, s);
       else
         e = g.bf16 ? launch_tip_v<uint16_t, 1>(g, grid_tip_pf, s) : launch_tip_v<float, 1>(g, grid_tip_pf, s);

@@ -46,6 +46,7 @@ struct Geo {
   int tstride;      // rows per cache (and k_dom) slab: T, or the split cache's capacity
   int scap;         // split cache: rows per streaming ring slab (n_sink + window)
   int kv_shift;     // log2(index groups per KV group): 0, or log2 G when every query head selects its own tokens
+  int sgrp;         // query heads per streaming attention unit beyond G: with kv_shift > 0, the KV group's heads (1 otherwise)
   int hkv_kv;       // KV groups per layer (Hkv >> kv_shift)
   // workspace
   int* plan;         // [4 + 3*kMaxPairs]: n_idx_pairs, n_att_ret, n_att_str, -, lists

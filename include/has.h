@@ -173,8 +173,10 @@ has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const 
  * (ties to the lower t) and attends over them; streaming groups as in
  * sparse_decode_step.  Arguments as in sparse_decode_step except idx_out
  * [n_layers,batch,n_q_heads,n_fac] (-1 rows for heads of streaming groups),
- * and n_layers * n_q_heads <= 8192.  It scores and gathers G times the rows
- * of sparse_decode_step. */
+ * and n_layers * n_q_heads <= 8192.  It gathers G times the selected rows
+ * of sparse_decode_step; a group's dominant key rows and streaming rows are
+ * still read once for its G heads (bf16 caches on steps large enough for a
+ * separate threshold launch; otherwise each head reads them). */
 size_t sparse_decode_per_head_workspace(const has_decode_dims* dims);
 has_status sparse_decode_step_per_head(const has_decode_dims* dims, const void* q, const void* k_cache,
                                        const void* v_cache, const void* k_dom, const int32_t* i_dom,
