@@ -154,6 +154,7 @@ def main():
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the full-attention comparison")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-label", action="store_true")
     ap.add_argument("--cpu-sample", default="24,72", help="retrieval,streaming items timed on the CPU")
     ap.add_argument("--cpu-reps", type=int, default=15, help="oracle calls timed per sampled item")
@@ -393,6 +394,38 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log(f"{args.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
 
+    # the same step captured once into a HIP graph and replayed: one graph
+    # launch per step from the host instead of the library's launches
+    graph_info = None
+    if not args.no_graph:
+        gside = torch.cuda.Stream()
+        gside.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gside):  # warm-up off the default stream before capture
+            step()
+        torch.cuda.current_stream().wait_stream(gside)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gw0 = time.perf_counter()
+        ga.record()
+        for _ in range(args.steps):
+            graph.replay()
+        gb.record()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - gw0
+        gms = ga.elapsed_time(gb) / args.steps
+        graph_info = {"ms_per_step": round(gms, 5), "value": round(1e3 / gms, 2), "replays": args.steps,
+                      "host_ms_per_step": round(gwall * 1e3 / args.steps, 5),
+                      "eager_host_ms_per_step": round(wall * 1e3 / args.steps, 5)}
+        del graph
+        log(f"graph replay {graph_info}")
+
     # full attention on the same cache and queries, for the speed-up the
     # pages quote: every (layer, KV group) attends all T positions, through
     # the library's own attention (every group streaming, no sink, a window
@@ -504,6 +537,8 @@ def main():
         "measured_copy_GBps": round(copy_gbps, 1),
         "label": label_info,
     }
+    if graph_info is not None:
+        res["graph_replay"] = graph_info
     if dense is not None:
         res["dense_attention"] = dense
         res["pages_speedups_context"] = PAGES_SPEEDUPS
