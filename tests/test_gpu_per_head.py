@@ -57,6 +57,23 @@ def test_per_head_against_oracle(over):
     assert any((idx[0, 0, G + j] != idx[0, 0, G]).any() for j in range(1, G))
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4)], ids=["G2", "G8"])
+def test_per_head_group_sizes(hq, hkv):
+    """Group sizes 2 and 8: a scoring unit serves the group's 2 or 8 heads
+    (steps large enough for the threshold launch), each with its own
+    threshold and candidates."""
+    cfg = R.get_config("c1", ctx_len=20000, batch=2, n_layers=2, n_q_heads=hq, n_kv_heads=hkv)
+    print(f"case per-head G={hq // hkv}", flush=True)
+    lab = np.zeros((cfg.n_layers, cfg.n_kv_heads), np.uint8)
+    lab[0, 1] = lab[1, hkv - 1] = 1
+    case = U.DeviceCase(cfg, labels=lab)
+    out, idx = _run(case)
+    G = cfg.group
+    heads = [(0, 0, G + j) for j in range(G)] + [(1, 1, (hkv - 1) * G + G - 1), (0, 1, 0), (1, 0, 0)]
+    _check_heads(case, out, idx, heads, f"per-head G{G}")
+    assert any((idx[0, 0, G + j] != idx[0, 0, G]).any() for j in range(1, G))
+
+
 def test_per_head_with_one_head_per_group_is_the_plain_step():
     cfg = R.get_config("c1", ctx_len=12000, batch=2, n_q_heads=8, n_kv_heads=8)
     print("case per-head G=1", flush=True)
