@@ -938,11 +938,14 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
 // workgroup lists the retrieval pairs from the labels in LDS, workgroup 0
 // writes the plan for the later launches, and the grid fills the -1 index
 // rows of streaming groups.
-template <typename E, int V, bool PLAN>
+// HG > 1 (per-query-head selection with a tau launch): a unit serves the HG
+// head items of one KV group, reading the group's sampled rows once.
+template <typename E, int V, bool PLAN, int HG = 1>
 __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
+  static_assert(HG == 1 || !PLAN, "heads share units only without the fused plan");
   constexpr int EPV = Vec<E>::N;
   constexpr int kBlocks = kSampleTokens / 256;
-  __shared__ float s_q[kMaxR];
+  __shared__ float s_q[HG][kMaxR];
   __shared__ uint16_t s_ret[PLAN ? kMaxPairs : 1];
   __shared__ int s_w[NWAVE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -987,20 +990,30 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
   } else {
     n_idx = n_idx_pairs(g);
   }
-  const int n_units = n_idx * g.B * kBlocks;
+  const int n_units = n_idx / HG * g.B * kBlocks;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int item = u / kBlocks, blk = u - item * kBlocks;
-    const int pidx = item / g.B, b = item - pidx * g.B;
+    const int unit_item = u / kBlocks, blk = u - unit_item * kBlocks;
+    const int pg = unit_item / g.B, b = unit_item - pg * g.B;
+    const int pidx0 = pg * HG;  // the heads of a KV group are consecutive index pairs
     __syncthreads();
-    const size_t slice = group_query_dom_at<E>(g, pidx, PLAN ? (int)s_ret[pidx] : idx_pair(g, pidx), b, s_q);
+    size_t slice = 0;
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+      slice = group_query_dom_at<E>(g, pidx0 + h, PLAN ? (int)s_ret[pidx0 + h] : idx_pair(g, pidx0 + h), b, s_q[h]);
     __syncthreads();
     if (blk == 0) {
-      for (int c = tid; c < R; c += NT) g.qbar[(size_t)item * R + c] = s_q[c];
-      if ((PLAN || g.host_plan) && tid < 4) g.info[(size_t)item * 4 + tid] = 0u;  // else the plan clears them
-    }
-    float qr[EPV];
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) qr[e] = s_q[(lane % V) * EPV + e];
+      for (int h = 0; h < HG; ++h) {
+        const size_t item = (size_t)(pidx0 + h) * g.B + b;
+        for (int c = tid; c < R; c += NT) g.qbar[item * R + c] = s_q[h][c];
+        if ((PLAN || g.host_plan) && tid < 4) g.info[item * 4 + tid] = 0u;  // else the plan clears them
+      }
+    }
+    float qr[HG][EPV];
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) qr[h][e] = s_q[h][(lane % V) * EPV + e];
     const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * R;
     const int start = (int)((long long)blk * (g.T - 256) / (kBlocks - 1));
     uint4 raw[V];
@@ -1009,18 +1022,25 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
       const int tok = start + wave * 64 + i * (64 / V) + lane / V;
       raw[i] = ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV);
     }
-    float mine = 0.f;
+    float mine[HG];
+#pragma unroll
+    for (int h = 0; h < HG; ++h) mine[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       float kv[EPV];
       Vec<E>::cvt(raw[i], kv);
-      float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) sum += qr[e] * kv[e];
-      sum = group_sum<V>(sum);
-      if ((lane % V) == i) mine = sum;
+      for (int h = 0; h < HG; ++h) {
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) sum += qr[h][e] * kv[e];
+        sum = group_sum<V>(sum);
+        if ((lane % V) == i) mine[h] = sum;
+      }
     }
-    g.skeys[(size_t)item * kSampleTokens + blk * 256 + wave * 64 + lane] = f2key(mine);
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+      g.skeys[((size_t)(pidx0 + h) * g.B + b) * kSampleTokens + blk * 256 + wave * 64 + lane] = f2key(mine[h]);
   }
 }
 
@@ -1972,6 +1992,18 @@ hipError_t launch_sample_p(const Geo& g, int grid, hipStream_t s) {
   }
   return hipGetLastError();
 }
+// Sampling when every query head selects its own tokens: the hg heads of a
+// KV group share each unit (bf16 caches).
+template <int V>
+hipError_t launch_sample_heads(const Geo& g, int hg, int grid, hipStream_t s) {
+  switch (hg) {
+    case 2: sample_kernel<uint16_t, V, false, 2><<<grid, NT, 0, s>>>(g); break;
+    case 4: sample_kernel<uint16_t, V, false, 4><<<grid, NT, 0, s>>>(g); break;
+    case 8: sample_kernel<uint16_t, V, false, 8><<<grid, NT, 0, s>>>(g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 template <typename E>
 hipError_t launch_sample_v(const Geo& g, int grid, hipStream_t s, bool plan) {
   return plan ? launch_sample_p<E, true>(g, grid, s) : launch_sample_p<E, false>(g, grid, s);
@@ -2136,12 +2168,22 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   const int grid_tip = clampi(n_idx_items * g.nch_t, 1, g.grid);
   const bool tau_inline = n_idx_items * g.nch_tip <= kTauInlineUnits;
   const int grid_item = clampi(n_idx_items, 1, g.grid);
+  // per-query-head selection: a KV group's hg heads share the sampling and
+  // scoring units (bf16 caches, steps with a tau launch)
+  const int hg = 1 << g.kv_shift;
+  const int tip_v = g.R * (g.bf16 ? 2 : 4) / 16;
+  const bool share = !tau_inline && hg > 1 && g.bf16 && (tip_v == 2 || tip_v == 4 || tip_v == 8);
+  const bool share_sample = share && !fuse_plan;  // the plan-building sampler serves one item per unit
   if (g.prefilter) {
     {
       KTimer t("sample", s);
-      const int grid_sample = clampi(n_idx_items * (kSampleTokens / 256), 1, g.grid);
-      e = g.bf16 ? launch_sample_v<uint16_t>(g, grid_sample, s, fuse_plan)
-                 : launch_sample_v<float>(g, grid_sample, s, fuse_plan);
+      const int grid_sample = clampi(n_idx_items / (share_sample ? hg : 1) * (kSampleTokens / 256), 1, g.grid);
+      if (share_sample)
+        e = tip_v == 2 ? launch_sample_heads<2>(g, hg, grid_sample, s)
+            : tip_v == 4 ? launch_sample_heads<4>(g, hg, grid_sample, s) : launch_sample_heads<8>(g, hg, grid_sample, s);
+      else
+        e = g.bf16 ? launch_sample_v<uint16_t>(g, grid_sample, s, fuse_plan)
+                   : launch_sample_v<float>(g, grid_sample, s, fuse_plan);
     }
     if (e != hipSuccess) return e;
     if (!tau_inline) {
@@ -2150,14 +2192,11 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
-      const int hg = 1 << g.kv_shift;
-      const int V = g.R * (g.bf16 ? 2 : 4) / 16;
-      const bool share = !tau_inline && hg > 1 && g.bf16 && (V == 2 || V == 4 || V == 8);
       const int grid_tip_pf = clampi(n_idx_items / (share ? hg : 1) * g.nch_tip, 1, g.grid);
       KTimer t("tip_score", s);
       if (share)
-        e = V == 2 ? launch_tip_heads<2>(g, hg, grid_tip_pf, s)
-                   : V == 4 ? launch_tip_heads<4>(g, hg, grid_tip_pf, s) : launch_tip_heads<8>(g, hg, grid_tip_pf, s);
+        e = tip_v == 2 ? launch_tip_heads<2>(g, hg, grid_tip_pf, s)
+            : tip_v == 4 ? launch_tip_heads<4>(g, hg, grid_tip_pf, s) : launch_tip_heads<8>(g, hg, grid_tip_pf, s);
       else if (tau_inline)
         e = g.bf16 ? launch_tip_v<uint16_t, 2>(g, grid_tip_pf, s) : launch_tip_v<float, 2>(g, grid_tip_pf, s);
       else
