@@ -74,6 +74,26 @@ def test_per_head_group_sizes(hq, hkv):
     assert any((idx[0, 0, G + j] != idx[0, 0, G]).any() for j in range(1, G))
 
 
+def test_per_head_all_scores_tied():
+    """Zero queries: every token scores 0 for every head, so every token is
+    a candidate (the shared scoring units overflow their staging and append
+    directly, then the selection falls back to rescoring); ties go to the
+    lower token, so each retrieval head selects tokens 0 .. n_fac - 1."""
+    cfg = R.get_config("c1", ctx_len=20000, batch=2, n_layers=2)
+    print("case per-head tied", flush=True)
+    lab = np.zeros((cfg.n_layers, cfg.n_kv_heads), np.uint8)
+    lab[0, 2] = lab[1, 5] = 1
+    case = U.DeviceCase(cfg, labels=lab, zero_q=True)
+    out, idx = _run(case)
+    G = cfg.group
+    want = np.arange(cfg.n_fac, dtype=np.int32)
+    for (l, g) in ((0, 2), (1, 5)):
+        for b in range(cfg.batch):
+            for j in range(G):
+                assert (idx[l, b, g * G + j] == want).all(), f"l{l} b{b} h{g * G + j}"
+    _check_heads(case, out, idx, [(0, 1, 2 * G + 3), (1, 0, 5 * G), (0, 0, 0)], "per-head tied")
+
+
 def test_per_head_with_one_head_per_group_is_the_plain_step():
     cfg = R.get_config("c1", ctx_len=12000, batch=2, n_q_heads=8, n_kv_heads=8)
     print("case per-head G=1", flush=True)
