@@ -1883,6 +1883,7 @@ __global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd
   constexpr int EPV = 16 / (int)sizeof(E);
   constexpr int kTileVec = 8 * NT;  // 16-byte vectors per tile (32 KB)
   __shared__ uint4 s_rows[kTileVec];
+  __shared__ int s_chn[kMaxR];  // the slice's source channel of each output element (-1: zero padding)
   const int vpr = g.d * (int)sizeof(E) / 16;  // 16-byte vectors per cache row (8, 16 or 32)
   const int tt = kTileVec / vpr;              // tokens per tile
   const int ovt = g.R / EPV;                  // 16-byte output vectors per token
@@ -1903,14 +1904,26 @@ __global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd
   };
   uint4 r[8];
   if (blockIdx.x < n_work) load_tile(blockIdx.x, r);
+  int cur = -1;  // slice whose channel list s_chn holds (uniform in the workgroup)
   for (long long w = blockIdx.x; w < n_work; w += gridDim.x) {
     const int s = (int)(w / n_tiles), tile = (int)(w - (long long)s * n_tiles);
-    const int gi = s % g.Hkv, l = s / (g.Hkv * g.B);
-    const int32_t* dom = g.i_dom + ((size_t)l * g.Hkv + gi) * g.n_dom;
     const int t0 = tile * tt, nt = min(tt, g.T - t0);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j) s_rows[threadIdx.x + j * NT] = r[j];
+    if (s != cur) {
+      const int gi = s % g.Hkv, l = s / (g.Hkv * g.B);
+      const int32_t* dom = g.i_dom + ((size_t)l * g.Hkv + gi) * g.n_dom;
+      for (int e = threadIdx.x; e < g.R; e += NT) {
+        int c = -1;
+        if (e < 2 * g.n_dom) {
+          const int f = min(max(dom[e >> 1], 0), hd - 1), cc = e & 1;  // as in group_query_dom
+          c = g.interleaved ? 2 * f + cc : f + cc * hd;
+        }
+        s_chn[e] = c;
+      }
+      cur = s;
+    }
     __syncthreads();
     if (w + gridDim.x < n_work) load_tile(w + gridDim.x, r);
     for (int o = threadIdx.x; o < nt * ovt; o += NT) {
@@ -1919,13 +1932,8 @@ __global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd
       E vals[EPV];
 #pragma unroll
       for (int q = 0; q < EPV; ++q) {
-        const int e = part * EPV + q;
-        E v = E(0);
-        if (e < 2 * g.n_dom) {
-          const int f = min(max(dom[e >> 1], 0), hd - 1), cc = e & 1;  // as in group_query_dom
-          v = row[g.interleaved ? 2 * f + cc : f + cc * hd];
-        }
-        vals[q] = v;
+        const int c = s_chn[part * EPV + q];
+        vals[q] = c >= 0 ? row[c] : E(0);
       }
       uint4 packed;
       __builtin_memcpy(&packed, vals, sizeof(packed));
