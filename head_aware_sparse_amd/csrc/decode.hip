@@ -1937,7 +1937,9 @@ __global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd
       }
       uint4 packed;
       __builtin_memcpy(&packed, vals, sizeof(packed));
-      *reinterpret_cast<uint4*>(kd + ((size_t)s * g.T + t0 + tok) * g.R + part * EPV) = packed;
+      // streaming store: the copy is read by later decode steps, not by this kernel
+      const u32x4 pv = {packed.x, packed.y, packed.z, packed.w};
+      __builtin_nontemporal_store(pv, reinterpret_cast<u32x4*>(kd + ((size_t)s * g.T + t0 + tok) * g.R + part * EPV));
     }
   }
 }
