@@ -256,8 +256,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
   constexpr int CB = D / 16;  // 16-col bands
   constexpr int CH = CB / 2;  // column bands per pass
   __shared__ double s_m[D * (D + 1) / 2];
-  __shared__ double s_v[D], s_p[D];
-  __shared__ double s_red[NWAVE], s_red2[NWAVE];
   __shared__ float s_d[D], s_e[D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.x;                 // l*Hq + h
@@ -277,11 +275,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
     for (int a = 0; a < RB; ++a)
 #pragma unroll
       for (int c = 0; c < CH; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // unrolled so that several k steps' operand loads are in flight together
+#pragma unroll 8
     for (int k = 0; k < D; k += 4) {
       const int kk = k + (lane >> 4);
       double av[RB];
 #pragma unroll
-      for (int a = 0; a < RB; ++a) av[a] = (double)GQ[(size_t)((wave * RB + a) * 16 + (lane & 15)) * D + kk];
+      // G_Q is symmetric: element (row, kk) is read at (kk, row), so the 16 lanes of a row band read consecutive words
+      for (int a = 0; a < RB; ++a) av[a] = (double)GQ[(size_t)kk * D + (wave * RB + a) * 16 + (lane & 15)];
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const double bv = Lg[(size_t)kk * D + (c0 + c) * 16 + (lane & 15)];
@@ -311,6 +312,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
     for (int a = 0; a < RB; ++a)
 #pragma unroll
       for (int c = 0; c < CH; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // unrolled so that several k steps' operand loads are in flight together
+#pragma unroll 8
     for (int k = 0; k < D; k += 4) {
       const int kk = k + (lane >> 4);
       double av[RB];
@@ -345,103 +348,95 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
     __syncthreads();
   }
 
-  // 3. Householder tridiagonalisation (similarity, eigenvalues kept).  Step k
-  //    reflects rows/columns k+1.. of the trailing m x m block with
-  //    v = x - alpha e1 (x: column k below the diagonal), p = beta A v,
-  //    w = p - (beta/2)(v.p) v, A -= v w^T + w v^T.  Four barriers per step.
-  for (int k = 0; k < D - 2; ++k) {
-    const int m = D - k - 1, r0 = k + 1;
-    const double x = tid < m ? A[pk(r0 + tid, k)] : 0.0;
-    const double part = wave_sum_d(x * x);
-    if (lane == 0) s_red[wave] = part;
-    __syncthreads();
-    double nrm2 = 0.0;
+  // 3. Householder tridiagonalisation (similarity, eigenvalues kept), the
+  //    symmetric matrix held in registers: thread (ty, tx) of a 16 x 16 grid
+  //    holds rows ty + 16 r and columns tx + 16 c (r, c < BS), so the lanes of
+  //    a row band read consecutive LDS words.  Step k
+  //    reflects rows/columns k+1.. with v = x - alpha e1 (x: column k below
+  //    the diagonal), p = beta A v, w = p - (beta/2)(v.p) v, A -= v w^T + w v^T;
+  //    v and w vanish on rows and columns <= k, which stay as they are.
+  //    Column k and p pass through LDS in two buffers taken in turn, so a step
+  //    needs two barriers; every wave forms the norms and dot products itself.
+  constexpr int BS = D / 16;
+  __shared__ double s_x[2][D], s_pp[2][D];
+  const int ty = tid >> 4, tx = tid & 15;
+  double a[BS][BS];
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) nrm2 += s_red[w];
-    const double x0 = A[pk(r0, k)];
+  for (int r = 0; r < BS; ++r)
+#pragma unroll
+    for (int c = 0; c < BS; ++c) {
+      const int i = ty + 16 * r, j = tx + 16 * c;
+      a[r][c] = j <= i ? A[pk(i, j)] : A[pk(j, i)];
+    }
+  for (int k = 0; k < D - 2; ++k) {
+    const int r0 = k + 1;
+    double* sx = s_x[k & 1];
+    double* sp = s_pp[k & 1];
+    if (tx == k % 16) {  // column k: below the diagonal into LDS, the diagonal to d
+      // k / 16 is the same in every thread, so only one register column is read
+#pragma unroll
+      for (int c = 0; c < BS; ++c) {
+        if (c != k / 16) continue;
+#pragma unroll
+        for (int r = 0; r < BS; ++r) {
+          const int i = ty + 16 * r;
+          sx[i] = i > k ? a[r][c] : 0.0;
+          if (i == k) s_d[k] = (float)a[r][c];
+        }
+      }
+    }
+    __syncthreads();
+    double xx = 0.0;
+    for (int i = lane; i < D; i += 64) xx += sx[i] * sx[i];
+    const double nrm2 = wave_sum_d(xx);
+    const double x0 = sx[r0];
     const double alpha = x0 >= 0.0 ? -sqrt(nrm2) : sqrt(nrm2);
     const double vn2 = nrm2 - x0 * x0 + (x0 - alpha) * (x0 - alpha);
-    if (tid == 0) {
-      s_d[k] = (float)A[pk(k, k)];
-      s_e[k] = (float)(vn2 > 0.0 ? alpha : x0);
-    }
-    if (!(vn2 > 0.0)) {  // uniform: the column is already reduced
-      __syncthreads();
-      continue;
-    }
+    if (tid == 0) s_e[k] = (float)(vn2 > 0.0 ? alpha : x0);
+    if (!(vn2 > 0.0)) continue;  // uniform: the column is already reduced
     const double beta = 2.0 / vn2;
-    if (tid < m) s_v[tid] = tid == 0 ? x0 - alpha : x;
-    __syncthreads();
-    // p = beta A v: two threads per row, each over half of the columns with
-    // four partial sums; the symmetric element (i, j > i) is read at (j, i)
-    {
-      const int i = tid >> 1, hh = tid & 1;
-      const int half = (m + 1) >> 1, jb = hh * half, je = min(m, jb + half);
-      double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-      if (i < m) {
-        auto a_ij = [&](int j) { return j <= i ? A[pk(r0 + i, r0 + j)] : A[pk(r0 + j, r0 + i)]; };
-        int j = jb;
-        for (; j + 7 < je; j += 8) {
-          s0 += a_ij(j) * s_v[j] + a_ij(j + 4) * s_v[j + 4];
-          s1 += a_ij(j + 1) * s_v[j + 1] + a_ij(j + 5) * s_v[j + 5];
-          s2 += a_ij(j + 2) * s_v[j + 2] + a_ij(j + 6) * s_v[j + 6];
-          s3 += a_ij(j + 3) * s_v[j + 3] + a_ij(j + 7) * s_v[j + 7];
-        }
-        for (; j < je; ++j) s0 += a_ij(j) * s_v[j];
-      }
-      double sum = (s0 + s1) + (s2 + s3);
-      sum += dpp_d<0xB1>(sum);  // the row's other half (lane pair)
-      const double pi = beta * sum;
-      if (hh == 0 && i < m) s_p[i] = pi;
-      const double vp = wave_sum_d((hh == 0 && i < m) ? s_v[i] * pi : 0.0);
-      if (lane == 0) s_red2[wave] = vp;
+    auto vof = [&](int i) { return i == r0 ? x0 - alpha : sx[i]; };  // 0 on rows <= k
+    double vc[BS];
+#pragma unroll
+    for (int c = 0; c < BS; ++c) vc[c] = vof(tx + 16 * c);
+    // p for this thread's rows: its block's share, summed over the row band's
+    // 16 lanes (one 16-lane row of the wave)
+#pragma unroll
+    for (int r = 0; r < BS; ++r) {
+      double pr = 0.0;
+#pragma unroll
+      for (int c = 0; c < BS; ++c) pr += a[r][c] * vc[c];
+      pr += dpp_d<0xB1>(pr);   // quad_perm [1,0,3,2]
+      pr += dpp_d<0x4E>(pr);   // quad_perm [2,3,0,1]
+      pr += dpp_d<0x141>(pr);  // row_half_mirror
+      pr += dpp_d<0x140>(pr);  // row_mirror
+      const int i = ty + 16 * r;
+      if (tx == r) sp[i] = i >= r0 ? beta * pr : 0.0;
     }
     __syncthreads();
-    double vp = 0.0;
+    double vpp = 0.0;
+    for (int i = lane; i < D; i += 64) vpp += vof(i) * sp[i];
+    const double kk = 0.5 * beta * wave_sum_d(vpp);
+    double wc[BS];
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) vp += s_red2[w];
-    const double kk = 0.5 * beta * vp;
-    // lane j's entries of v and w for columns j and j + 64 stay in registers;
-    // each wave updates four of its rows per pass so their LDS round trips
-    // overlap
-    double vj[2], wj[2];
+    for (int c = 0; c < BS; ++c) wc[c] = sp[tx + 16 * c] - kk * vc[c];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int j = lane + 64 * c;
-      vj[c] = j < m ? s_v[j] : 0.0;
-      wj[c] = j < m ? s_p[j] - kk * vj[c] : 0.0;
+    for (int r = 0; r < BS; ++r) {
+      const double vr = vof(ty + 16 * r), wr = sp[ty + 16 * r] - kk * vr;
+#pragma unroll
+      for (int c = 0; c < BS; ++c) a[r][c] -= vr * wc[c] + wr * vc[c];
     }
-    for (int i0 = wave; i0 < m; i0 += 4 * NWAVE) {
-      double vi[4], wi[4], a[4][2];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = min(i0 + q * NWAVE, m - 1);
-        vi[q] = s_v[i];
-        wi[q] = s_p[i] - kk * vi[q];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int j = lane + 64 * c;
-          a[q][c] = j <= i ? A[pk(r0 + i, r0 + j)] : 0.0;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = i0 + q * NWAVE;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int j = lane + 64 * c;
-          if (i < m && j <= i) A[pk(r0 + i, r0 + j)] = a[q][c] - (vi[q] * wj[c] + wi[q] * vj[c]);
-        }
-      }
-    }
-    __syncthreads();
   }
-  if (tid == 0) {
-    s_d[D - 2] = (float)A[pk(D - 2, D - 2)];
-    s_e[D - 2] = (float)A[pk(D - 1, D - 2)];
-    s_d[D - 1] = (float)A[pk(D - 1, D - 1)];
-    s_e[D - 1] = 0.f;
-  }
+  // the last 2 x 2 block
+#pragma unroll
+  for (int r = 0; r < BS; ++r)
+#pragma unroll
+    for (int c = 0; c < BS; ++c) {
+      const int i = ty + 16 * r, j = tx + 16 * c;
+      if (i == j && i >= D - 2) s_d[i] = (float)a[r][c];
+      if (i == D - 1 && j == D - 2) s_e[D - 2] = (float)a[r][c];
+    }
+  if (tid == 0) s_e[D - 1] = 0.f;
   __syncthreads();
   float* tri = g.tri + (size_t)head * 2 * D;
   for (int i = tid; i < D; i += NT) {
