@@ -13,7 +13,7 @@
 //   cholesky  per key head, in fp64 LDS: G_K = L L^T.
 //   spectrum  per query head: the symmetric S = L^T G_Q L (fp64 matrix
 //             cores), which is similar to C_h = G_Q G_K; Householder
-//             tridiagonalisation of S in fp64 LDS.
+//             tridiagonalisation of S in fp64, the matrix in registers.
 //   bisect    eigenvalues of the tridiagonal by Sturm-count bisection (one
 //             thread per eigenvalue), sigma = sqrt(max(lambda, 0)) and ER.
 //   finalize  group mean of ER, global rank with ties to the lower index,
@@ -248,8 +248,8 @@ __global__ __launch_bounds__(NT) void chol_kernel(LGeo g) {
 // lane%16); output (4*r + lane/16, lane%16) in register r (checked on the
 // device: unlike the fp32 16x16 forms, rows interleave across lane groups).
 // Per query head: S = L^T G_Q L (similar to C_h = G_Q G_K) on the fp64 matrix
-// cores, then Householder tridiagonalisation of S in LDS, holding only the
-// lower triangle of the symmetric trailing matrix.
+// cores, symmetrised into a packed lower triangle in LDS, then Householder
+// tridiagonalisation of S with the matrix spread over the threads' registers.
 template <int D>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void spectrum_kernel(LGeo g) {
   constexpr int RB = D / 64;  // 16-row bands per wave
