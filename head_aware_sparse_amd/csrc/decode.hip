@@ -930,10 +930,11 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
   }
 }
 
-// sample: TIP keys of kSampleTokens tokens per index item, in 16 evenly
-// spread blocks of 256; one unit = (item, block), each wave scoring 64 tokens
-// with the same lane layout as tip_kernel.  Block 0 also stores the item's
-// group query for the scoring pass.
+// sample: TIP keys of kSampleTokens tokens per index item, in 64 V evenly
+// spread blocks of 64 / V tokens (V 16-byte pieces per key row: 256 blocks of
+// 16 for bf16 d 128); one unit = (item, 256 of the tokens), each wave scoring
+// 64 of them (one block per load) with tip_kernel's reduction.  Unit 0 of the
+// item also stores its group query for the scoring pass.
 // PLAN (steps without the side stream): no plan launch precedes; every
 // workgroup lists the retrieval pairs from the labels in LDS, workgroup 0
 // writes the plan for the later launches, and the grid fills the -1 index
@@ -1015,11 +1016,17 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
 #pragma unroll
       for (int e = 0; e < EPV; ++e) qr[h][e] = s_q[h][(lane % V) * EPV + e];
     const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * R;
-    const int start = (int)((long long)blk * (g.T - 256) / (kBlocks - 1));
+    // The sampled tokens: 64 V blocks of 64 / V consecutive tokens, evenly
+    // spread over the context, one block per load of a wave (the unit holds
+    // blocks blk * 4V .. blk * 4V + 4V - 1).  Many short blocks: nearby TIP
+    // scores are correlated, so the blocks, not the tokens, set how well the
+    // sample places tau.
+    constexpr int kBlen = 64 / V, kNsb = 64 * V;
     uint4 raw[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const int tok = start + wave * 64 + i * (64 / V) + lane / V;
+      const int sb = blk * (NWAVE * V) + wave * V + i;
+      const int tok = (int)((long long)sb * (g.T - kBlen) / (kNsb - 1)) + lane / V;
       raw[i] = ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV);
     }
     float mine[HG];

@@ -203,7 +203,8 @@ def test_prefilter_fallback_too_few_candidates(T):
     print(f"case prefilter fallback T={T}", flush=True)
     hi = R.HostInputs(cfg, with_weights=False)
     T = cfg.ctx_len
-    sampled = np.concatenate([np.arange(256) + (blk * (T - 256)) // 15 for blk in range(16)])
+    # the library's sample: 256 evenly spread blocks of 16 tokens (bf16, d 128: 4 pieces per key row)
+    sampled = np.concatenate([np.arange(16) + (sb * (T - 16)) // 255 for sb in range(256)])
     (l, g) = R.planted_groups(cfg)[0]
     case = U.DeviceCase(cfg, hi=hi)
     kk = case.k[l, 0, g].float()
