@@ -1067,7 +1067,6 @@ __global__ __launch_bounds__(NT) void sample_kernel(Geo g) {
 // LONG = false (T <= kShortMaxT): the bitmap has an LDS array of its own, so
 // it always fits beside the candidates and the compacting path is compiled
 // out; LONG = true: the bitmap goes in the candidate buffer.
-constexpr int kShortMaxT = 131072;
 // One item per workgroup of kFinalThreads: the kernel's LDS admits one
 // workgroup per CU, so it brings sixteen waves.
 constexpr int kFinalThreads = 1024;

@@ -264,9 +264,12 @@ def test_tied_scores_select_exactly(shared_q, levels, T):
 @pytest.mark.parametrize("over", [
     dict(ctx_len=150000, n_fac=2048, batch=1),   # prefiltered, a ragged last scoring unit
     dict(ctx_len=8191, n_fac=500, batch=2),      # just below its 8192-token minimum
-    dict(ctx_len=32768, n_fac=6000, batch=1),    # 3 n_fac above its 16384 candidate slots
+    dict(ctx_len=32768, n_fac=9600, batch=1),    # expected candidates above 80% of its 16384 slots
+    dict(ctx_len=32768, n_fac=9498, batch=1),    # its largest n_fac at 32768 tokens (prefiltered)
+    dict(ctx_len=131072, n_fac=8401, batch=1),   # its largest n_fac at 131072 tokens (prefiltered)
+    dict(ctx_len=131073, n_fac=6000, batch=1),   # beyond 131072 tokens: 3 n_fac above the 16384 slots
     dict(ctx_len=8192, n_fac=3000, batch=1),     # near its largest n_fac at its smallest T (prefiltered)
-], ids=["T150000", "T8191", "nfac6000", "edge-prefilter"])
+], ids=["T150000", "T8191", "nfac9600", "nfac9498", "T131072-nfac8401", "T131073-nfac6000", "edge-prefilter"])
 def test_selection_path_boundaries(over):
     """The general selection path (every score written, radix threshold over
     chunks) and the prefiltered one at the edges of the rule choosing
