@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     sparse_decode_step_per_head,
     sparse_decode_step_split,
     sparse_decode_workspace,
+    sparse_selection_path,
     sparse_select,
     sparse_select_workspace,
     status_string,

@@ -55,6 +55,8 @@ def lib():
         L.kdom_pack.restype = I
         L.sparse_decode_workspace.argtypes = [DP]
         L.sparse_decode_workspace.restype = S
+        L.sparse_selection_path.argtypes = [DP]
+        L.sparse_selection_path.restype = I
         L.sparse_decode_step.argtypes = [DP, P, P, P, P, P, P, P, P, P, S, P]
         L.sparse_decode_step.restype = I
         L.shared_index_workspace.argtypes = [DP]
@@ -138,6 +140,15 @@ def kdom_row_elems(dims):
 
 def sparse_decode_workspace(dims):
     return int(lib().sparse_decode_workspace(ctypes.byref(dims)))
+
+
+def sparse_selection_path(dims):
+    """1 if sparse_decode_step selects through the sampled prefilter, 0 if
+    through the general radix path (host only)."""
+    r = lib().sparse_selection_path(ctypes.byref(dims))
+    if r < 0:
+        raise HasError(1, last_error())
+    return r
 
 
 def shared_index_workspace(dims):

@@ -552,6 +552,11 @@ size_t sparse_decode_workspace(const has_decode_dims* dims) {
   return make_layout(dims, false).bytes;
 }
 
+int sparse_selection_path(const has_decode_dims* dims) {
+  if (check_dims(dims, false) != HAS_OK) return -1;
+  return make_layout(dims, false).g.prefilter;
+}
+
 has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const void* k_cache,
                               const void* v_cache, const void* k_dom, const int32_t* i_dom,
                               const uint8_t* labels, float* out, int32_t* idx_out, void* ws, size_t ws_bytes,

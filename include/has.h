@@ -159,6 +159,17 @@ has_status kdom_pack(const has_decode_dims* dims, const void* k_cache, const int
  * retrieval groups and -1 for streaming groups; it may be NULL.
  * Accumulation is fp32; scores and selection are deterministic. */
 size_t sparse_decode_workspace(const has_decode_dims* dims);
+
+/* Which of the two exact selection paths ([FASA] §2.B.1 top-N_fac, the same
+ * set either way) sparse_decode_step takes for these dims; host only, no HIP
+ * call.  1: prefiltered (a sampled key threshold; TIP writes only the tokens
+ * at or above it, the final kernel ranks them).  0: general (TIP writes every
+ * score, an exact radix threshold follows).  -1: invalid dims, the reason in
+ * has_last_error().  The prefiltered path needs 8192 <= ctx_len <= 524288
+ * and its 16384 candidate slots to hold the expected candidates with room to
+ * spare: their expected count within 80% of the slots up to ctx_len 131072,
+ * 3*n_fac within them beyond. */
+int sparse_selection_path(const has_decode_dims* dims);
 has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const void* k_cache,
                               const void* v_cache, const void* k_dom, const int32_t* i_dom,
                               const uint8_t* labels, float* out, int32_t* idx_out, void* ws,

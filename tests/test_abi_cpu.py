@@ -175,3 +175,21 @@ def test_split_cache_argument_checks():
     assert split(d, vs=None) == 1 and "v_str" in H.last_error()
     assert split(d, lab=None) == 1
     assert split(d) == 3  # arguments valid: stops at the NULL workspace
+
+
+@pytest.mark.parametrize("T,n_fac,path", [
+    (8191, 500, 0), (8192, 3000, 1), (8192, 3002, 0),       # below the sample's 2 x 4096 tokens; the first edge
+    (32768, 2048, 1), (32768, 9498, 1), (32768, 9600, 0),   # expected candidates within 80% of 16384 slots
+    (131072, 4096, 1), (131072, 8401, 1), (131072, 8402, 0),
+    (131073, 5461, 1), (131073, 5462, 0),                   # beyond 131072 tokens: 3 n_fac within the slots
+    (524288, 4096, 1), (524289, 4096, 0),                   # the final kernel's token bitmap limit
+])
+def test_selection_path_rule(T, n_fac, path):
+    """The rule choosing between the two exact selection paths, at its edges
+    (the GPU boundary tests run the same shapes against the oracle)."""
+    assert H.sparse_selection_path(_dims(ctx_len=T, n_fac=n_fac)) == path
+
+
+def test_selection_path_rejects_bad_dims():
+    with pytest.raises(H.HasError):
+        H.sparse_selection_path(_dims(n_fac=40000))

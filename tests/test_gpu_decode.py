@@ -207,6 +207,7 @@ def test_prefilter_fallback_too_few_candidates(T):
     sampled = np.concatenate([np.arange(16) + (sb * (T - 16)) // 255 for sb in range(256)])
     (l, g) = R.planted_groups(cfg)[0]
     case = U.DeviceCase(cfg, hi=hi)
+    assert H.sparse_selection_path(case.dims) == 1
     kk = case.k[l, 0, g].float()
     kk[torch.from_numpy(sampled).cuda()] *= 40.0
     case.k[l, 0, g] = kk.to(case.k.dtype)
@@ -261,22 +262,23 @@ def test_tied_scores_select_exactly(shared_q, levels, T):
     U.check_out(out[l, 0, g * G:(g + 1) * G], ref, "ties out")
 
 
-@pytest.mark.parametrize("over", [
-    dict(ctx_len=150000, n_fac=2048, batch=1),   # prefiltered, a ragged last scoring unit
-    dict(ctx_len=8191, n_fac=500, batch=2),      # just below its 8192-token minimum
-    dict(ctx_len=32768, n_fac=9600, batch=1),    # expected candidates above 80% of its 16384 slots
-    dict(ctx_len=32768, n_fac=9498, batch=1),    # its largest n_fac at 32768 tokens (prefiltered)
-    dict(ctx_len=131072, n_fac=8401, batch=1),   # its largest n_fac at 131072 tokens (prefiltered)
-    dict(ctx_len=131073, n_fac=6000, batch=1),   # beyond 131072 tokens: 3 n_fac above the 16384 slots
-    dict(ctx_len=8192, n_fac=3000, batch=1),     # near its largest n_fac at its smallest T (prefiltered)
+@pytest.mark.parametrize("over,path", [
+    (dict(ctx_len=150000, n_fac=2048, batch=1), 1),   # prefiltered, a ragged last scoring unit
+    (dict(ctx_len=8191, n_fac=500, batch=2), 0),      # just below its 8192-token minimum
+    (dict(ctx_len=32768, n_fac=9600, batch=1), 0),    # expected candidates above 80% of its 16384 slots
+    (dict(ctx_len=32768, n_fac=9498, batch=1), 1),    # its largest n_fac at 32768 tokens
+    (dict(ctx_len=131072, n_fac=8401, batch=1), 1),   # its largest n_fac at 131072 tokens
+    (dict(ctx_len=131073, n_fac=6000, batch=1), 0),   # beyond 131072 tokens: 3 n_fac above the 16384 slots
+    (dict(ctx_len=8192, n_fac=3000, batch=1), 1),     # near its largest n_fac at its smallest T
 ], ids=["T150000", "T8191", "nfac9600", "nfac9498", "T131072-nfac8401", "T131073-nfac6000", "edge-prefilter"])
-def test_selection_path_boundaries(over):
+def test_selection_path_boundaries(over, path):
     """The general selection path (every score written, radix threshold over
     chunks) and the prefiltered one at the edges of the rule choosing
     between them give the oracle's selection."""
     cfg = R.get_config("c1", **over)
     print(f"case boundaries {over}", flush=True)
     case = U.DeviceCase(cfg)
+    assert H.sparse_selection_path(case.dims) == path, "the case must sit on the intended side of the rule"
     _check_items(case, _all_items(cfg)[:cfg.n_kv_heads * 2], f"boundary {over}")
 
 
@@ -291,6 +293,7 @@ def test_long_context_selection(T):
     print(f"case long context T={T}", flush=True)
     lab = np.array([[1, 0]], np.uint8)
     case = U.DeviceCase(cfg, labels=lab)
+    assert H.sparse_selection_path(case.dims) == (1 if T <= 524288 else 0)
     out, idx = _check_items(case, [(0, 0, 0), (0, 0, 1)], f"T{T}")
     assert np.isin(R.needle_positions(cfg, 0, 0, 0), idx[0, 0, 0]).all()
 
