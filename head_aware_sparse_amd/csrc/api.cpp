@@ -147,16 +147,15 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   // Prefiltered selection: a sample of kSampleTokens scores places a key
   // threshold expected to pass about 1.25 n_fac tokens plus 4 standard
   // deviations of the sampled count; used when that fits the kCandFast
-  // candidate slots comfortably: the expected count within 80% of them up to
-  // kShortMaxT tokens (the selected tokens need no room of their own there),
-  // n_fac within a third of them beyond (they are compacted beside the
-  // candidates and the token bitmap).
+  // candidate slots comfortably: the expected count within 80% of them, and
+  // beyond kShortMaxT tokens n_fac within the kSelMaxLong words that the
+  // final kernel keeps for the selected tokens beside its token bitmap.
   {
     const double S = has::kSampleTokens, p = (double)g.n_fac / g.T;
     const double r = 1.25 * S * p + 4.0 * std::sqrt(S * p) + 16.0;
     g.samp_rank = (int)std::ceil(r);
-    const bool fits = g.T <= has::kShortMaxT ? std::ceil(r) / S * g.T <= 0.8 * has::kCandFast
-                                             : 3LL * g.n_fac <= has::kCandFast;
+    const bool fits = std::ceil(r) / S * g.T <= 0.8 * has::kCandFast &&
+                      (g.T <= has::kShortMaxT || g.n_fac <= has::kSelMaxLong);
     g.prefilter = (g.T >= 2 * has::kSampleTokens && g.T <= has::kPrefilterMaxT && fits &&
                    g.samp_rank < has::kSampleTokens / 2) ? 1 : 0;
   }

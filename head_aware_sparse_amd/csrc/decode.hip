@@ -1088,12 +1088,12 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(Geo g) {
   // bitmap words per thread for the prefix counts: a multiple of 4 (16-byte
   // reads), so the bitmap spans BT * per words
   const int per = ((g.bm_words + BT - 1) / BT + 3) & ~3;
-  constexpr int kSelWords = (kCandFast / 3 + 63) / 64 * 64;  // n_fac <= kCandFast / 3 on this path
+  constexpr int kSelWords = kSelMaxLong;  // n_fac on this path, a multiple of 4 words
   constexpr int kPerMax = (kPrefilterMaxT / 32 / BT + 3) & ~3;
   static_assert(kCandFast * sizeof(uint2) >= (kSelWords + BT * kPerMax) * sizeof(uint32_t) +
                                                  BT * kPerMax * sizeof(uint16_t),
                 "selected tokens, bitmap and u16 prefixes fit the candidate buffer");
-  static_assert(kCandFast / 3 < 65536, "prefiltered n_fac fits u16 prefixes");
+  static_assert(kSelMaxLong % 4 == 0 && kSelMaxLong < 65536, "16-byte aligned bitmap; n_fac fits u16 prefixes");
   const int tid = threadIdx.x;
   const int n_items = n_idx_pairs(g) * g.B;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {

@@ -17,6 +17,7 @@ constexpr int kCandFast = 16384;     // candidates per item on the prefiltered p
 constexpr int kSampleTokens = 4096;  // tokens scored per item to place the prefilter
 constexpr int kPrefilterMaxT = 524288;  // token bitmap of the prefiltered path fits the final kernel's LDS
 constexpr int kShortMaxT = 131072;      // up to here the final kernel's token bitmap has an LDS array of its own
+constexpr int kSelMaxLong = 8192;       // beyond kShortMaxT: n_fac the final kernel compacts beside its bitmap
 
 // One decode call, with the workspace carved.  Passed by value to kernels.
 struct Geo {

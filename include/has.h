@@ -167,8 +167,8 @@ size_t sparse_decode_workspace(const has_decode_dims* dims);
  * score, an exact radix threshold follows).  -1: invalid dims, the reason in
  * has_last_error().  The prefiltered path needs 8192 <= ctx_len <= 524288
  * and its 16384 candidate slots to hold the expected candidates with room to
- * spare: their expected count within 80% of the slots up to ctx_len 131072,
- * 3*n_fac within them beyond. */
+ * spare (their expected count within 80% of the slots), and beyond ctx_len
+ * 131072 also n_fac <= 8192. */
 int sparse_selection_path(const has_decode_dims* dims);
 has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const void* k_cache,
                               const void* v_cache, const void* k_dom, const int32_t* i_dom,

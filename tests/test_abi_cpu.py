@@ -181,7 +181,8 @@ def test_split_cache_argument_checks():
     (8191, 500, 0), (8192, 3000, 1), (8192, 3002, 0),       # below the sample's 2 x 4096 tokens; the first edge
     (32768, 2048, 1), (32768, 9498, 1), (32768, 9600, 0),   # expected candidates within 80% of 16384 slots
     (131072, 4096, 1), (131072, 8401, 1), (131072, 8402, 0),
-    (131073, 5461, 1), (131073, 5462, 0),                   # beyond 131072 tokens: 3 n_fac within the slots
+    (131073, 8192, 1), (131073, 8193, 0),                   # beyond 131072 tokens: also n_fac <= 8192
+    (262144, 7420, 1), (262144, 7421, 0), (524288, 6001, 1), (524288, 6002, 0),
     (524288, 4096, 1), (524289, 4096, 0),                   # the final kernel's token bitmap limit
 ])
 def test_selection_path_rule(T, n_fac, path):

@@ -268,9 +268,11 @@ def test_tied_scores_select_exactly(shared_q, levels, T):
     (dict(ctx_len=32768, n_fac=9600, batch=1), 0),    # expected candidates above 80% of its 16384 slots
     (dict(ctx_len=32768, n_fac=9498, batch=1), 1),    # its largest n_fac at 32768 tokens
     (dict(ctx_len=131072, n_fac=8401, batch=1), 1),   # its largest n_fac at 131072 tokens
-    (dict(ctx_len=131073, n_fac=6000, batch=1), 0),   # beyond 131072 tokens: 3 n_fac above the 16384 slots
+    (dict(ctx_len=131073, n_fac=8193, batch=1), 0),   # beyond 131072 tokens: n_fac above its 8192 maximum
+    (dict(ctx_len=262144, n_fac=7420, batch=1), 1),   # its largest n_fac at 262144 tokens (selected tokens compacted)
     (dict(ctx_len=8192, n_fac=3000, batch=1), 1),     # near its largest n_fac at its smallest T
-], ids=["T150000", "T8191", "nfac9600", "nfac9498", "T131072-nfac8401", "T131073-nfac6000", "edge-prefilter"])
+], ids=["T150000", "T8191", "nfac9600", "nfac9498", "T131072-nfac8401", "T131073-nfac8193", "T262144-nfac7420",
+                           "edge-prefilter"])
 def test_selection_path_boundaries(over, path):
     """The general selection path (every score written, radix threshold over
     chunks) and the prefiltered one at the edges of the rule choosing
