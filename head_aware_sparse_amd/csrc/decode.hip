@@ -721,10 +721,30 @@ struct CandSource {
     if (lds) {
       for (int i = threadIdx.x; i < n; i += NT) f(lds[i].x, lds[i].y);
     } else {
-      for (int t = threadIdx.x; t < T; t += NT) {
-        const uint32_t key = f2key(sc[t]);
+      // every score of the item (rows are 64-float aligned): eight 16-byte
+      // loads in flight per thread, then the scalar tail
+      auto visit = [&](float v, int t) {
+        const uint32_t key = f2key(v);
         if ((key >> 21) == b1) f(key, (uint32_t)t);
+      };
+      const float4* s4 = reinterpret_cast<const float4*>(sc);
+      const int n4 = T / 4;
+      for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * NT) {
+        float4 r[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = i0 + j * NT < n4 ? s4[i0 + j * NT] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = i0 + j * NT;
+          if (i < n4) {
+            visit(r[j].x, 4 * i);
+            visit(r[j].y, 4 * i + 1);
+            visit(r[j].z, 4 * i + 2);
+            visit(r[j].w, 4 * i + 3);
+          }
+        }
       }
+      for (int t = n4 * 4 + (int)threadIdx.x; t < T; t += NT) visit(sc[t], t);
     }
   }
 };
