@@ -1324,7 +1324,9 @@ __global__ __launch_bounds__(NT) void select_b_kernel(Geo g) {
   __shared__ uint32_t s_chunk[kMaxTipChunks];
   __shared__ int s_w[NWAVE];
   __shared__ uint32_t s_res[2];
+  __shared__ uint32_t s_n;
   const int tid = threadIdx.x;
+  const int ct = g.ct;
   const int n_items = n_idx_pairs(g) * g.B;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     __syncthreads();
@@ -1349,6 +1351,26 @@ __global__ __launch_bounds__(NT) void select_b_kernel(Geo g) {
     find_bin_top(s_hist, 2048, need, s_w, s_res, bin, above);
     need -= above;
     const uint32_t pre22 = (b1 << 11) | (uint32_t)bin;
+    // scores rescanned: when the members of the threshold's 22-bit key prefix
+    // fit the LDS, one more scan moves them there and counts per chunk the
+    // tokens above that prefix (all selected); the later passes read the LDS
+    const uint32_t members = s_hist[bin];
+    const bool compact = !in_lds && members <= (uint32_t)kCandLds;
+    for (int c = tid; c < g.nch_t; c += NT) s_chunk[c] = 0;
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    if (compact) {
+      src.for_each([&](uint32_t k, uint32_t t) {
+        const uint32_t p = k >> 10;
+        if (p == pre22)
+          s_c[atomicAdd(&s_n, 1u)] = make_uint2(k, t);
+        else if (p > pre22)
+          atomicAdd(&s_chunk[t / ct], 1u);
+      });
+      __syncthreads();
+      src.lds = s_c;
+      src.n = (int)members;
+    }
     // key bits 9..0
     histogram(src, s_hist, 1024, [=](uint32_t k, uint32_t) { return (k >> 10) == pre22; },
               [](uint32_t k, uint32_t) { return k & 0x3FFu; });
@@ -1367,10 +1389,8 @@ __global__ __launch_bounds__(NT) void select_b_kernel(Geo g) {
       tpre |= (1023u - (uint32_t)bin) << shift;
     }
     const uint32_t tstar = tpre;
-    // per-chunk counts of selected candidates
-    for (int c = tid; c < g.nch_t; c += NT) s_chunk[c] = 0;
-    __syncthreads();
-    const int ct = g.ct;
+    // per-chunk counts of selected candidates (after a compaction, those of
+    // the prefix's members, the rest being counted already)
     src.for_each([&](uint32_t k, uint32_t t) {
       if (k > kstar || (k == kstar && t <= tstar)) atomicAdd(&s_chunk[t / ct], 1u);
     });

@@ -324,3 +324,29 @@ def test_debug_checks_reject_bad_arrays(monkeypatch):
             H.kdom_pack(case.kd_dims, case.k, case.i_dom, case.k_dom) if what != "label 2" else case.run(ws=ws)
     case.i_dom.copy_(good_dom)
     case.labels.copy_(good_lab)
+
+
+def _key_prefix_counts(scores, n_fac):
+    """(tokens sharing the n_fac-th score's 11-bit key prefix, tokens sharing
+    its 22-bit prefix), keys being the order-preserving bit images of the
+    fp32 scores."""
+    u = np.asarray(scores, np.float32).view(np.uint32).astype(np.uint64)
+    key = np.where(u >> 31 == 1, ~u & 0xFFFFFFFF, u | 0x80000000)
+    kth = key[np.argsort(-np.asarray(scores, np.float64), kind="stable")[n_fac - 1]]
+    return int((key >> 21 == kth >> 21).sum()), int((key >> 10 == kth >> 10).sum())
+
+
+def test_general_path_rescans_long_context():
+    """The general selection at 262144 tokens with n_fac 9000: the n_fac-th
+    score's 11-bit key bin holds more tokens than the exact threshold keeps
+    in LDS (8192), so it rescans the item's scores and moves the members of
+    the 22-bit prefix into LDS; selection and outputs against the oracle."""
+    cfg = R.get_config("c1", ctx_len=262144, n_fac=9000, batch=1)
+    print("case general path rescans T=262144 n_fac=9000", flush=True)
+    case = U.DeviceCase(cfg)
+    assert H.sparse_selection_path(case.dims) == 0
+    (l, g) = R.planted_groups(cfg)[0]
+    _, _, scores = U.oracle_item(cfg, case.hi, case.labels_np, l, 0, g)
+    bin11, bin22 = _key_prefix_counts(scores, cfg.n_fac)
+    assert bin11 > 8192 >= bin22, (bin11, bin22)
+    _check_items(case, [(l, 0, g), (l, 0, (g + 1) % cfg.n_kv_heads)], "general rescans")
