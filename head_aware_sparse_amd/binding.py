@@ -167,10 +167,18 @@ def aoh_label_workspace(n_layers, n_q_heads, n_kv_heads, d_model, d_head):
     return int(lib().aoh_label_workspace(n_layers, n_q_heads, n_kv_heads, d_model, d_head))
 
 
-def _workspace(nbytes, ws, like):
+def _workspace(nbytes, ws, like, stream=None):
+    """The caller's workspace, or a new one.  A new one is allocated on the
+    stream the library enqueues on, so that the caching allocator does not
+    hand its memory to another tensor while that stream's kernels still use
+    it (also when the caller drops the returned tensor)."""
     import torch
     if ws is None:
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+        if stream is not None:
+            with torch.cuda.stream(stream):
+                ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+        else:
+            ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
     _dev(ws, "ws", torch.uint8)
     return ws
 
@@ -200,7 +208,7 @@ def sparse_decode_step(dims, q, k_cache, v_cache, k_dom, i_dom, labels, out, idx
     _dev(out, "out", torch.float32, (L, B, Hq, d))
     _dev(idx_out, "idx_out", torch.int32, (L, B, Hkv, dims.n_fac))
     nbytes = sparse_decode_workspace(dims)
-    ws = _workspace(nbytes, ws, q)
+    ws = _workspace(nbytes, ws, q, stream)
     _check(lib().sparse_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_dom),
                                     _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(),
                                     _stream(stream)))
@@ -226,7 +234,7 @@ def sparse_decode_step_per_head(dims, q, k_cache, v_cache, k_dom, i_dom, labels,
     _dev(out, "out", torch.float32, (L, B, Hq, d))
     _dev(idx_out, "idx_out", torch.int32, (L, B, Hq, dims.n_fac))
     nbytes = sparse_decode_per_head_workspace(dims)
-    ws = _workspace(nbytes, ws, q)
+    ws = _workspace(nbytes, ws, q, stream)
     _check(lib().sparse_decode_step_per_head(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                              _ptr(k_dom), _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out),
                                              _ptr(ws), ws.numel(), _stream(stream)))
@@ -249,7 +257,7 @@ def shared_index_decode(dims, q, k_cache, v_cache, k_dom, i_dom, out, q_index=No
     _dev(out, "out", torch.float32, (N, B, Hq, d))
     _dev(idx_out, "idx_out", torch.int32, (B, Hkv, dims.n_fac))
     nbytes = shared_index_workspace(dims)
-    ws = _workspace(nbytes, ws, q)
+    ws = _workspace(nbytes, ws, q, stream)
     _check(lib().shared_index_decode(ctypes.byref(dims), _ptr(q), _ptr(q_index), _ptr(k_cache), _ptr(v_cache),
                                      _ptr(k_dom), _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _ptr(ws),
                                      ws.numel(), _stream(stream)))
@@ -324,7 +332,7 @@ def sparse_decode_step_split(dims, q, k_ret, v_ret, k_dom_ret, k_str, v_str, i_d
     _dev(idx_out, "idx_out", torch.int32, (L, B, Hkv, dims.n_fac))
     cap = _split_capacity(dims, k_ret, v_ret, k_dom_ret, k_str, v_str)
     nbytes = sparse_decode_workspace(dims)
-    ws = _workspace(nbytes, ws, q)
+    ws = _workspace(nbytes, ws, q, stream)
     _check(lib().sparse_decode_step_split(ctypes.byref(dims), cap, _ptr(q), _ptr_nonempty(k_ret),
                                           _ptr_nonempty(v_ret), _ptr_nonempty(k_dom_ret), _ptr_nonempty(k_str),
                                           _ptr_nonempty(v_str), _ptr(i_dom), _ptr(labels),
@@ -341,7 +349,7 @@ def sparse_select(dims, q_index, k_dom, i_dom, idx_out, ws=None, stream=None):
     _dev(i_dom, "i_dom", torch.int32, (Hkv, dims.n_dom))
     _dev(idx_out, "idx_out", torch.int32, (B, Hkv, dims.n_fac))
     nbytes = sparse_select_workspace(dims)
-    ws = _workspace(nbytes, ws, q_index)
+    ws = _workspace(nbytes, ws, q_index, stream)
     _check(lib().sparse_select(ctypes.byref(dims), _ptr(q_index), _ptr(k_dom), _ptr(i_dom), _ptr(idx_out),
                                _ptr(ws), ws.numel(), _stream(stream)))
     return ws
@@ -357,7 +365,7 @@ def fac_attend(dims, q, k_cache, v_cache, idx, out, ws=None, stream=None):
     _dev(idx, "idx", torch.int32, (B, Hkv, dims.n_fac))
     _dev(out, "out", torch.float32, (B, Hq, d))
     nbytes = fac_attend_workspace(dims)
-    ws = _workspace(nbytes, ws, q)
+    ws = _workspace(nbytes, ws, q, stream)
     _check(lib().fac_attend(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), _ptr(out),
                             _ptr(ws), ws.numel(), _stream(stream)))
     return ws
@@ -379,7 +387,7 @@ def aoh_label(w_q, w_k, n_q_heads, n_kv_heads, d_head, labels, n_retrieval=-1, e
     _dev(er_head, "er_head", torch.float32, (L, n_q_heads))
     _dev(er_group, "er_group", torch.float32, (L, n_kv_heads))
     nbytes = aoh_label_workspace(L, n_q_heads, n_kv_heads, d_model, d_head)
-    ws = _workspace(nbytes, ws, w_q)
+    ws = _workspace(nbytes, ws, w_q, stream)
     _check(lib().aoh_label(L, n_q_heads, n_kv_heads, d_model, d_head, wdt, _ptr(w_q), _ptr(w_k), int(n_retrieval),
                            float(er_threshold), _ptr(er_head), _ptr(er_group), _ptr(labels), _ptr(ws), ws.numel(),
                            _stream(stream)))

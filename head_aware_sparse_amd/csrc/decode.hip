@@ -389,13 +389,15 @@ __device__ uint2 item_tau(const Geo& g, int item, uint32_t* s_hist, int* s_w, ui
   uint32_t tau = lo + ((uint32_t)bin << sh);
   if (sh > 0) {
     // second digit inside that bin
+    // (the bits of the offset inside that bin: sh - sh2 <= 11 of them, so a
+    // narrow span never folds bits of the first digit into the second)
     const int sh2 = sh > 11 ? sh - 11 : 0;
-    const uint32_t b1 = (uint32_t)bin;
+    const uint32_t b1 = (uint32_t)bin, mask2 = (1u << (sh - sh2)) - 1u;
     for (int i = threadIdx.x; i < kHistBins; i += NT) s_hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (((k[i] - lo) >> sh) == b1) atomicAdd(&s_hist[((k[i] - lo) >> sh2) & (kHistBins - 1)], 1u);
+      if (((k[i] - lo) >> sh) == b1) atomicAdd(&s_hist[((k[i] - lo) >> sh2) & mask2], 1u);
     __syncthreads();
     find_bin_top(s_hist, kHistBins, (uint32_t)g.samp_rank - above, s_w, s_res, bin, above);
     tau += (uint32_t)bin << sh2;

@@ -262,6 +262,46 @@ def test_tied_scores_select_exactly(shared_q, levels, T):
     U.check_out(out[l, 0, g * G:(g + 1) * G], ref, "ties out")
 
 
+@pytest.mark.parametrize("step_exp", [10, 14], ids=["span-2^17-ulps", "span-2^13-ulps"])
+def test_narrow_score_span(step_exp):
+    """All TIP scores of one item within a narrow band, 16 + m * 2^-step_exp
+    for 257 integer levels m: the sampled keys span 2^13 to 2^17 fp32 steps,
+    so the candidate threshold's first 11-bit digit leaves only a few bits
+    for the second.  Scores are exact in fp32, and the selection must equal
+    the oracle's top-n (ties to the lower token) exactly."""
+    cfg = R.get_config("c1", batch=1)
+    print(f"case narrow score span 2^-{step_exp}", flush=True)
+    hi = R.HostInputs(cfg, with_weights=False)
+    (l, g) = R.planted_groups(cfg)[0]
+    G = cfg.group
+    assert H.sparse_selection_path(U.dims_of(cfg)) == 1
+    rng = np.random.default_rng(11 + step_exp)
+    case = U.DeviceCase(cfg, hi=hi)
+    f0, f1 = (int(x) for x in hi.i_dom[l, g][:2])
+    k = U.f64(hi.rows("k", l, 0, g), cfg).astype(np.float32)
+    k[:, f0] = 16.0
+    k[:, f1] = rng.integers(-128, 129, size=cfg.ctx_len)
+    q = U.f64(hi.q[l, 0, g * G:(g + 1) * G], cfg).astype(np.float32)
+    dom = np.concatenate([hi.i_dom[l, g], hi.i_dom[l, g] + cfg.d_head // 2])
+    q[:, dom] = 0.0
+    q[:, f0] = 1.0
+    q[:, f1] = 2.0 ** -step_exp
+    case.k[l, 0, g] = torch.from_numpy(k).to(case.k.dtype).cuda()
+    case.q[l, 0, g * G:(g + 1) * G] = torch.from_numpy(q).to(case.q.dtype).cuda()
+    H.kdom_pack(case.kd_dims, case.k, case.i_dom, case.k_dom)
+    torch.cuda.synchronize()
+    out, idx, _ = case.run()
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    k_host, q_host = bits(case.k[l, 0, g]), bits(case.q[l, 0, g * G:(g + 1) * G])
+    from oracle import fasa
+    scores = fasa.tip_scores(U.f64(q_host, cfg), U.f64(k_host, cfg), hi.i_dom[l, g])
+    assert np.ptp(scores) <= 256 * 2.0 ** -step_exp and np.unique(scores).size > 200
+    want = np.sort(fasa.top_n(scores, cfg.n_fac))
+    assert (idx[l, 0, g] == want).all()
+    ref, _ = U.oracle_item_custom(cfg, q_host, k_host, hi.rows("v", l, 0, g), hi.i_dom[l, g], True)
+    U.check_out(out[l, 0, g * G:(g + 1) * G], ref, "narrow span out")
+
+
 @pytest.mark.parametrize("over,path", [
     (dict(ctx_len=150000, n_fac=2048, batch=1), 1),   # prefiltered, a ragged last scoring unit
     (dict(ctx_len=8191, n_fac=500, batch=2), 0),      # just below its 8192-token minimum

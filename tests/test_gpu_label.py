@@ -119,3 +119,30 @@ def test_max_pairs_8192():
     print("case label 8192 pairs", flush=True)
     got, ref = _run(cfg, k=100)
     _check(got, ref, 100)
+
+
+def test_c4_32_layers_bf16():
+    """The full-size labeller call: 32 layers of Llama-3-8B-shaped bf16
+    weights (W_Q 4096 x 4096, W_K 1024 x 4096 per layer), 1024 query heads
+    in 256 (layer, KV group) pairs, the 64 lowest group ERs retrieval.  The
+    oracle scores the heads layer by layer (so the host holds one layer in
+    fp64 at a time) and ranks all 256 pairs together."""
+    cfg = R.get_config("c4")
+    print("case label c4 32 layers", flush=True)
+    w_q, w_k = R.weights(cfg)
+    wq = sdev.to_device(w_q, "cuda", True)
+    wk = sdev.to_device(w_k, "cuda", True)
+    lab = torch.full((cfg.n_layers, cfg.n_kv_heads), 7, dtype=torch.uint8, device="cuda")
+    erh = torch.empty((cfg.n_layers, cfg.n_q_heads), dtype=torch.float32, device="cuda")
+    erg = torch.empty((cfg.n_layers, cfg.n_kv_heads), dtype=torch.float32, device="cuda")
+    H.aoh_label(wq, wk, cfg.n_q_heads, cfg.n_kv_heads, cfg.d_head, lab, cfg.n_retrieval, er_head=erh, er_group=erg)
+    torch.cuda.synchronize()
+    del wq, wk
+    f = lambda a: R.storage_to_f64(a, True)
+    r_erh = np.concatenate([aoh.head_effective_ranks(f(w_q[l:l + 1]), f(w_k[l:l + 1]), cfg.n_q_heads,
+                                                     cfg.n_kv_heads, cfg.d_head) for l in range(cfg.n_layers)])
+    r_erg = aoh.group_scores(r_erh, cfg.n_kv_heads)
+    r_lab = aoh.labels_top_k(r_erg, cfg.n_retrieval)
+    got = (erh.cpu().numpy(), erg.cpu().numpy(), lab.cpu().numpy())
+    _check(got, (r_erh, r_erg, r_lab), cfg.n_retrieval)
+    assert (got[2] == R.planted_labels(cfg)).all()

@@ -40,8 +40,10 @@ def test_clsa_single_layer_equals_sparse_decode():
     out, idx, _ = U.run_clsa(case)
     out2, idx2, _ = case.run()
     assert (idx2[0] == idx).all()
-    # same selection; the attention sums differ only in fp32 summation order
-    # (matrix cores in the shared-index mode, vector ALUs in the plain step)
+    # same selection; with one layer both calls attend on the vector ALUs
+    # (the matrix-core kernel serves two or more layers sharing the index),
+    # and the tolerance leaves room for a different split of the selected
+    # rows over attention units, i.e. a different fp32 summation order
     np.testing.assert_allclose(out2, out, rtol=1e-4, atol=1e-5)
 
 

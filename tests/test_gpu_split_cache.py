@@ -165,7 +165,8 @@ def test_host_resident_rows_fasa_m():
     """The retrieval groups' full K and V rows in pinned host memory, only the
     dominant-key copy (and the streaming rings) in HBM: appends and decode
     read and write them over the host link and give exactly the results of
-    the all-device split cache.  Pageable host memory is refused before any
+    the all-device split cache, and the oracle's on one retrieval and one
+    streaming item per sequence.  Pageable host memory is refused before any
     launch."""
     cfg = R.get_config("c1", ctx_len=12000, batch=2, n_layers=2)
     print("case FASA-M host rows", flush=True)
@@ -188,6 +189,19 @@ def test_host_resident_rows_fasa_m():
     out_h, idx_h = _decode_split(case, host, case.dims)
     assert (idx_h == idx_d).all()
     assert np.array_equal(out_h, out_d)
+    # the host-row path against the oracle: one retrieval and one streaming
+    # item over all ctx_len rows, the two tokens appended one by one included
+    ret, strm = _pairs(case)
+    G = cfg.group
+    for b in range(cfg.batch):
+        for p in list(ret)[:1] + list(strm)[:1]:
+            l, g = divmod(p, cfg.n_kv_heads)
+            ref, ridx, scores = U.oracle_item(cfg, case.hi, case.labels_np, l, b, g)
+            U.check_out(out_h[l, b, g * G:(g + 1) * G], ref, f"FASA-M out l{l} b{b} g{g}")
+            if ridx is None:
+                assert (idx_h[l, b, g] == -1).all()
+            else:
+                U.check_index_set(idx_h[l, b, g], scores, cfg.n_fac, f"FASA-M idx l{l} b{b} g{g}")
     pageable = dict(host)
     pageable["v_ret"] = torch.zeros(dev["v_ret"].shape, dtype=dev["v_ret"].dtype)  # not pinned
     with pytest.raises((ValueError, H.HasError)):
