@@ -23,6 +23,8 @@ from .binding import (  # noqa: F401
     shared_index_workspace,
     sparse_decode_per_head_workspace,
     sparse_decode_step,
+    sparse_decode_step_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     sparse_decode_step_per_head,
     sparse_decode_step_split,
     sparse_decode_workspace,

@@ -59,6 +59,8 @@ def lib():
         L.sparse_selection_path.restype = I
         L.sparse_decode_step.argtypes = [DP, P, P, P, P, P, P, P, P, P, S, P]
         L.sparse_decode_step.restype = I
+        L.sparse_decode_step_noalloc.argtypes = [DP, P, P, P, P, P, P, P, P, P]
+        L.sparse_decode_step_noalloc.restype = I
         L.shared_index_workspace.argtypes = [DP]
         L.shared_index_workspace.restype = S
         L.shared_index_decode.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, S, P]
@@ -213,6 +215,28 @@ def sparse_decode_step(dims, q, k_cache, v_cache, k_dom, i_dom, labels, out, idx
                                     _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _ptr(ws), ws.numel(),
                                     _stream(stream)))
     return ws
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # HAS_NOALLOC_SCRATCH_BYTES of has.h
+
+
+def sparse_decode_step_noalloc(dims, q, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out=None, stream=None):
+    """sparse_decode_step without a workspace: the library's fixed per-device
+    scratch serves instead (nothing is allocated here or in the library)."""
+    import torch
+    L, B, Hq, Hkv, T, d = (dims.n_layers, dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.ctx_len,
+                           dims.d_head)
+    dt = _kv_torch_dtype(dims)
+    _dev(q, "q", dt, (L, B, Hq, d))
+    _dev(k_cache, "k_cache", dt, (L, B, Hkv, T, d))
+    _dev(v_cache, "v_cache", dt, (L, B, Hkv, T, d))
+    _dev(k_dom, "k_dom", dt, (L, B, Hkv, T, kdom_row_elems(dims)))
+    _dev(i_dom, "i_dom", torch.int32, (L, Hkv, dims.n_dom))
+    _dev(labels, "labels", torch.uint8, (L, Hkv))
+    _dev(out, "out", torch.float32, (L, B, Hq, d))
+    _dev(idx_out, "idx_out", torch.int32, (L, B, Hkv, dims.n_fac))
+    _check(lib().sparse_decode_step_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_dom),
+                                            _ptr(i_dom), _ptr(labels), _ptr(out), _ptr(idx_out), _stream(stream)))
 
 
 def sparse_decode_per_head_workspace(dims):

@@ -16,6 +16,13 @@
 #include "internal.h"
 #include "label.h"
 
+// Scratch of sparse_decode_step_noalloc: one fixed device array per GPU the
+// library runs on, allocated with the code object and held until the
+// process ends.  Host code never passes this name to a kernel (on the host
+// it is only a stand-in for the device symbol); it uses the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[HAS_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -345,6 +352,34 @@ has_status row_store(const void* p, const char* name, const void*& dev) {
   return fail(HAS_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", name);
 }
 
+// Device address of `scratch` on each device, looked up once per device
+// with that device current.
+struct ScratchAddr {
+  int device;
+  void* ptr;
+};
+std::mutex g_scratch_mu;
+std::vector<ScratchAddr> g_scratch;
+
+has_status scratch_address(void*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  for (const ScratchAddr& a : g_scratch)
+    if (a.device == dev) {
+      out = a.ptr;
+      return HAS_OK;
+    }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  if (!p || !aligned16(p)) return fail(HAS_ERR_HIP, "scratch has no usable device address on device %d", dev);
+  g_scratch.push_back(ScratchAddr{dev, p});
+  out = p;
+  return HAS_OK;
+}
+
 // The split cache of sparse_decode_step_split: slabs of `capacity` rows for
 // retrieval groups, rings of n_sink + window rows for streaming groups.
 struct SplitCache {
@@ -356,7 +391,7 @@ struct SplitCache {
 has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, const void* q_index,
                       const void* k_cache, const void* v_cache, const void* k_dom, const int32_t* i_dom,
                       const uint8_t* labels, float* out, int32_t* idx_out, void* ws, size_t ws_bytes,
-                      void* stream, const SplitCache* sc = nullptr, int kv_div = 1) {
+                      void* stream, const SplitCache* sc = nullptr, int kv_div = 1, bool static_scratch = false) {
   has_status s = check_dims(dims, clsa);
   if (s != HAS_OK) return s;
   if (sc) {
@@ -377,6 +412,16 @@ has_status run_decode(const has_decode_dims* dims, bool clsa, const void* q, con
   REQUIRE_PTR(out, "out");
   OPTIONAL_PTR(idx_out, "idx_out");
   Layout L = make_layout(dims, clsa);
+  if (static_scratch) {
+    // sparse_decode_step_noalloc: the fixed per-device array stands in for ws
+    if (L.bytes > (size_t)HAS_NOALLOC_SCRATCH_BYTES)
+      return fail(HAS_ERR_WORKSPACE,
+                  "sparse_decode_step_noalloc: these dims need %zu bytes of scratch, above the fixed %zu; "
+                  "call sparse_decode_step with a workspace instead",
+                  L.bytes, (size_t)HAS_NOALLOC_SCRATCH_BYTES);
+    if ((s = scratch_address(ws)) != HAS_OK) return s;
+    ws_bytes = (size_t)HAS_NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws) return fail(HAS_ERR_WORKSPACE, "ws is NULL");
   if (!aligned16(ws)) return fail(HAS_ERR_INVALID_ARG, "ws is not 16-byte aligned");
   if (ws_bytes < L.bytes) return fail(HAS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, L.bytes);
@@ -562,6 +607,13 @@ has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const 
                               void* stream) {
   return run_decode(dims, false, q, nullptr, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out, ws,
                     ws_bytes, stream);
+}
+
+has_status sparse_decode_step_noalloc(const has_decode_dims* dims, const void* q, const void* k_cache,
+                                      const void* v_cache, const void* k_dom, const int32_t* i_dom,
+                                      const uint8_t* labels, float* out, int32_t* idx_out, void* stream) {
+  return run_decode(dims, false, q, nullptr, k_cache, v_cache, k_dom, i_dom, labels, out, idx_out, nullptr, 0,
+                    stream, nullptr, 1, true);
 }
 
 size_t sparse_decode_per_head_workspace(const has_decode_dims* dims) {

@@ -175,6 +175,25 @@ has_status sparse_decode_step(const has_decode_dims* dims, const void* q, const 
                               const uint8_t* labels, float* out, int32_t* idx_out, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* sparse_decode_step_noalloc: sparse_decode_step for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results and errors as sparse_decode_step, without ws/ws_bytes: the
+ * scratch is a fixed array of HAS_NOALLOC_SCRATCH_BYTES in device memory,
+ * one per GPU, set up by the first call on that GPU and held until the
+ * process ends.  The call itself allocates nothing.  Dims whose
+ * sparse_decode_workspace() exceeds HAS_NOALLOC_SCRATCH_BYTES are rejected
+ * with HAS_ERR_WORKSPACE before anything is launched (64 MiB covers one
+ * Llama-3-8B-shaped layer at batch 16 and 32768 tokens, or batch 4 at
+ * 131072).  Every call on one GPU shares that GPU's array, and each call
+ * leaves its contents behind: two calls that can overlap on one GPU (on
+ * different streams, or from different threads without ordering) race on
+ * it and their results are undefined. */
+#define HAS_NOALLOC_SCRATCH_BYTES (64u << 20)
+has_status sparse_decode_step_noalloc(const has_decode_dims* dims, const void* q, const void* k_cache,
+                                      const void* v_cache, const void* k_dom, const int32_t* i_dom,
+                                      const uint8_t* labels, float* out, int32_t* idx_out, void* stream);
+
 /* sparse_decode_step_per_head: the per-query-head selection variant, to
  * ablate the group-mean TIP above ([FASA] §2.B.1 scores with one head's
  * query; with G heads per KV group, sparse_decode_step scores with their mean

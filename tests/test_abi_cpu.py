@@ -69,6 +69,29 @@ def test_bad_pointers_and_workspace():
     assert H.sparse_decode_workspace(_dims(d_head=96)) == 0
 
 
+def _noalloc(d, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, kd=FAKE, idom=FAKE, lab=FAKE, out=FAKE, idx=None)
+    p.update(ptrs)
+    P = ctypes.c_void_p
+    return lib().sparse_decode_step_noalloc(ctypes.byref(d), P(p["q"]), P(p["k"]), P(p["v"]), P(p["kd"]),
+                                            P(p["idom"]), P(p["lab"]), P(p["out"]), P(p["idx"]), None)
+
+
+def test_noalloc_checks_before_touching_the_device():
+    """The allocation-free variant validates like sparse_decode_step, and
+    rejects dims whose scratch exceeds the fixed array, all before its first
+    HIP call (no GPU here)."""
+    assert H.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert _noalloc(_dims(d_head=96)) == 2
+    assert _noalloc(_dims(), q=None) == 1 and "q" in H.last_error()
+    assert _noalloc(_dims(), out=FAKE + 4) == 1
+    big = _dims(n_layers=32, batch=4, ctx_len=131072, n_fac=4096, window=2048)
+    assert H.sparse_decode_workspace(big) > H.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(big) == 3 and "noalloc" in H.last_error()
+    fits = _dims(batch=16)
+    assert H.sparse_decode_workspace(fits) <= H.NOALLOC_SCRATCH_BYTES
+
+
 def test_shared_index_allows_null_labels_only_there():
     d = _dims(n_layers=8)
     P = ctypes.c_void_p
