@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse decode-attn steps/s at 32K & 128K ctx; achieved HBM TB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
+REPLICA_TOUCH_BYTES = 600e6  # bytes a rotation of cache copies must touch (> the 256 MB MALL)
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 # speed-ups over full attention that the pages report, on hardware they do
 # not name: context for the measured full-attention comparison, not targets
@@ -95,44 +96,115 @@ def traffic_from_profiles(kernel_key):
     return rec["hbm_bytes_per_launch"]
 
 
-def cpu_baseline(cfg, hi, labels, n_ret_sample, n_str_sample, reps):
-    """fp64 oracle on a bounded sample of the step's items, each timed over
-    `reps` calls, scaled to the whole step (input generation excluded from
-    the timing)."""
+def _host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_time_items(items, make_inputs, run_item, reps, cores):
+    """Times the oracle over `items` with `cores` of them in flight at once
+    (one thread each, BLAS limited to one thread per call), in rounds of
+    `cores` items whose inputs are built beforehand (not timed).  Returns
+    (effective seconds per item call on all the cores, CPU seconds spent)."""
+    import concurrent.futures as cf
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    wall, calls = 0.0, 0
+    for r0 in range(0, len(items), cores):
+        chunk = items[r0:r0 + cores]
+        inputs = [make_inputs(it) for it in chunk]
+
+        def work(x):
+            for _ in range(reps):
+                run_item(x)
+
+        ctx = threadpool_limits(limits=1) if threadpool_limits else None
+        if ctx is not None:
+            ctx.__enter__()
+        try:
+            t0 = time.perf_counter()
+            with cf.ThreadPoolExecutor(len(chunk)) as ex:
+                list(ex.map(work, inputs))
+            wall += time.perf_counter() - t0
+        finally:
+            if ctx is not None:
+                ctx.__exit__(None, None, None)
+        calls += len(chunk) * reps
+        del inputs
+    return wall / calls, wall * min(cores, len(items))
+
+
+def cpu_baseline(cfg, hi, labels, n_ret_sample, n_str_sample, reps, cores=None):
+    """fp64 oracle (oracle.fasa.decode_group) on a bounded sample of the
+    step's (layer, sequence, KV group) items, `cores` items at a time on the
+    host's cores, scaled to the whole step (input generation excluded)."""
     import numpy as np
     from oracle import fasa
     from synth import recipe as R
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    cores = cores or min(16, _host_cores())
     G = cfg.group
     ret = [(l, g) for l in range(cfg.n_layers) for g in range(cfg.n_kv_heads) if labels[l, g]]
     strm = [(l, g) for l in range(cfg.n_layers) for g in range(cfg.n_kv_heads) if not labels[l, g]]
     rng = np.random.default_rng(7)
-    t_ret, t_str = [], []
-    for pool, n, acc in [(ret, n_ret_sample, t_ret), (strm, n_str_sample, t_str)]:
-        if not pool:
+
+    def make(it):
+        l, g, b = it
+        f = lambda a: R.storage_to_f64(a, cfg.bf16)
+        return (f(hi.q[l, b, g * G:(g + 1) * G]), f(hi.rows("k", l, b, g)), f(hi.rows("v", l, b, g)), l, g)
+
+    def run(x):
+        q, k, v, l, g = x
+        fasa.decode_group(q, k, v, hi.i_dom[l, g], bool(labels[l, g]), cfg.n_fac, cfg.n_sink, cfg.window)
+
+    step_s, cpu_s, counts = 0.0, 0.0, []
+    for pool, n in ((ret, n_ret_sample), (strm, n_str_sample)):
+        if not pool or n <= 0:
+            counts.append(0)
             continue
-        for i in rng.choice(len(pool), size=min(n, len(pool)), replace=False):
-            l, g = pool[i]
-            b = int(rng.integers(cfg.batch))
-            k = R.storage_to_f64(hi.rows("k", l, b, g), cfg.bf16)
-            v = R.storage_to_f64(hi.rows("v", l, b, g), cfg.bf16)
-            q = R.storage_to_f64(hi.q[l, b, g * G:(g + 1) * G], cfg.bf16)
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                fasa.decode_group(q, k, v, hi.i_dom[l, g], bool(labels[l, g]), cfg.n_fac, cfg.n_sink, cfg.window)
-            acc.append((time.perf_counter() - t0) / reps)
-    n_ret_items = len(ret) * cfg.batch
-    n_str_items = len(strm) * cfg.batch
-    step_s = (np.mean(t_ret) if t_ret else 0.0) * n_ret_items + (np.mean(t_str) if t_str else 0.0) * n_str_items
+        pick = rng.choice(len(pool), size=min(n, len(pool) * cfg.batch), replace=len(pool) < n)
+        items = [(*pool[i], int(rng.integers(cfg.batch))) for i in pick]
+        per_call, used = cpu_time_items(items, make, run, reps, cores)
+        step_s += per_call * len(pool) * cfg.batch
+        cpu_s += used
+        counts.append(len(items))
+    n_ret_items, n_str_items = len(ret) * cfg.batch, len(strm) * cfg.batch
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"{len(t_ret)} retrieval + {len(t_str)} streaming (layer, sequence, KV group) items of "
-                       f"the step, each timed over {reps} calls of the fp64 numpy oracle "
-                       f"({reps * (sum(t_ret) + sum(t_str)):.1f} s of CPU work), scaled to {n_ret_items} + "
-                       f"{n_str_items} items")}
+            "sample": (f"{counts[0]} retrieval + {counts[1]} streaming (layer, sequence, KV group) items of the "
+                       f"step, each run {reps} times by the fp64 numpy oracle with {cores} items in flight on "
+                       f"{cores} host threads ({cpu_s:.1f} CPU-s), scaled to {n_ret_items} + {n_str_items} items")}
+
+
+def cpu_baseline_clsa(cfg, hi, reps, cores=None):
+    """fp64 oracle (oracle.clsa.shared_index_decode, one (sequence, KV group)
+    item per call: the indexer's TIP and top-n_fac once, then every layer's
+    attention over that index) on the whole step's items, `cores` at a time."""
+    import numpy as np
+    from oracle import clsa as oclsa
+    from synth import recipe as R
+    cores = cores or min(16, _host_cores())
+    G = cfg.group
+    f = lambda a: R.storage_to_f64(a, cfg.bf16)
+    items = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
+
+    def make(it):
+        b, g = it
+        return (f(hi.q[:, b:b + 1, g * G:(g + 1) * G]), f(hi.rows("k", 0, b, g))[None, None],
+                f(hi.rows("v", 0, b, g))[None, None], g)
+
+    def run(x):
+        q, k, v, g = x
+        oclsa.shared_index_decode(q, k, v, hi.i_dom[0, g:g + 1], cfg.n_fac)
+
+    per_call, used = cpu_time_items(items, make, run, reps, cores)
+    step_s = per_call * len(items)
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"all {len(items)} (sequence, KV group) items of the step, each run {reps} times by the "
+                       f"fp64 numpy oracle with {cores} items in flight on {cores} host threads "
+                       f"({used:.1f} CPU-s)")}
 
 
 def main():
@@ -157,7 +229,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-label", action="store_true")
     ap.add_argument("--cpu-sample", default="24,72", help="retrieval,streaming items timed on the CPU")
-    ap.add_argument("--cpu-reps", type=int, default=15, help="oracle calls timed per sampled item")
+    ap.add_argument("--cpu-reps", type=int, default=4, help="oracle calls timed per sampled item")
+    ap.add_argument("--extra-configs", default="c3,c2,c1",
+                    help="after the default c4 line: also time these workloads and report them under 'configs' "
+                         "('none' to skip)")
     ap.add_argument("--calib-bytes", type=int, default=1 << 30,
                     help="size of the reference copy kernel (torch.neg, fp32) timed beside the step")
     args = ap.parse_args()
@@ -168,6 +243,39 @@ def main():
               "see the design notes)", file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    res = run_config(args, args.config, headline=True)
+    extra = [c for c in args.extra_configs.split(",") if c and c != "none"]
+    variant = (args.ctx_len is not None or args.batch is not None or args.cache != "full" or args.select != "group"
+               or args.clsa_mode != "fused" or args.config != "c4")
+    if extra and not variant:
+        # the other workloads of the metric, each on a fresh set of inputs
+        # after the previous one's memory is released
+        res["configs"] = {}
+        for name in extra:
+            torch.cuda.empty_cache()
+            sub = argparse.Namespace(**vars(args))
+            sub.no_label, sub.no_graph, sub.no_split = True, True, True
+            # the CPU oracle on every item of the small steps (a few CPU-s each)
+            sub.cpu_sample, sub.cpu_reps = {"c1": ("2,6", 40), "c2": ("32,96", 4)}.get(name, (args.cpu_sample,
+                                                                                           args.cpu_reps))
+            sub.steps = max(args.steps, 200)
+            sub.warmup = max(args.warmup, 20)
+            r = run_config(sub, name, headline=False)
+            res["configs"][name] = {k: r[k] for k in (
+                "value", "unit", "ms_per_step", "steps", "warmup", "config", "roofline", "step_algorithmic_bytes",
+                "step_hbm_GBps", "step_hbm_frac", "tokens_scored_per_s", "kernels_ms", "replicas",
+                "dense_attention", "cpu_baseline") if k in r}
+            log(f"{name}: {r['ms_per_step']:.4f} ms/step, {r['step_hbm_frac']:.3f} of peak")
+    print(json.dumps(res), flush=True)
+
+
+def run_config(args, cfg_name, headline=True):
+    """Builds one workload's inputs in HBM, times its step and returns the
+    result record (the headline line's keys)."""
     import numpy as np
     import torch
 
@@ -178,7 +286,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     over = {k: v for k, v in (("ctx_len", args.ctx_len), ("batch", args.batch)) if v is not None}
-    cfg = R.get_config(args.config, **over)
+    cfg = R.get_config(cfg_name, **over) if headline else R.get_config(cfg_name)
     log(f"config {cfg}")
     t0 = time.time()
     hi = R.HostInputs(cfg, with_weights=(cfg.d_model > 0 and not args.no_label))
@@ -194,21 +302,23 @@ def main():
                      dtype=k.dtype, device="cuda")
     log(f"inputs resident ({(k.numel() + v.numel()) * k.element_size() / 1e9:.1f} GB cache) in {time.time() - t0:.1f}s")
 
-    # reference: a plain elementwise copy of known size (reads and writes
-    # calib-bytes each); its rate is the measured stream bandwidth, and under
-    # rocprofv3 its FETCH_SIZE/WRITE_SIZE calibrate the counters
-    cal_x = torch.ones(args.calib_bytes // 4, dtype=torch.float32, device="cuda")
-    cal_y = torch.empty_like(cal_x)
-    torch.neg(cal_x, out=cal_y)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(5):
+    copy_gbps = None
+    if headline:
+        # reference: a plain elementwise copy of known size (reads and writes
+        # calib-bytes each); its rate is the measured stream bandwidth, and under
+        # rocprofv3 its FETCH_SIZE/WRITE_SIZE calibrate the counters
+        cal_x = torch.ones(args.calib_bytes // 4, dtype=torch.float32, device="cuda")
+        cal_y = torch.empty_like(cal_x)
         torch.neg(cal_x, out=cal_y)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * args.calib_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del cal_x, cal_y
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            torch.neg(cal_x, out=cal_y)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * args.calib_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del cal_x, cal_y
 
     # cache-write-time packing of the dominant key channels (timed separately)
     H.timing_enable(True)
@@ -261,6 +371,11 @@ def main():
 
     out = torch.empty((cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.d_head), dtype=torch.float32, device="cuda")
     sequential = cfg.clsa and args.clsa_mode == "sequential"
+    # steps rotate over copies of the cache until the bytes they touch exceed
+    # the 256 MB memory-side cache (MALL) with room to spare, so that no step
+    # finds the previous step's rows there: c1 64 copies, c2 4, c3 2, c4 1
+    ab0 = algorithmic_bytes(cfg, None if cfg.clsa else labels_np)
+    n_rep = max(1, -(-int(REPLICA_TOUCH_BYTES) // ab0["total"]))
     per_head = args.select == "per-head" and not cfg.clsa
     split = args.cache in ("split", "split-host") and not cfg.clsa and not per_head
     cache_info = None
@@ -337,9 +452,13 @@ def main():
     elif cfg.clsa:
         k0, v0, kd0, id0 = k[0], v[0], kd[0], i_dom[0]
         ws = H.shared_index_decode(dims, q, k0, v0, kd0, id0, out, labels=None)
+        reps = [(k0, v0, kd0)] + [(k0.clone(), v0.clone(), kd0.clone()) for _ in range(n_rep - 1)]
+        turn = [0]
 
         def step():
-            H.shared_index_decode(dims, q, k0, v0, kd0, id0, out, labels=None, ws=ws)
+            kr, vr, kdr = reps[turn[0] % n_rep]
+            turn[0] += 1
+            H.shared_index_decode(dims, q, kr, vr, kdr, id0, out, labels=None, ws=ws)
     elif per_head:
         ws = H.sparse_decode_step_per_head(dims, q, k, v, kd, i_dom, labels, out)
 
@@ -347,9 +466,13 @@ def main():
             H.sparse_decode_step_per_head(dims, q, k, v, kd, i_dom, labels, out, ws=ws)
     else:
         ws = H.sparse_decode_step(dims, q, k, v, kd, i_dom, labels, out)
+        reps = [(k, v, kd)] + [(k.clone(), v.clone(), kd.clone()) for _ in range(n_rep - 1)]
+        turn = [0]
 
         def step():
-            H.sparse_decode_step(dims, q, k, v, kd, i_dom, labels, out, ws=ws)
+            kr, vr, kdr = reps[turn[0] % n_rep]
+            turn[0] += 1
+            H.sparse_decode_step(dims, q, kr, vr, kdr, i_dom, labels, out, ws=ws)
 
     for _ in range(args.warmup):
         step()
@@ -534,7 +657,7 @@ def main():
         "tokens_scored_per_s": round(n_scored / (ms * 1e-3), 1),
         "kernels_ms": {n: round(t, 5) for n, t in kernels_ms.items()},
         "kdom_pack_ms": round(kdom_ms, 4),
-        "measured_copy_GBps": round(copy_gbps, 1),
+        "measured_copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "label": label_info,
     }
     if graph_info is not None:
@@ -548,11 +671,16 @@ def main():
         res["cache"] = cache_info
     if split_extra is not None:
         res["split_cache"] = split_extra
-    if not args.no_cpu_baseline and not cfg.clsa:
-        nr, ns = (int(x) for x in args.cpu_sample.split(","))
+    res["replicas"] = n_rep if not (split or sequential or per_head) else 1
+    if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the step")
-        res["cpu_baseline"] = cpu_baseline(cfg, hi, labels_np, nr, ns, args.cpu_reps)
-    print(json.dumps(res), flush=True)
+        if cfg.clsa:
+            res["cpu_baseline"] = cpu_baseline_clsa(cfg, hi, max(1, args.cpu_reps // 2))
+        else:
+            nr, ns = (int(x) for x in args.cpu_sample.split(","))
+            res["cpu_baseline"] = cpu_baseline(cfg, hi, labels_np, nr, ns, args.cpu_reps)
+        log(f"cpu baseline {res['cpu_baseline']}")
+    return res
 
 
 if __name__ == "__main__":
