@@ -167,6 +167,14 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
                    g.samp_rank < has::kSampleTokens / 2) ? 1 : 0;
   }
   g.cand_cap = g.prefilter ? has::kCandFast : (g.T < has::kCandLds ? g.T : has::kCandLds);
+  // The shared-index attention units find their item's cut themselves when
+  // the token bitmap fits their LDS beside the expected candidates (at most
+  // 70% of the slots they hold; more are read from global memory).
+  {
+    const double expect = (double)g.samp_rank / has::kSampleTokens * g.T;
+    g.fuse_sel = (g.clsa_mfma && g.prefilter && g.T <= has::kShortMaxT && g.n_fac < 65536 &&
+                  expect <= 0.7 * has::kFusedSelCand) ? 1 : 0;
+  }
   // prefiltered scoring units: about 2048 over the worst-case item count,
   // between 1024 and 16384 tokens
   g.ct_tip = clampi(pow2_floor((long long)g.T * n_idx / 2048), 1024, 16384);

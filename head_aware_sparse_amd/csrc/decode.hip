@@ -431,8 +431,10 @@ __global__ __launch_bounds__(NT) void tau_kernel(Geo g) {
 // writes 64 consecutive scores.
 // MODE 0: every score and a histogram (general path); 1: prefiltered, tau
 // from tau_kernel; 2: prefiltered, each unit derives tau from the sampled
-// keys itself (steps with few index items, where a separate launch costs
-// more than the redundant work), unit 0 of the item storing it.
+// keys itself (steps with few scoring units, where a separate launch costs
+// more than the redundant work), unit 0 of the item storing it; 3: as 2,
+// with the unit's first ring loads issued before tau is derived, so they
+// are in flight meanwhile (steps with more units, up to kTauInlineUnitsMax).
 // HG > 1 (prefiltered with a tau launch, per-query-head selection): the HG
 // index items of one KV group's heads share a unit, so the group's dominant
 // key rows are read once and scored against HG queries, each head with its
@@ -441,6 +443,7 @@ template <typename E, int V, int MODE, int HG = 1>
 __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
   constexpr bool PF = MODE != 0;
   static_assert(HG == 1 || MODE == 1, "heads share units only with a tau launch");
+  static_assert(MODE >= 0 && MODE <= 3, "scoring modes 0-3");
   constexpr int EPV = Vec<E>::N;
   constexpr int U = V >= 8 ? 2 : 16 / V;  // 64-token steps in flight per wave (16 loads per lane)
   __shared__ uint32_t s_hist[PF ? 1 : kHistBins];
@@ -460,6 +463,7 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     const int unit_item = u / nch, ch = u - unit_item * nch;
     __syncthreads();
+    uint4 ring0[U][V];  // the prefiltered ring (MODE 3 fills it before tau)
     float qr[HG][EPV];
     int item[HG];  // index items of the unit (the heads' items when HG > 1)
     size_t slice;
@@ -478,7 +482,20 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) qr[h][e] = qb[e];
       }
-      if constexpr (MODE == 2) {
+      if constexpr (MODE == 3) {
+        const E* kd0 = (const E*)g.kdom + slice * (size_t)g.tstride * R;
+        const int tt0 = ch * ct, tt1 = min(g.T, tt0 + ct);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            const int tok = min(tt0 + wave * 64 + j * NT + i * (64 / V) + lane / V, tt1 - 1);
+            ring0[j][i] = ld16_stream(kd0 + (size_t)tok * R + (lane % V) * EPV);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (MODE >= 2) {
         __shared__ int s_w2[2 * NWAVE];
         __shared__ uint32_t s_res2[2];
         static_assert(kCandUnit * sizeof(uint2) >= kHistBins * sizeof(uint32_t), "tau histogram in s_cand");
@@ -538,13 +555,15 @@ __global__ __launch_bounds__(NT) void tip_kernel(Geo g) {
           raw[i] = ld16_stream(kd + (size_t)tok * R + (lane % V) * EPV);
         }
       };
-      uint4 ring[UR][V];
+      uint4 (&ring)[UR][V] = ring0;
       // issued in ring order (the scheduler may not reorder them), so each
       // step's wait leaves the later steps' loads in flight
+      if constexpr (MODE != 3) {
 #pragma unroll
-      for (int j = 0; j < UR; ++j) {
-        ld_step(ring[j], wbase0 + j * NT);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < UR; ++j) {
+          ld_step(ring[j], wbase0 + j * NT);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       for (int base = wbase0; base < t1; base += NT * UR) {
 #pragma unroll
@@ -1745,6 +1764,9 @@ typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kClsaPad = 136;          // bf16 elements per K/V/Q LDS row (128 + 16 B of padding)
 constexpr int kPPad = kClsaRows + 4;   // floats per P row (16-byte aligned rows)
+constexpr int kClsaTileBytes = kClsaRows * kClsaPad * 2;  // one K or V tile in LDS
+constexpr int kClsaQBytes = 32 * kClsaPad * 2;            // the query tile
+constexpr int kClsaLdsBytes = 2 * kClsaTileBytes + kClsaQBytes;
 
 // bf16 bits of x rounded to nearest even (x finite)
 __device__ __forceinline__ unsigned short bf16_rne(float x) {
@@ -1752,20 +1774,179 @@ __device__ __forceinline__ unsigned short bf16_rne(float x) {
   return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-__global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
+// The attention of one unit over its nrows gathered rows, whose cache
+// positions rows(r) gives (r < nrows; values in [0, T)), into the chunk
+// partials.  qreg holds this thread's two 16-byte pieces of the query tile
+// (see clsa_load_q), already loaded.  lds: kClsaLdsBytes, 16-byte aligned;
+// s_ml/s_lab small LDS arrays.  The caller synchronises before the call when
+// lds was in other use.
+__device__ __forceinline__ void clsa_load_q(const Geo& g, int b, int gi, uint4 (&qreg)[2]) {
+  constexpr int D = 128;
+  const int QV = g.Lq * g.G;
+  static_assert(32 * 16 == 2 * NT, "two query elements per thread");
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = threadIdx.x + i * NT, qv = min(e >> 4, QV - 1), part = e & 15;
+    const int n = qv / g.G, h = qv - n * g.G;
+    qreg[i] = ld16((const uint16_t*)g.q + (((size_t)n * g.B + b) * g.Hq + (size_t)gi * g.G + h) * D + part * 8);
+  }
+}
+
+template <class Rows>
+__device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, int chunk, int nrows, Rows rows,
+                                                 const uint4 (&qreg)[2], unsigned char* lds, float (*s_ml)[2],
+                                                 uint8_t* s_lab) {
   constexpr int D = 128;
   constexpr int ROWS = kClsaRows;
   constexpr float kScale = 0.08838834764831845f * 1.4426950408889634f;
-  static_assert(32 * kPPad * sizeof(float) <= ROWS * kClsaPad * sizeof(uint16_t), "P fits the K tile");
-  __shared__ __attribute__((aligned(16))) uint16_t s_kp[ROWS * kClsaPad];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[ROWS][kClsaPad];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[32][kClsaPad];
-  __shared__ float s_ml[32][2];
-  __shared__ uint8_t s_lab[32];  // per query vector: its layer attends (retrieval label)
-  uint16_t (*s_k)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(s_kp);
-  float (*s_p)[kPPad] = reinterpret_cast<float (*)[kPPad]>(s_kp);
+  static_assert(32 * kPPad * sizeof(float) <= kClsaTileBytes, "P fits the K tile");
+  uint16_t (*s_k)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(lds);
+  float (*s_p)[kPPad] = reinterpret_cast<float (*)[kPPad]>(lds);
+  uint16_t (*s_v)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(lds + kClsaTileBytes);
+  uint16_t (*s_q)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(lds + 2 * kClsaTileBytes);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int QV = g.Lq * g.G;
+  const size_t kvs = (size_t)b * g.Hkv + gi;
+  const uint16_t* kb = (const uint16_t*)g.k + kvs * (size_t)g.T * D;
+  const uint16_t* vb = (const uint16_t*)g.v + kvs * (size_t)g.T * D;
+  // every K and V element of the tile (16 bytes per element e = row * 16 +
+  // part) is loaded unconditionally (rows past the end read the last valid
+  // one, then store zeros), so the loads issue as one group
+  static_assert(ROWS * 16 == 8 * NT, "eight tile elements per thread");
+  int rowi[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    // positions come from the selection and lie in [0, T); the clamp only
+    // keeps a corrupted index from turning into out-of-range reads
+    const int r = min((tid + u * NT) >> 4, nrows - 1);
+    rowi[u] = min(max(rows(r), 0), g.T - 1);
+  }
+  uint4 rk[8], rv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + u * NT;
+    rk[u] = ld16_stream(kb + (size_t)rowi[u] * D + (e & 15) * 8);
+    rv[u] = ld16_stream(vb + (size_t)rowi[u] * D + (e & 15) * 8);
+  }
+  if (tid < 32) s_lab[tid] = tid < QV ? (uint8_t)label_at(g, (tid / g.G) * g.Hkv + gi) : (uint8_t)0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + i * NT;
+    *reinterpret_cast<uint4*>(&s_q[e >> 4][(e & 15) * 8]) = (e >> 4) < QV ? qreg[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + u * NT, r = e >> 4;
+    const bool live = r < nrows;
+    *reinterpret_cast<uint4*>(&s_k[r][(e & 15) * 8]) = live ? rk[u] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&s_v[r][(e & 15) * 8]) = live ? rv[u] : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  // S = Q K^T for row block `wave`, then (the K tile being free) into s_p
+  {
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const int kofs = (lane >> 5) * 8;
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s_q[lane & 31][k0 + kofs]);
+      const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&s_k[wave * 32 + (lane & 31)][k0 + kofs]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+    }
+    __syncthreads();
+    const int row = wave * 32 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qv = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      s_p[qv][row] = row < nrows ? acc[r] * kScale : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // softmax: 8 consecutive lanes per query vector, 16 rows each
+  {
+    const int qv = tid >> 3, seg = tid & 7;
+    float4* pr = reinterpret_cast<float4*>(&s_p[qv][seg * 16]);
+    float z[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v4 = pr[i];
+      z[4 * i] = v4.x;
+      z[4 * i + 1] = v4.y;
+      z[4 * i + 2] = v4.z;
+      z[4 * i + 3] = v4.w;
+    }
+    float m = z[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, z[i]);
+    m = group_max<8>(m);
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      z[i] = exp2f(z[i] - m);
+      l += z[i];
+    }
+    l = group_sum<8>(l);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = make_float4(z[4 * i], z[4 * i + 1], z[4 * i + 2], z[4 * i + 3]);
+    if (seg == 0) {
+      s_ml[qv][0] = m;
+      s_ml[qv][1] = l;
+    }
+  }
+  __syncthreads();
+  // O = P V for channel block `wave`, P split into bf16 hi + lo
+  f32x16_t o;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[r] = 0.f;
+  {
+    const int dcol = wave * 32 + (lane & 31), ks = (lane >> 5) * 8;
+#pragma unroll 2
+    for (int k0 = 0; k0 < ROWS; k0 += 16) {
+      const float4 p0 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks]);
+      const float4 p1 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks + 4]);
+      const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      u16x8_t hi, lo, vv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned short h = bf16_rne(pv[i]);
+        hi[i] = h;
+        lo[i] = bf16_rne(pv[i] - __uint_as_float((uint32_t)h << 16));
+        vv[i] = s_v[k0 + ks + i][dcol];
+      }
+      const bf16x8_t vb8 = __builtin_bit_cast(bf16x8_t, vv);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, hi), vb8, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lo), vb8, o, 0, 0, 0);
+    }
+  }
+  // partials: acc for (layer, head) = qv, channel block `wave`
+  {
+    const int dcol = wave * 32 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qv = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (s_lab[qv]) {  // 0 past QV
+        const int n = qv / g.G, h = qv - n * g.G;
+        const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
+        g.part[(((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4) + dcol] = o[r];
+      }
+    }
+  }
+  if (tid < QV && s_lab[tid]) {
+    const int n = tid / g.G, h = tid - n * g.G;
+    const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
+    float* pp = g.part + (((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4);
+    pp[D] = s_ml[tid][0];
+    pp[D + 1] = s_ml[tid][1];
+  }
+}
+
+// The shared-index attention over an index already in g.idx (the final
+// kernel's, or a caller's for fac_attend).
+__global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_lds[kClsaLdsBytes];
+  __shared__ float s_ml[32][2];
+  __shared__ uint8_t s_lab[32];  // per query vector: its layer attends (retrieval label)
   const int J = g.Hkv * g.B * g.nch_f;
   for (int j = blockIdx.x; j < J; j += gridDim.x) {
     const int chunk = j % g.nch_f;
@@ -1774,150 +1955,268 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
     const size_t iitem = g.idx_bmajor ? (size_t)b * g.Hkv + gi : (size_t)gi * g.B + b;
     const int32_t* ix = g.idx + iitem * g.n_fac + (size_t)chunk * g.cf;
     const int nrows = min(g.cf, g.n_fac - chunk * g.cf);
-    const size_t kvs = (size_t)b * g.Hkv + gi;
-    const uint16_t* kb = (const uint16_t*)g.k + kvs * (size_t)g.T * D;
-    const uint16_t* vb = (const uint16_t*)g.v + kvs * (size_t)g.T * D;
     __syncthreads();
-    // Query vectors qv = n * G + h first (zero rows past QV), then the row
-    // indices, then every K and V element of the tile (16 bytes per element
-    // e = row * 16 + part): all loads are unconditional (rows past the end
-    // and query rows past QV read the last valid one, then store zeros), so
-    // each group is issued whole and the three latencies are paid once each.
-    static_assert(32 * 16 == 2 * NT, "two query elements per thread");
-    static_assert(ROWS * 16 == 8 * NT, "eight tile elements per thread");
     uint4 qreg[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + i * NT, qv = min(e >> 4, QV - 1), part = e & 15;
-      const int n = qv / g.G, h = qv - n * g.G;
-      qreg[i] = ld16((const uint16_t*)g.q + (((size_t)n * g.B + b) * g.Hq + (size_t)gi * g.G + h) * D + part * 8);
+    clsa_load_q(g, b, gi, qreg);
+    clsa_attend_unit(g, b, gi, chunk, nrows, [&](int r) { return ix[r]; }, qreg, s_lds, s_ml, s_lab);
+  }
+}
+
+// Elements for the selection fused into the attention: (key, token) pairs
+// through a generic pointer (LDS, or global memory when an item's
+// candidates do not fit there), or an item's whole score row.  One type for
+// the three cases, so the threshold helpers (and their LDS) are instantiated
+// once; four reads in flight per thread.
+template <int BT = NT>
+struct SelSrcT {
+  const uint2* pairs;  // null: the score row sc
+  const float* sc;
+  int n;
+  template <class F>
+  __device__ __forceinline__ void for_each(F f) const {
+    int i = threadIdx.x;
+    if (pairs) {
+      for (; i + 3 * BT < n; i += 4 * BT) {
+        const uint2 a = pairs[i], b = pairs[i + BT], c = pairs[i + 2 * BT], d = pairs[i + 3 * BT];
+        f(a.x, a.y);
+        f(b.x, b.y);
+        f(c.x, c.y);
+        f(d.x, d.y);
+      }
+      for (; i < n; i += BT) f(pairs[i].x, pairs[i].y);
+    } else {
+      for (; i + 3 * BT < n; i += 4 * BT) {
+        const float a = sc[i], b = sc[i + BT], c = sc[i + 2 * BT], d = sc[i + 3 * BT];
+        f(f2key(a), (uint32_t)i);
+        f(f2key(b), (uint32_t)(i + BT));
+        f(f2key(c), (uint32_t)(i + 2 * BT));
+        f(f2key(d), (uint32_t)(i + 3 * BT));
+      }
+      for (; i < n; i += BT) f(f2key(sc[i]), (uint32_t)i);
     }
-    int rowi[8];
+  }
+};
+
+// Selection fused into the shared-index attention (prefiltered path, T <=
+// kShortMaxT): every unit (sequence, group, chunk) finds its item's exact
+// top-n_fac cut from the candidates itself -- the item's units repeat the
+// same deterministic work side by side instead of waiting for one final
+// workgroup -- then takes the selected tokens whose ascending rank falls in
+// its chunk, writes those idx_out entries, and attends over them.
+//   1. candidates -> LDS (from global memory when more than fit), counted
+//      in 2048 bins of (key - tau) >> sh as in the final kernel;
+//   2. the bin holding the n_fac-th candidate; its members (<= kRankMax)
+//      ranked directly, else the general radix threshold: the cut (k*, t*);
+//      every selected token is marked in a token bitmap;
+//   3. exclusive prefix counts of the bitmap words (u16);
+//   4. thread r finds rank r0 + r: the last word whose prefix count is at
+//      most that rank, then the set bit of that order inside the word.
+// With fewer than n_fac candidates or an overflow, the unit rescores the
+// item in full (every unit of the item writes the same score row) and
+// selects from it: exact either way.
+constexpr int kSelBitmapWords = kShortMaxT / 32;                      // 4096
+constexpr int kSelHistBytes = kHistBins * 4;                          // 8 KB: histogram, later u16 prefixes
+constexpr int kSelListBytes = kRankMax * 8;                           // 2 KB
+constexpr int kSelCandOfs = kSelHistBytes + kSelListBytes + kSelBitmapWords * 4;
+constexpr int kSelCandLds = (kClsaLdsBytes - kSelCandOfs) / 8;        // candidates held in LDS
+static_assert(kSelBitmapWords * 2 <= kSelHistBytes, "u16 prefixes fit the histogram");
+static_assert(kSelCandLds == kFusedSelCand, "the host sizes the fused selection with this capacity");
+static_assert(kClsaRows <= NT, "one thread per row of a unit");
+
+// The bit position of the k-th set bit (0-based, k < popcount) of x.
+__device__ __forceinline__ int nth_set_bit(uint32_t x, int k) {
+  int pos = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      // indices come from the selection and lie in [0, T); the clamp only
-      // keeps a corrupted workspace from turning into out-of-range reads
-      const int r = min((tid + u * NT) >> 4, nrows - 1);
-      rowi[u] = min(max(ix[r], 0), g.T - 1);
+  for (int half = 16; half >= 1; half >>= 1) {
+    const uint32_t low = x & ((1u << half) - 1u);
+    const int c = __popc(low);
+    if (k >= c) {
+      k -= c;
+      x >>= half;
+      pos += half;
+    } else {
+      x = low;
     }
-    uint4 rk[8], rv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + u * NT;
-      rk[u] = ld16_stream(kb + (size_t)rowi[u] * D + (e & 15) * 8);
-      rv[u] = ld16_stream(vb + (size_t)rowi[u] * D + (e & 15) * 8);
-    }
-    if (tid < 32) s_lab[tid] = tid < QV ? (uint8_t)label_at(g, (tid / g.G) * g.Hkv + gi) : (uint8_t)0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + i * NT;
-      *reinterpret_cast<uint4*>(&s_q[e >> 4][(e & 15) * 8]) = (e >> 4) < QV ? qreg[i] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + u * NT, r = e >> 4;
-      const bool live = r < nrows;
-      *reinterpret_cast<uint4*>(&s_k[r][(e & 15) * 8]) = live ? rk[u] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&s_v[r][(e & 15) * 8]) = live ? rv[u] : make_uint4(0, 0, 0, 0);
-    }
+  }
+  return pos;
+}
+
+__global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
+  constexpr int BT = NT;
+  __shared__ __attribute__((aligned(16))) unsigned char s_lds[kClsaLdsBytes];
+  __shared__ float s_ml[32][2];
+  __shared__ uint8_t s_lab[32];
+  __shared__ int s_rows[kClsaRows];
+  __shared__ int s_w[NWAVE];
+  __shared__ uint32_t s_res[2];
+  __shared__ int s_m;
+  uint32_t* s_hist = reinterpret_cast<uint32_t*>(s_lds);
+  uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_lds);
+  uint2* s_list = reinterpret_cast<uint2*>(s_lds + kSelHistBytes);
+  uint32_t* s_bm = reinterpret_cast<uint32_t*>(s_lds + kSelHistBytes + kSelListBytes);
+  uint2* s_c = reinterpret_cast<uint2*>(s_lds + kSelCandOfs);
+  float* s_qd = reinterpret_cast<float*>(s_lds + kSelCandOfs);  // rescoring only: the group query
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the bitmap always spans kShortMaxT tokens (the words past T stay 0), so
+  // the prefix scan below has a fixed shape
+  constexpr int nrow64 = kSelBitmapWords / (64 * NWAVE);  // 64-word rows per wave
+  constexpr int nwords = kSelBitmapWords;
+  const int J = g.Hkv * g.B * g.nch_f;
+  for (int j = blockIdx.x; j < J; j += gridDim.x) {
+    const int chunk = j % g.nch_f;
+    const int r2 = j / g.nch_f;
+    const int b = r2 % g.B, gi = r2 / g.B;
+    const int item = gi * g.B + b;  // index item (pidx = gi in the shared-index mode)
+    const int r0 = chunk * g.cf;
+    const int nrows = min(g.cf, g.n_fac - r0);
+    int32_t* ox = g.idx_out ? g.idx_out + ((size_t)b * g.Hkv + gi) * g.n_fac : nullptr;
     __syncthreads();
-    // S = Q K^T for row block `wave`, then (the K tile being free) into s_p
-    {
-      f32x16_t acc;
+    uint4 qreg[2];
+    clsa_load_q(g, b, gi, qreg);  // in flight during the selection
+    const uint32_t count = g.info[(size_t)item * 4 + 2];
+    const uint2 th = g.tau[item];
+    for (int w = tid; w < nwords; w += BT) s_bm[w] = 0u;
+    for (int i = tid; i < kHistBins; i += BT) s_hist[i] = 0u;
+    if (tid == 0) s_m = 0;
+    auto mark = [&](uint32_t t) { atomicOr(&s_bm[t >> 5], 1u << (t & 31)); };
+    // the general cut (key desc, token asc) over any source, every selected
+    // token marked
+    auto cut_general = [&](const SelSrcT<BT>& src) {
+      uint32_t kstar, tstar;
+      exact_threshold<BT>(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+      src.for_each([&](uint32_t k, uint32_t t) {
+        if (k > kstar || (k == kstar && t <= tstar)) mark(t);
+      });
+    };
+    // the cut inside the first-digit bin `ub` that holds the n_fac-th
+    // candidate: everything above it is selected, its members (m <=
+    // kRankMax) are ranked against each other
+    auto cut_binned = [&](const auto& src, uint32_t tau, int sh, uint32_t ub, uint32_t above) {
+      src.for_each([&](uint32_t k, uint32_t t) {
+        const uint32_t d = min((k - tau) >> sh, (uint32_t)kHistBins - 1u);
+        if (d > ub) mark(t);
+        const bool mem = d == ub;
+        const uint64_t bal = __ballot(mem);
+        if (bal) {  // one reservation per wave, by its first active lane (the
+                    // strided loop's tail runs with part of the wave)
+          const int leader = __builtin_amdgcn_readfirstlane(lane);
+          int base = 0;
+          if (lane == leader) base = atomicAdd(&s_m, __popcll(bal));
+          base = __builtin_amdgcn_readfirstlane(base);
+          if (mem) s_list[base + mbcnt(bal)] = make_uint2(k, t);
+        }
+      });
+      __syncthreads();
+      const uint32_t need = (uint32_t)g.n_fac - above;
+      const int m = s_m;
+      for (int i = tid; i < m; i += BT) {
+        const uint2 me = s_list[i];
+        uint32_t r = 0;
+#pragma unroll 8
+        for (int q = 0; q < m; ++q) {
+          const uint2 o = s_list[q];
+          r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+        }
+        if (r < need) mark(me.y);
+      }
+    };
+    if (count >= (uint32_t)g.n_fac && count <= (uint32_t)g.cand_cap) {
+      const uint32_t tau = th.x;
+      const uint32_t span = th.y > tau ? th.y - tau : 0u;
+      const int bits = span ? 32 - __clz(span) : 0;
+      const int sh = bits > 11 ? bits - 11 : 0;
+      const bool in_lds = count <= (uint32_t)kSelCandLds;
+      const uint2* gc = g.cand + (size_t)item * g.cand_cap;
+      __syncthreads();
+      // candidates -> LDS when they fit, counted by their first digit
+      const uint4* c4 = reinterpret_cast<const uint4*>(gc);
+      const int n4 = (int)(count + 1) / 2;
+      for (int i0 = tid; i0 < n4; i0 += 8 * BT) {
+        uint4 r[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      const int kofs = (lane >> 5) * 8;
+        for (int q = 0; q < 8; ++q) r[q] = i0 + q * BT < n4 ? c4[i0 + q * BT] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 16) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s_q[lane & 31][k0 + kofs]);
-        const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&s_k[wave * 32 + (lane & 31)][k0 + kofs]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+        for (int q = 0; q < 8; ++q) {
+          const int i = i0 + q * BT;
+          if (i < n4) {
+            if (in_lds) s_c[2 * i] = make_uint2(r[q].x, r[q].y);
+            atomicAdd(&s_hist[min((r[q].x - tau) >> sh, (uint32_t)kHistBins - 1u)], 1u);
+            if (2 * i + 1 < (int)count) {
+              if (in_lds) s_c[2 * i + 1] = make_uint2(r[q].z, r[q].w);
+              atomicAdd(&s_hist[min((r[q].z - tau) >> sh, (uint32_t)kHistBins - 1u)], 1u);
+            }
+          }
+        }
       }
       __syncthreads();
-      const int row = wave * 32 + (lane & 31);
+      int bin;
+      uint32_t above;
+      find_bin_top<BT>(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, bin, above);
+      const uint32_t members = s_hist[bin];
+      __syncthreads();
+      const SelSrcT<BT> gsrc{in_lds ? s_c : gc, nullptr, (int)count};
+      if (bin < kHistBins - 1 && members <= (uint32_t)kRankMax) {
+        if (in_lds)
+          cut_binned(LdsPairsT<BT>{s_c, (int)count}, tau, sh, (uint32_t)bin, above);
+        else
+          cut_binned(gsrc, tau, sh, (uint32_t)bin, above);
+      } else {
+        cut_general(gsrc);
+      }
+    } else {
+      // rescoring: the item's full score row (the same values from every unit)
+      __syncthreads();
+      const size_t slice = group_query_dom<uint16_t>(g, item, s_qd);
+      __syncthreads();
+      const uint16_t* kd = (const uint16_t*)g.kdom + slice * (size_t)g.tstride * g.R;
+      float* sc = g.scores + (size_t)item * g.Ts;
+      for (int t = tid; t < g.T; t += BT) sc[t] = score_one<uint16_t>(kd + (size_t)t * g.R, s_qd, g.R);
+      __threadfence();
+      __syncthreads();
+      cut_general(SelSrcT<BT>{nullptr, sc, g.T});
+    }
+    __syncthreads();
+    // exclusive prefix counts of the bitmap words: each wave a contiguous
+    // quarter, lane L on word L of each 64-word row; the rows' scans are
+    // independent, then carried through
+    {
+      const uint32_t* wb = s_bm + wave * nrow64 * 64;
+      uint32_t x[nrow64], inc[nrow64];
+      uint32_t tot = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qv = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        s_p[qv][row] = row < nrows ? acc[r] * kScale : -INFINITY;
+      for (int k = 0; k < nrow64; ++k) {
+        x[k] = (uint32_t)__popc(wb[k * 64 + lane]);
+        inc[k] = wave_incl_scan_u(x[k]);
+        tot += (uint32_t)__builtin_amdgcn_readlane((int)inc[k], 63);
+      }
+      if (lane == 0) s_w[wave] = (int)tot;
+      __syncthreads();  // the histogram (aliased by the prefixes) is free since the cut
+      uint32_t carry = 0;
+      for (int w = 0; w < wave; ++w) carry += (uint32_t)s_w[w];
+      uint16_t* wp = s_pre + wave * nrow64 * 64;
+#pragma unroll
+      for (int k = 0; k < nrow64; ++k) {
+        wp[k * 64 + lane] = (uint16_t)(carry + inc[k] - x[k]);
+        carry += (uint32_t)__builtin_amdgcn_readlane((int)inc[k], 63);
       }
     }
     __syncthreads();
-    // softmax: 8 consecutive lanes per query vector, 16 rows each
-    {
-      const int qv = tid >> 3, seg = tid & 7;
-      float4* pr = reinterpret_cast<float4*>(&s_p[qv][seg * 16]);
-      float z[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 v4 = pr[i];
-        z[4 * i] = v4.x;
-        z[4 * i + 1] = v4.y;
-        z[4 * i + 2] = v4.z;
-        z[4 * i + 3] = v4.w;
+    // rank r0 + tid: the last word whose prefix count is at most it, then
+    // the set bit of that order inside the word
+    if (tid < nrows) {
+      const uint32_t rank = (uint32_t)(r0 + tid);
+      int lo = 0, hi = nwords - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((uint32_t)s_pre[mid] <= rank) lo = mid;
+        else hi = mid - 1;
       }
-      float m = z[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) m = fmaxf(m, z[i]);
-      m = group_max<8>(m);
-      float l = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        z[i] = exp2f(z[i] - m);
-        l += z[i];
-      }
-      l = group_sum<8>(l);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = make_float4(z[4 * i], z[4 * i + 1], z[4 * i + 2], z[4 * i + 3]);
-      if (seg == 0) {
-        s_ml[qv][0] = m;
-        s_ml[qv][1] = l;
-      }
+      const int t = lo * 32 + nth_set_bit(s_bm[lo], (int)(rank - s_pre[lo]));
+      s_rows[tid] = t;
+      if (ox) ox[rank] = t;
     }
     __syncthreads();
-    // O = P V for channel block `wave`, P split into bf16 hi + lo
-    f32x16_t o;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[r] = 0.f;
-    {
-      const int dcol = wave * 32 + (lane & 31), ks = (lane >> 5) * 8;
-#pragma unroll 2
-      for (int k0 = 0; k0 < ROWS; k0 += 16) {
-        const float4 p0 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks]);
-        const float4 p1 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks + 4]);
-        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        u16x8_t hi, lo, vv;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const unsigned short h = bf16_rne(pv[i]);
-          hi[i] = h;
-          lo[i] = bf16_rne(pv[i] - __uint_as_float((uint32_t)h << 16));
-          vv[i] = s_v[k0 + ks + i][dcol];
-        }
-        const bf16x8_t vb8 = __builtin_bit_cast(bf16x8_t, vv);
-        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, hi), vb8, o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lo), vb8, o, 0, 0, 0);
-      }
-    }
-    // partials: acc for (layer, head) = qv, channel block `wave`
-    {
-      const int dcol = wave * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qv = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (s_lab[qv]) {  // 0 past QV
-          const int n = qv / g.G, h = qv - n * g.G;
-          const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
-          g.part[(((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4) + dcol] = o[r];
-        }
-      }
-    }
-    if (tid < QV && s_lab[tid]) {
-      const int n = tid / g.G, h = tid - n * g.G;
-      const size_t a = ((size_t)n * g.B + b) * g.Hkv + gi;
-      float* pp = g.part + (((a * g.nparts + chunk) * g.G) + h) * (size_t)(D + 4);
-      pp[D] = s_ml[tid][0];
-      pp[D + 1] = s_ml[tid][1];
-    }
+    clsa_attend_unit(g, b, gi, chunk, nrows, [&](int r) { return s_rows[r]; }, qreg, s_lds, s_ml, s_lab);
   }
 }
 
@@ -2177,6 +2476,7 @@ constexpr long long kSideStreamRows = 1LL << 20;
 // Prefiltered scoring units per call (index items x units per item) up to
 // which each unit derives tau itself instead of a separate launch.
 constexpr long long kTauInlineUnits = 512;
+constexpr long long kTauInlineUnitsMax = 4096;
 // Output elements per call from which the merge moves 4 per thread in
 // 16-byte vectors; below, one per thread keeps more threads in flight.
 constexpr long long kMergeVecOutputs = 1LL << 18;
@@ -2224,11 +2524,15 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     if ((e = hipEventRecord(ss.join, ss.side)) != hipSuccess) return e;
   }
   const int grid_tip = clampi(n_idx_items * g.nch_t, 1, g.grid);
-  const bool tau_inline = n_idx_items * g.nch_tip <= kTauInlineUnits;
   const int grid_item = clampi(n_idx_items, 1, g.grid);
   // per-query-head selection: a KV group's hg heads share the sampling and
   // scoring units (bf16 caches, steps with a tau launch)
   const int hg = 1 << g.kv_shift;
+  // tau inside the scoring units: always up to kTauInlineUnits units; up to
+  // kTauInlineUnitsMax (with the ring issued first) when no heads share units
+  const long long units_tip = n_idx_items * g.nch_tip;
+  const bool tau_early = hg == 1 && units_tip > kTauInlineUnits && units_tip <= kTauInlineUnitsMax;
+  const bool tau_inline = units_tip <= kTauInlineUnits || tau_early;
   const int tip_v = g.R * (g.bf16 ? 2 : 4) / 16;
   const bool share = !tau_inline && hg > 1 && g.bf16 && (tip_v == 2 || tip_v == 4 || tip_v == 8);
   const bool share_sample = share && !fuse_plan;  // the plan-building sampler serves one item per unit
@@ -2255,13 +2559,15 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
       if (share)
         e = tip_v == 2 ? launch_tip_heads<2>(g, hg, grid_tip_pf, s)
             : tip_v == 4 ? launch_tip_heads<4>(g, hg, grid_tip_pf, s) : launch_tip_heads<8>(g, hg, grid_tip_pf, s);
+      else if (tau_inline && tau_early)
+        e = g.bf16 ? launch_tip_v<uint16_t, 3>(g, grid_tip_pf, s) : launch_tip_v<float, 3>(g, grid_tip_pf, s);
       else if (tau_inline)
         e = g.bf16 ? launch_tip_v<uint16_t, 2>(g, grid_tip_pf, s) : launch_tip_v<float, 2>(g, grid_tip_pf, s);
       else
         e = g.bf16 ? launch_tip_v<uint16_t, 1>(g, grid_tip_pf, s) : launch_tip_v<float, 1>(g, grid_tip_pf, s);
     }
     if (e != hipSuccess) return e;
-    {
+    if (!g.fuse_sel) {
       KTimer t("select_final", s);
       if (g.T <= kShortMaxT) {
         if (g.bf16) final_kernel<uint16_t, false><<<grid_item, kFinalThreads, 0, s>>>(g);
@@ -2306,7 +2612,13 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     g.attn_mode = with_stream && !g.clsa_mfma ? 0 : 1;
     KTimer t("attention_fac", s);
     if (g.clsa_mfma) {
-      attn_clsa_mfma_kernel<<<clampi((long long)g.Hkv * g.B * g.nch_f, 1, g.grid), NT, 0, s>>>(g);
+      const int grid_c = clampi((long long)g.Hkv * g.B * g.nch_f, 1, g.grid);
+      if (g.fuse_sel) {
+        KTimer ts("select_attend", s);
+        select_attn_clsa_kernel<<<grid_c, NT, 0, s>>>(g);
+      } else {
+        attn_clsa_mfma_kernel<<<grid_c, NT, 0, s>>>(g);
+      }
       e = hipGetLastError();
       if (e == hipSuccess && with_stream) {
         Geo gs = g;

@@ -18,6 +18,7 @@ constexpr int kSampleTokens = 4096;  // tokens scored per item to place the pref
 constexpr int kPrefilterMaxT = 524288;  // token bitmap of the prefiltered path fits the final kernel's LDS
 constexpr int kShortMaxT = 131072;      // up to here the final kernel's token bitmap has an LDS array of its own
 constexpr int kSelMaxLong = 8192;       // beyond kShortMaxT: n_fac the final kernel compacts beside its bitmap
+constexpr int kFusedSelCand = 6464;     // candidates the selection fused into the shared-index attention holds in LDS
 
 // One decode call, with the workspace carved.  Passed by value to kernels.
 struct Geo {
@@ -27,6 +28,7 @@ struct Geo {
   int bf16;         // kv dtype
   int clsa;         // 1: one index per (b, g) shared by Lq layers over one cache
   int clsa_mfma;    // shared-index retrieval attention on the matrix cores (bf16, d 128, 2 <= Lq, Lq*G <= 32)
+  int fuse_sel;     // prefiltered shared-index step: the exact selection runs inside the attention units
   int interleaved;  // rope pairing
   int host_plan;    // shared-index mode, no labels, prefiltered: the plan is implicit (no plan launch)
   // chunking
