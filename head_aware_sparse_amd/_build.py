@@ -2,6 +2,10 @@
 
 libhas.so    the product: C ABI of include/has.h (HIP kernels + host code)
 libsynth.so  the seeded input generator (host + device fill), test/bench input
+tests/_build/libhas_san.so
+             the same sources with AddressSanitizer and UndefinedBehavior-
+             Sanitizer on the host code (device code as usual), for the CPU
+             tests of the argument validation
 """
 import os
 import subprocess
@@ -44,9 +48,34 @@ def build_synth():
     os.replace(SYNTH_LIB + ".tmp", SYNTH_LIB)
 
 
+SAN_LIB = os.path.join(ROOT, "tests", "_build", "libhas_san.so")
+# sanitizers on the host pass only (-Xarch_host before each): the kernels are
+# built as in the product, the validation and launch code is instrumented;
+# undefined behaviour aborts instead of printing and continuing
+SAN_FLAGS = ["-O1", "-g", "-fPIC", "-shared", "-std=c++17", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-shared-libsan",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_has_sanitized():
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    _run([HIPCC, *SAN_FLAGS, "-I", os.path.join(ROOT, "include"), "-x", "hip", *HAS_SOURCES, "-o", SAN_LIB + ".tmp"])
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+
+
+def asan_runtime():
+    """The clang AddressSanitizer runtime the sanitized library links to."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
 def build_all():
     build_synth()
     build_has()
+    build_has_sanitized()
 
 
 if __name__ == "__main__":
