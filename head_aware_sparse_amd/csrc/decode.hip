@@ -160,6 +160,15 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer resource word 3 (data format) for raw 32-bit buffer accesses on
+// gfx9-family parts, and a streaming 16-byte buffer load (nontemporal).
+constexpr int kBufRsrcWord3 = 0x00020000;
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ uint4 buf_load16_stream(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kCachePolicyNT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Index groups are the KV groups, or with kv_shift > 0 the query heads (each
 // selecting its own tokens): (layer, index group) pairs and cache slabs map
 // to the KV group that holds the rows, i_dom and the label.
@@ -1792,7 +1801,10 @@ __device__ __forceinline__ void clsa_load_q(const Geo& g, int b, int gi, uint4 (
   }
 }
 
-template <class Rows>
+// Q_FIRST: the query tile goes to LDS before the row loads are issued (its
+// registers are then free during the gather; the query loads completed
+// earlier); otherwise after them, so its loads overlap theirs.
+template <bool Q_FIRST, class Rows>
 __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, int chunk, int nrows, Rows rows,
                                                  const uint4 (&qreg)[2], unsigned char* lds, float (*s_ml)[2],
                                                  uint8_t* s_lab) {
@@ -1813,27 +1825,37 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
   // part) is loaded unconditionally (rows past the end read the last valid
   // one, then store zeros), so the loads issue as one group
   static_assert(ROWS * 16 == 8 * NT, "eight tile elements per thread");
-  int rowi[8];
+  auto store_q = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + i * NT;
+      *reinterpret_cast<uint4*>(&s_q[e >> 4][(e & 15) * 8]) = (e >> 4) < QV ? qreg[i] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if constexpr (Q_FIRST) store_q();
+  // K and V rows through buffer loads: one 32-bit byte offset per element
+  // serves both slices (their bases sit in scalar resource descriptors), and
+  // the hardware returns zeros past the slice instead of reading outside it
+  const __amdgpu_buffer_rsrc_t k_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), 0,
+                                                                        g.T * D * 2, kBufRsrcWord3);
+  const __amdgpu_buffer_rsrc_t v_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), 0,
+                                                                        g.T * D * 2, kBufRsrcWord3);
+  int off[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     // positions come from the selection and lie in [0, T); the clamp only
-    // keeps a corrupted index from turning into out-of-range reads
+    // keeps a corrupted index from reading another row of the slice
     const int r = min((tid + u * NT) >> 4, nrows - 1);
-    rowi[u] = min(max(rows(r), 0), g.T - 1);
+    off[u] = min(max(rows(r), 0), g.T - 1) * (D * 2) + ((tid + u * NT) & 15) * 16;
   }
   uint4 rk[8], rv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int e = tid + u * NT;
-    rk[u] = ld16_stream(kb + (size_t)rowi[u] * D + (e & 15) * 8);
-    rv[u] = ld16_stream(vb + (size_t)rowi[u] * D + (e & 15) * 8);
+    rk[u] = buf_load16_stream(k_rs, off[u]);
+    rv[u] = buf_load16_stream(v_rs, off[u]);
   }
   if (tid < 32) s_lab[tid] = tid < QV ? (uint8_t)label_at(g, (tid / g.G) * g.Hkv + gi) : (uint8_t)0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = tid + i * NT;
-    *reinterpret_cast<uint4*>(&s_q[e >> 4][(e & 15) * 8]) = (e >> 4) < QV ? qreg[i] : make_uint4(0, 0, 0, 0);
-  }
+  if constexpr (!Q_FIRST) store_q();
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int e = tid + u * NT, r = e >> 4;
@@ -1958,7 +1980,7 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
     __syncthreads();
     uint4 qreg[2];
     clsa_load_q(g, b, gi, qreg);
-    clsa_attend_unit(g, b, gi, chunk, nrows, [&](int r) { return ix[r]; }, qreg, s_lds, s_ml, s_lab);
+    clsa_attend_unit<false>(g, b, gi, chunk, nrows, [&](int r) { return ix[r]; }, qreg, s_lds, s_ml, s_lab);
   }
 }
 
@@ -2131,12 +2153,12 @@ __global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
       // candidates -> LDS when they fit, counted by their first digit
       const uint4* c4 = reinterpret_cast<const uint4*>(gc);
       const int n4 = (int)(count + 1) / 2;
-      for (int i0 = tid; i0 < n4; i0 += 8 * BT) {
-        uint4 r[8];
+      for (int i0 = tid; i0 < n4; i0 += 4 * BT) {
+        uint4 r[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) r[q] = i0 + q * BT < n4 ? c4[i0 + q * BT] : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) r[q] = i0 + q * BT < n4 ? c4[i0 + q * BT] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 4; ++q) {
           const int i = i0 + q * BT;
           if (i < n4) {
             if (in_lds) s_c[2 * i] = make_uint2(r[q].x, r[q].y);
@@ -2216,7 +2238,7 @@ __global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
       if (ox) ox[rank] = t;
     }
     __syncthreads();
-    clsa_attend_unit(g, b, gi, chunk, nrows, [&](int r) { return s_rows[r]; }, qreg, s_lds, s_ml, s_lab);
+    clsa_attend_unit<true>(g, b, gi, chunk, nrows, [&](int r) { return s_rows[r]; }, qreg, s_lds, s_ml, s_lab);
   }
 }
 
