@@ -18,6 +18,9 @@
 //             thread per eigenvalue), sigma = sqrt(max(lambda, 0)) and ER.
 //   finalize  group mean of ER, global rank with ties to the lower index,
 //             labels.
+#include <type_traits>
+#include <utility>
+
 #include "internal.h"
 #include "label.h"
 
@@ -40,7 +43,6 @@ struct LGeo {
   const void* wk;
   float* gram;     // [L*Hq + L*Hkv][d][d]: query heads, then key heads
   double* lscr;    // [L*Hkv][d][d] Cholesky factor of each key head's Gram matrix
-  double* tscr;    // [L*Hq][d][d] scratch for G_Q L
   float* tri;      // [L*Hq][2][d]: diagonal, off-diagonal (fp32)
   float* er_head;  // [L*Hq]
   float* er_group; // [L*Hkv]
@@ -50,7 +52,7 @@ struct LGeo {
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct LabelLayout {
-  size_t gram, lscr, tscr, tri, erh, erg, bytes;
+  size_t gram, lscr, tri, erh, erg, bytes;
 };
 
 LabelLayout label_layout(int L, int Hq, int Hkv, int d) {
@@ -60,8 +62,6 @@ LabelLayout label_layout(int L, int Hq, int Hkv, int d) {
   at = align256(at + (size_t)(L * Hq + L * Hkv) * d * d * 4);
   o.lscr = at;
   at = align256(at + (size_t)L * Hkv * d * d * 8);
-  o.tscr = at;
-  at = align256(at + (size_t)L * Hq * d * d * 8);
   o.tri = at;
   at = align256(at + (size_t)L * Hq * 2 * d * 4);
   o.erh = at;
@@ -203,62 +203,112 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
 }
 
-// Cholesky G_K = L L^T of each key head's Gram matrix (fp64, in LDS), once
-// per (layer, KV group): right-looking, the trailing update tiled 16 x 16
-// over the threads.  Columns whose pivot is not positive (rank-deficient key
-// projections) are zeroed.  L (lower, zeros above) goes to lscr.
+// Sum over the 16 lanes of a DPP row, identical in every lane of the row.
+// In the 16 x 16 thread grids below a row is the 16 tx of one ty.
+__device__ __forceinline__ double row16_sum(double x) {
+  x += dpp_d<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_d<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_d<0x141>(x);  // row_half_mirror
+  x += dpp_d<0x140>(x);  // row_mirror
+  return x;
+}
+
+// f(std::integral_constant<int, B>{}) for B = 0 .. N-1 in turn: code
+// specialised on a 16-wide band B indexes the register blocks statically and
+// skips the blocks that no longer change.
+template <class F, int... B>
+__device__ __forceinline__ void each_band(F&& f, std::integer_sequence<int, B...>) {
+  (f(std::integral_constant<int, B>{}), ...);
+}
+
+// Cholesky G_K = L L^T of each key head's Gram matrix (fp64), once per
+// (layer, KV group), right-looking with the matrix in registers: thread
+// (ty, tx) of a 16 x 16 grid holds rows ty + 16 r and columns tx + 16 c.
+// Step j: the threads holding column j put it in LDS; after one barrier
+// every thread scales its rows' and columns' entries of it by 1/sqrt(pivot)
+// and updates its trailing entries (blocks left of or above column j's band
+// are final and skipped).  Columns whose pivot is not above 1e-12 of the
+// largest diagonal entry (rank-deficient key projections) are zeroed.  L
+// (lower, zeros above) goes to lscr.
 template <int D>
-__global__ __launch_bounds__(NT) void chol_kernel(LGeo g) {
-  constexpr int LD = D + 1;
-  __shared__ double s_m[D * LD];
-  __shared__ double s_ld[D];  // the diagonal of L, written back at the end
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void chol_kernel(LGeo g) {
+  constexpr int BS = D / 16;
+  __shared__ double s_x[2][D];
+  __shared__ double s_max[NWAVE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ty = tid >> 4, tx = tid & 15;
   const int grp = blockIdx.x;  // l*Hkv + gk
   const float* GK = g.gram + (size_t)(g.L * g.Hq + grp) * D * D;
-  double* A = s_m;
-  for (int e = tid; e < D * D; e += NT) A[(e / D) * LD + (e % D)] = (double)GK[e];
+  double a[BS][BS];
+#pragma unroll
+  for (int r = 0; r < BS; ++r)
+#pragma unroll
+    for (int c = 0; c < BS; ++c) a[r][c] = (double)GK[(size_t)(ty + 16 * r) * D + tx + 16 * c];
+  double dm = 0.0;
+#pragma unroll
+  for (int r = 0; r < BS; ++r) dm = fmax(dm, tx == ty ? a[r][r] : 0.0);
+  for (int o = 32; o >= 1; o >>= 1) dm = fmax(dm, __shfl_xor(dm, o));
+  if (lane == 0) s_max[wave] = dm;
   __syncthreads();
-  double dmax = 0.0;
-  for (int i = 0; i < D; ++i) dmax = fmax(dmax, A[i * LD + i]);
-  const double tol = 1e-12 * dmax;
-  for (int j = 0; j < D; ++j) {
-    // the diagonal entry is only read here (its square root is kept apart),
-    // so the column can be scaled without waiting for every thread to read it
-    const double piv = A[j * LD + j];
-    const bool zero = !(piv > tol);
-    const double ljj = zero ? 0.0 : sqrt(piv);
-    const double inv = zero ? 0.0 : 1.0 / ljj;
-    if (tid == 0) s_ld[j] = ljj;
-    for (int i = j + 1 + tid; i < D; i += NT) A[i * LD + j] *= inv;
-    __syncthreads();
-    for (int r = j + 1 + ty; r < D; r += 16) {
-      const double arj = A[r * LD + j];
-      for (int c = j + 1 + tx; c <= r; c += 16) A[r * LD + c] -= arj * A[c * LD + j];
+  for (int w = 0; w < NWAVE; ++w) dm = fmax(dm, s_max[w]);
+  const double tol = 1e-12 * dm;
+  each_band([&](auto band) {
+    constexpr int JB = decltype(band)::value;
+#pragma unroll 1
+    for (int jl = 0; jl < 16; ++jl) {
+      const int j = 16 * JB + jl;
+      double* sx = s_x[j & 1];
+      if (tx == jl) {
+#pragma unroll
+        for (int r = JB; r < BS; ++r) sx[ty + 16 * r] = a[r][JB];
+      }
+      __syncthreads();
+      const double piv = sx[j];
+      const bool zero = !(piv > tol);
+      const double ljj = zero ? 0.0 : sqrt(piv);
+      const double inv = zero ? 0.0 : 1.0 / ljj;
+      double lr[BS], lc[BS];
+#pragma unroll
+      for (int r = JB; r < BS; ++r) lr[r] = ty + 16 * r > j ? sx[ty + 16 * r] * inv : 0.0;
+#pragma unroll
+      for (int c = JB; c < BS; ++c) lc[c] = tx + 16 * c > j ? sx[tx + 16 * c] * inv : 0.0;
+#pragma unroll
+      for (int r = JB; r < BS; ++r)
+#pragma unroll
+        for (int c = JB; c < BS; ++c) a[r][c] = fma(-lr[r], lc[c], a[r][c]);
+      if (tx == jl) {  // column j of L in place (the update left that column as it was)
+#pragma unroll
+        for (int r = JB; r < BS; ++r) {
+          const int i = ty + 16 * r;
+          if (i >= j) a[r][JB] = i == j ? ljj : lr[r];
+        }
+      }
     }
-    __syncthreads();
-  }
+  }, std::make_integer_sequence<int, BS>{});
   double* Lo = g.lscr + (size_t)grp * D * D;
-  for (int e = tid; e < D * D; e += NT) {
-    const int i = e / D, j = e % D;
-    Lo[e] = j < i ? A[i * LD + j] : (j == i ? s_ld[i] : 0.0);
-  }
+#pragma unroll
+  for (int r = 0; r < BS; ++r)
+#pragma unroll
+    for (int c = 0; c < BS; ++c) {
+      const int i = ty + 16 * r, j = tx + 16 * c;
+      Lo[(size_t)i * D + j] = j <= i ? a[r][c] : 0.0;
+    }
 }
 
 // MFMA f64 16x16x4: A element (lane%16, lane/16), B element (lane/16,
 // lane%16); output (4*r + lane/16, lane%16) in register r (checked on the
 // device: unlike the fp32 16x16 forms, rows interleave across lane groups).
 // Per query head: S = L^T G_Q L (similar to C_h = G_Q G_K) on the fp64 matrix
-// cores, symmetrised into a packed lower triangle in LDS, then Householder
+// cores, its lower triangle packed into LDS, then Householder
 // tridiagonalisation of S with the matrix spread over the threads' registers.
 template <int D>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void spectrum_kernel(LGeo g) {
-  constexpr int RB = D / 64;  // 16-row bands per wave
-  constexpr int CB = D / 16;  // 16-col bands
-  constexpr int CH = CB / 2;  // column bands per pass
+  constexpr int NB = D / 16;       // 16-wide bands
+  constexpr int CPW = NB / NWAVE;  // column bands per wave
   __shared__ double s_m[D * (D + 1) / 2];
   __shared__ float s_d[D], s_e[D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int head = blockIdx.x;                 // l*Hq + h
+  const int ln = lane & 15, lk = lane >> 4;
+  const int head = blockIdx.x;  // l*Hq + h
   const int l = head / g.Hq, h = head - l * g.Hq;
   const int grp = l * g.Hkv + h / g.G;
   const float* GQ = g.gram + (size_t)head * D * D;
@@ -266,98 +316,72 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
   double* A = s_m;
   auto pk = [](int i, int j) { return i * (i + 1) / 2 + j; };  // (i, j <= i)
 
-  // 1. T = G_Q L (A operand G_Q fp32 -> fp64, B operand L, both from global),
-  //    in two halves of the columns to bound the accumulator registers.
-  double* T = g.tscr + (size_t)head * D * D;
-  f64x4 acc[RB][CH];
-  for (int c0 = 0; c0 < CB; c0 += CH) {
+  // 1. S = L^T (G_Q L), lower triangle, by column bands: wave w takes bands
+  //    w and NB-1-w (about equal shares of the triangular work).  For band
+  //    cb, T = G_Q L[:, cb] (L[k][16 cb ..] = 0 for k < 16 cb, so k starts
+  //    there) is only needed on row bands >= cb and stays in registers: in the
+  //    matrix cores' output layout, register r of T's tile kb holds row
+  //    16 kb + 4 r + lane/16 -- the B operand of k step 16 kb + 4 r of the next
+  //    product.  Then S[a][cb] = sum over k >= 16 a of L[k][16 a + n] T[k][..]
+  //    for the row bands a >= cb.
 #pragma unroll
-    for (int a = 0; a < RB; ++a)
+  for (int q = 0; q < CPW; ++q) {
+    const int cb = q == 0 ? wave : NB - 1 - wave;
+    f64x4 t[NB];
 #pragma unroll
-      for (int c = 0; c < CH; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
-    // unrolled so that several k steps' operand loads are in flight together
-#pragma unroll 8
-    for (int k = 0; k < D; k += 4) {
-      const int kk = k + (lane >> 4);
-      double av[RB];
+    for (int a = 0; a < NB; ++a) t[a] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k = 16 * cb; k < D; k += 4) {
+      const int kk = k + lk;
+      const double bv = Lg[(size_t)kk * D + cb * 16 + ln];
 #pragma unroll
-      // G_Q is symmetric: element (row, kk) is read at (kk, row), so the 16 lanes of a row band read consecutive words
-      for (int a = 0; a < RB; ++a) av[a] = (double)GQ[(size_t)kk * D + (wave * RB + a) * 16 + (lane & 15)];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const double bv = Lg[(size_t)kk * D + (c0 + c) * 16 + (lane & 15)];
-#pragma unroll
-        for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
+      for (int a = 0; a < NB; ++a) {
+        if (a < cb) continue;
+        // G_Q is symmetric: element (row, kk) is read at (kk, row), so the 16 lanes of a row band read consecutive words
+        const double av = (double)GQ[(size_t)kk * D + a * 16 + ln];
+        t[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, t[a], 0, 0, 0);
       }
     }
+    f64x4 s[NB];
 #pragma unroll
-    for (int a = 0; a < RB; ++a)
+    for (int a = 0; a < NB; ++a) s[a] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int c = 0; c < CH; ++c)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          T[(size_t)((wave * RB + a) * 16 + 4 * r + (lane >> 4)) * D + (c0 + c) * 16 + (lane & 15)] = acc[a][c][r];
+      for (int r = 0; r < 4; ++r) {
+        const int kk = 16 * kb + 4 * r + lk;
+#pragma unroll
+        for (int a = 0; a <= kb; ++a) {
+          if (a < cb) continue;
+          const double av = Lg[(size_t)kk * D + a * 16 + ln];
+          s[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, t[kb][r], s[a], 0, 0, 0);
+        }
+      }
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      if (a < cb) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * a + 4 * r + lk, j = 16 * cb + ln;
+        if (j <= i) A[pk(i, j)] = s[a][r];
+      }
+    }
   }
-  __threadfence();
   __syncthreads();
 
-  // 2. S = L^T T (A operand L^T, B operand T, from global) in two column
-  //    halves, symmetrised into the packed lower triangle straight from the
-  //    registers: each pass first writes its elements on or below the
-  //    diagonal (halved off it), then, after a barrier, adds half of each of
-  //    its elements above the diagonal to the mirror element -- which an
-  //    earlier write of this pass or of the first pass placed.
-  for (int c0 = 0; c0 < CB; c0 += CH) {
-#pragma unroll
-    for (int a = 0; a < RB; ++a)
-#pragma unroll
-      for (int c = 0; c < CH; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
-    // unrolled so that several k steps' operand loads are in flight together
-#pragma unroll 8
-    for (int k = 0; k < D; k += 4) {
-      const int kk = k + (lane >> 4);
-      double av[RB];
-#pragma unroll
-      for (int a = 0; a < RB; ++a) av[a] = Lg[(size_t)kk * D + (wave * RB + a) * 16 + (lane & 15)];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const double bv = T[(size_t)kk * D + (c0 + c) * 16 + (lane & 15)];
-#pragma unroll
-        for (int a = 0; a < RB; ++a) acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv, acc[a][c], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int a = 0; a < RB; ++a)
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = (wave * RB + a) * 16 + 4 * r + (lane >> 4), j = (c0 + c) * 16 + (lane & 15);
-          if (j <= i) A[pk(i, j)] = j == i ? acc[a][c][r] : 0.5 * acc[a][c][r];
-        }
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < RB; ++a)
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = (wave * RB + a) * 16 + 4 * r + (lane >> 4), j = (c0 + c) * 16 + (lane & 15);
-          if (j > i) A[pk(j, i)] += 0.5 * acc[a][c][r];
-        }
-    __syncthreads();
-  }
-
-  // 3. Householder tridiagonalisation (similarity, eigenvalues kept), the
-  //    symmetric matrix held in registers: thread (ty, tx) of a 16 x 16 grid
-  //    holds rows ty + 16 r and columns tx + 16 c (r, c < BS), so the lanes of
-  //    a row band read consecutive LDS words.  Step k
-  //    reflects rows/columns k+1.. with v = x - alpha e1 (x: column k below
-  //    the diagonal), p = beta A v, w = p - (beta/2)(v.p) v, A -= v w^T + w v^T;
-  //    v and w vanish on rows and columns <= k, which stay as they are.
-  //    Column k and p pass through LDS in two buffers taken in turn, so a step
-  //    needs two barriers; every wave forms the norms and dot products itself.
-  constexpr int BS = D / 16;
+  // 2. Householder tridiagonalisation (similarity, eigenvalues kept) with the
+  //    symmetric matrix in registers: thread (ty, tx) of a 16 x 16 grid holds
+  //    rows ty + 16 r and columns tx + 16 c (r, c < BS), so the lanes of a row
+  //    band read consecutive LDS words.  Step k reflects rows/columns k+1..
+  //    with v = x - alpha e1 (x: column k below the diagonal), p = beta A v,
+  //    w = p - (beta/2)(v.p) v, A -= v w^T + w v^T.  v and w vanish on rows
+  //    and columns <= k, which stay as they are: the blocks left of or above
+  //    column k's band are skipped.  Column k and p pass through LDS (two
+  //    buffers taken in turn: two barriers a step); norms and dot products
+  //    are summed over the 16 lanes of a row, whose columns cover every index
+  //    from the band on.  A v is formed from x while alpha's square root is
+  //    in flight (v differs from x in entry k+1 only) and corrected after.
+  constexpr int BS = NB;
   __shared__ double s_x[2][D], s_pp[2][D];
   const int ty = tid >> 4, tx = tid & 15;
   double a[BS][BS];
@@ -368,65 +392,83 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
       const int i = ty + 16 * r, j = tx + 16 * c;
       a[r][c] = j <= i ? A[pk(i, j)] : A[pk(j, i)];
     }
-  for (int k = 0; k < D - 2; ++k) {
-    const int r0 = k + 1;
-    double* sx = s_x[k & 1];
-    double* sp = s_pp[k & 1];
-    if (tx == k % 16) {  // column k: below the diagonal into LDS, the diagonal to d
-      // k / 16 is the same in every thread, so only one register column is read
+  each_band([&](auto band) {
+    constexpr int KB = decltype(band)::value;
+    constexpr int KB1 = KB + 1 < BS ? KB + 1 : KB;
+#pragma unroll 1
+    for (int kl = 0; kl < 16; ++kl) {
+      const int k = 16 * KB + kl;
+      if (k >= D - 2) break;
+      const int r0 = k + 1;
+      double* sx = s_x[k & 1];
+      double* sp = s_pp[k & 1];
+      if (tx == kl) {  // column k below the diagonal (zero on rows <= k), the diagonal to d
 #pragma unroll
-      for (int c = 0; c < BS; ++c) {
-        if (c != k / 16) continue;
-#pragma unroll
-        for (int r = 0; r < BS; ++r) {
+        for (int r = KB; r < BS; ++r) {
           const int i = ty + 16 * r;
-          sx[i] = i > k ? a[r][c] : 0.0;
-          if (i == k) s_d[k] = (float)a[r][c];
+          sx[i] = i > k ? a[r][KB] : 0.0;
         }
+        if (ty == kl) s_d[k] = (float)a[KB][KB];
+      }
+      __syncthreads();
+      double xc[BS], xr[BS], pr[BS];
+#pragma unroll
+      for (int c = KB; c < BS; ++c) xc[c] = sx[tx + 16 * c];
+#pragma unroll
+      for (int r = KB; r < BS; ++r) xr[r] = sx[ty + 16 * r];
+      const double x0 = sx[r0];
+      double nn = 0.0;
+#pragma unroll
+      for (int c = KB; c < BS; ++c) nn = fma(xc[c], xc[c], nn);
+      nn = row16_sum(nn);
+#pragma unroll
+      for (int r = KB; r < BS; ++r) {
+        pr[r] = 0.0;
+#pragma unroll
+        for (int c = KB; c < BS; ++c) pr[r] = fma(a[r][c], xc[c], pr[r]);
+      }
+      const double sq = sqrt(nn);
+      const double alpha = x0 >= 0.0 ? -sq : sq;
+      // beta = 2 / |v|^2 with |v|^2 = 2 (|x|^2 + |x0| |x|); 0 when x = 0 (then v = 0)
+      const double beta = nn > 0.0 ? 1.0 / fma(fabs(x0), sq, nn) : 0.0;
+      if (tid == 0) s_e[k] = (float)alpha;
+      if (tx == (r0 & 15)) {  // A v = A x - alpha (column k+1)
+#pragma unroll
+        for (int r = KB; r < BS; ++r) pr[r] = fma(-alpha, kl == 15 ? a[r][KB1] : a[r][KB], pr[r]);
+      }
+#pragma unroll
+      for (int r = KB; r < BS; ++r) pr[r] = row16_sum(pr[r]);
+      {  // lane tx writes p of row ty + 16 tx
+        double pv = 0.0;
+#pragma unroll
+        for (int r = KB; r < BS; ++r) pv = tx == r ? pr[r] : pv;
+        const int i = ty + 16 * tx;
+        if (tx >= KB && tx < BS) sp[i] = i > k ? beta * pv : 0.0;
+      }
+      __syncthreads();
+      double pc[BS], vc[BS];
+#pragma unroll
+      for (int c = KB; c < BS; ++c) {
+        pc[c] = sp[tx + 16 * c];
+        vc[c] = tx + 16 * c == r0 ? x0 - alpha : xc[c];
+      }
+      double vp = 0.0;
+#pragma unroll
+      for (int c = KB; c < BS; ++c) vp = fma(vc[c], pc[c], vp);
+      const double kk = 0.5 * beta * row16_sum(vp);
+      double wc[BS];
+#pragma unroll
+      for (int c = KB; c < BS; ++c) wc[c] = fma(-kk, vc[c], pc[c]);
+#pragma unroll
+      for (int r = KB; r < BS; ++r) {
+        const int i = ty + 16 * r;
+        const double vr = i == r0 ? x0 - alpha : xr[r];
+        const double wr = fma(-kk, vr, sp[i]);
+#pragma unroll
+        for (int c = KB; c < BS; ++c) a[r][c] = fma(-vr, wc[c], fma(-wr, vc[c], a[r][c]));
       }
     }
-    __syncthreads();
-    double xx = 0.0;
-    for (int i = lane; i < D; i += 64) xx += sx[i] * sx[i];
-    const double nrm2 = wave_sum_d(xx);
-    const double x0 = sx[r0];
-    const double alpha = x0 >= 0.0 ? -sqrt(nrm2) : sqrt(nrm2);
-    const double vn2 = nrm2 - x0 * x0 + (x0 - alpha) * (x0 - alpha);
-    if (tid == 0) s_e[k] = (float)(vn2 > 0.0 ? alpha : x0);
-    if (!(vn2 > 0.0)) continue;  // uniform: the column is already reduced
-    const double beta = 2.0 / vn2;
-    auto vof = [&](int i) { return i == r0 ? x0 - alpha : sx[i]; };  // 0 on rows <= k
-    double vc[BS];
-#pragma unroll
-    for (int c = 0; c < BS; ++c) vc[c] = vof(tx + 16 * c);
-    // p for this thread's rows: its block's share, summed over the row band's
-    // 16 lanes (one 16-lane row of the wave)
-#pragma unroll
-    for (int r = 0; r < BS; ++r) {
-      double pr = 0.0;
-#pragma unroll
-      for (int c = 0; c < BS; ++c) pr += a[r][c] * vc[c];
-      pr += dpp_d<0xB1>(pr);   // quad_perm [1,0,3,2]
-      pr += dpp_d<0x4E>(pr);   // quad_perm [2,3,0,1]
-      pr += dpp_d<0x141>(pr);  // row_half_mirror
-      pr += dpp_d<0x140>(pr);  // row_mirror
-      const int i = ty + 16 * r;
-      if (tx == r) sp[i] = i >= r0 ? beta * pr : 0.0;
-    }
-    __syncthreads();
-    double vpp = 0.0;
-    for (int i = lane; i < D; i += 64) vpp += vof(i) * sp[i];
-    const double kk = 0.5 * beta * wave_sum_d(vpp);
-    double wc[BS];
-#pragma unroll
-    for (int c = 0; c < BS; ++c) wc[c] = sp[tx + 16 * c] - kk * vc[c];
-#pragma unroll
-    for (int r = 0; r < BS; ++r) {
-      const double vr = vof(ty + 16 * r), wr = sp[ty + 16 * r] - kk * vr;
-#pragma unroll
-      for (int c = 0; c < BS; ++c) a[r][c] -= vr * wc[c] + wr * vc[c];
-    }
-  }
+  }, std::make_integer_sequence<int, BS>{});
   // the last 2 x 2 block
 #pragma unroll
   for (int r = 0; r < BS; ++r)
@@ -446,33 +488,54 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
 }
 
 // ------------------------------------------------------------------ bisect
-// Number of eigenvalues of the tridiagonal below x (Sturm sequence of the
-// LDL^T pivots; an exact zero pivot is nudged negative).
+// Number of eigenvalues of the tridiagonal below x: the negative LDL^T
+// pivots of T - x I (Sturm sequence), an exact zero pivot nudged negative.
+// d4 holds the diagonal, e4 the squared off-diagonal entry left of each row
+// (0 for the first), four entries a read (broadcast to every lane).
 template <int D>
-__device__ __forceinline__ int sturm_count(const float* d, const float* e2, float x) {
+__device__ __forceinline__ int sturm_count(const float4* d4, const float4* e4, float x) {
   int cnt = 0;
-  float q = d[0] - x;
-  cnt += q < 0.f;
-  for (int i = 1; i < D; ++i) {
+  float q = 1.f;
+  auto step = [&](float d, float e2) {
     if (fabsf(q) < 1e-30f) q = -1e-30f;
-    q = (d[i] - x) - e2[i - 1] * __builtin_amdgcn_rcpf(q);
+    q = (d - x) - e2 * __builtin_amdgcn_rcpf(q);
     cnt += q < 0.f;
+  };
+#pragma unroll 8
+  for (int i = 0; i < D / 4; ++i) {
+    const float4 dv = d4[i], ev = e4[i];
+    step(dv.x, ev.x);
+    step(dv.y, ev.y);
+    step(dv.z, ev.z);
+    step(dv.w, ev.w);
   }
   return cnt;
 }
 
+// One thread per eigenvalue j (ascending) in Gershgorin's interval, padded.
+// A first round is shared: thread t counts at the t-th of D equally spaced
+// interior points, and eigenvalue j starts between the last point whose count
+// is <= j and the first whose count is above it.  Then bisection until the
+// bracket's image under sqrt(max(., 0)) -- the singular value it brackets --
+// is 2^-19 of sqrt(the interval's magnitude) wide: what the ER needs, with
+// exact zero eigenvalues (rank-deficient projections) driven to 2^-38 of the
+// magnitude.  lambda is the bracket's midpoint; sigma = sqrt(max(lambda, 0))
+// and the head's ER follow.
 template <int D>
 __global__ __launch_bounds__(D) void bisect_kernel(LGeo g) {
-  __shared__ float s_d[D], s_e2[D];
-  __shared__ float s_lo[D / 64], s_hi[D / 64];
+  __shared__ float4 s_d4[D / 4], s_e4[D / 4];
+  __shared__ float s_lo[D / 64], s_hi[D / 64], s_x[D];
+  __shared__ int s_cnt[D];
   __shared__ double s_sum[D / 64];
+  float* s_d = reinterpret_cast<float*>(s_d4);
+  float* s_e2 = reinterpret_cast<float*>(s_e4);
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
   const int head = blockIdx.x;
   const float* tri = g.tri + (size_t)head * 2 * D;
   const float dj = tri[j], ej = tri[D + j];
-  s_d[j] = dj;
-  s_e2[j] = ej * ej;
   const float ejm = j > 0 ? tri[D + j - 1] : 0.f;
+  s_d[j] = dj;
+  s_e2[j] = ejm * ejm;
   float lo = dj - fabsf(ej) - fabsf(ejm), hi = dj + fabsf(ej) + fabsf(ejm);
   for (int o = 32; o >= 1; o >>= 1) {
     lo = fminf(lo, __shfl_xor(lo, o));
@@ -489,10 +552,24 @@ __global__ __launch_bounds__(D) void bisect_kernel(LGeo g) {
   }
   const float pad = 1e-6f * fmaxf(fabsf(lo), fabsf(hi)) + 1e-30f;
   float a = lo - pad, b = hi + pad;
+  const float tol_s = 0x1p-19f * sqrtf(fmaxf(fabsf(a), fabsf(b)));
+  const float xt = a + (b - a) * ((float)(j + 1) / (float)(D + 1));
+  s_x[j] = xt;
+  s_cnt[j] = sturm_count<D>(s_d4, s_e4, xt);
+  __syncthreads();
+  int t0 = 0, t1 = D;  // the first point whose count is above j
+  while (t0 < t1) {
+    const int m = (t0 + t1) >> 1;
+    if (s_cnt[m] > j) t1 = m;
+    else t0 = m + 1;
+  }
+  if (t0 < D) b = s_x[t0];
+  if (t0 > 0) a = s_x[t0 - 1];
   for (int it = 0; it < 64; ++it) {
+    if (!(sqrtf(fmaxf(b, 0.f)) - sqrtf(fmaxf(a, 0.f)) > tol_s)) break;
     const float mid = 0.5f * (a + b);
     if (!(mid > a && mid < b)) break;
-    if (sturm_count<D>(s_d, s_e2, mid) > j) b = mid;
+    if (sturm_count<D>(s_d4, s_e4, mid) > j) b = mid;
     else a = mid;
   }
   const double lam = fmax(0.5 * ((double)a + (double)b), 0.0);
@@ -569,7 +646,6 @@ hipError_t launch_label(const LabelArgs& a, hipStream_t s) {
   g.wk = a.w_k;
   g.gram = (float*)(ws + lo.gram);
   g.lscr = (double*)(ws + lo.lscr);
-  g.tscr = (double*)(ws + lo.tscr);
   g.tri = (float*)(ws + lo.tri);
   g.er_head = a.er_head ? a.er_head : (float*)(ws + lo.erh);
   g.er_group = a.er_group ? a.er_group : (float*)(ws + lo.erg);
