@@ -303,7 +303,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 template <int D>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void spectrum_kernel(LGeo g) {
   constexpr int NB = D / 16;       // 16-wide bands
-  constexpr int CPW = NB / NWAVE;  // column bands per wave
   __shared__ double s_m[D * (D + 1) / 2];
   __shared__ float s_d[D], s_e[D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -317,26 +316,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
   auto pk = [](int i, int j) { return i * (i + 1) / 2 + j; };  // (i, j <= i)
 
   // 1. S = L^T (G_Q L), lower triangle, by column bands: wave w takes bands
-  //    w and NB-1-w (about equal shares of the triangular work).  For band
-  //    cb, T = G_Q L[:, cb] (L[k][16 cb ..] = 0 for k < 16 cb, so k starts
-  //    there) is only needed on row bands >= cb and stays in registers: in the
+  //    w and NB-1-w (about equal shares of the triangular work), each with
+  //    its band index a compile-time constant, so that the operand loads of a
+  //    band form one straight run that the scheduler can issue ahead.  For
+  //    band CB, T = G_Q L[:, CB] (L[k][16 CB ..] = 0 for k < 16 CB, so k starts
+  //    there) is only needed on row bands >= CB and stays in registers: in the
   //    matrix cores' output layout, register r of T's tile kb holds row
   //    16 kb + 4 r + lane/16 -- the B operand of k step 16 kb + 4 r of the next
-  //    product.  Then S[a][cb] = sum over k >= 16 a of L[k][16 a + n] T[k][..]
-  //    for the row bands a >= cb.
-#pragma unroll
-  for (int q = 0; q < CPW; ++q) {
-    const int cb = q == 0 ? wave : NB - 1 - wave;
+  //    product.  Then S[a][CB] = sum over k >= 16 a of L[k][16 a + n] T[k][..]
+  //    for the row bands a >= CB.
+  each_band([&](auto band) {
+    constexpr int CB = decltype(band)::value;
+    if (CB != wave && CB != NB - 1 - wave) return;
     f64x4 t[NB];
 #pragma unroll
-    for (int a = 0; a < NB; ++a) t[a] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int a = CB; a < NB; ++a) t[a] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
-    for (int k = 16 * cb; k < D; k += 4) {
+    for (int k = 16 * CB; k < D; k += 4) {
       const int kk = k + lk;
-      const double bv = Lg[(size_t)kk * D + cb * 16 + ln];
+      const double bv = Lg[(size_t)kk * D + CB * 16 + ln];
 #pragma unroll
-      for (int a = 0; a < NB; ++a) {
-        if (a < cb) continue;
+      for (int a = CB; a < NB; ++a) {
         // G_Q is symmetric: element (row, kk) is read at (kk, row), so the 16 lanes of a row band read consecutive words
         const double av = (double)GQ[(size_t)kk * D + a * 16 + ln];
         t[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, t[a], 0, 0, 0);
@@ -344,29 +344,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
     }
     f64x4 s[NB];
 #pragma unroll
-    for (int a = 0; a < NB; ++a) s[a] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int a = CB; a < NB; ++a) s[a] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+    for (int kb = CB; kb < NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kk = 16 * kb + 4 * r + lk;
 #pragma unroll
-        for (int a = 0; a <= kb; ++a) {
-          if (a < cb) continue;
+        for (int a = CB; a <= kb; ++a) {
           const double av = Lg[(size_t)kk * D + a * 16 + ln];
           s[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, t[kb][r], s[a], 0, 0, 0);
         }
       }
 #pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      if (a < cb) continue;
+    for (int a = CB; a < NB; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * a + 4 * r + lk, j = 16 * cb + ln;
+        const int i = 16 * a + 4 * r + lk, j = 16 * CB + ln;
         if (j <= i) A[pk(i, j)] = s[a][r];
       }
-    }
-  }
+  }, std::make_integer_sequence<int, NB>{});
   __syncthreads();
 
   // 2. Householder tridiagonalisation (similarity, eigenvalues kept) with the
@@ -403,11 +400,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
       double* sx = s_x[k & 1];
       double* sp = s_pp[k & 1];
       if (tx == kl) {  // column k below the diagonal (zero on rows <= k), the diagonal to d
+        sx[ty + 16 * KB] = ty > kl ? a[KB][KB] : 0.0;
 #pragma unroll
-        for (int r = KB; r < BS; ++r) {
-          const int i = ty + 16 * r;
-          sx[i] = i > k ? a[r][KB] : 0.0;
-        }
+        for (int r = KB + 1; r < BS; ++r) sx[ty + 16 * r] = a[r][KB];
         if (ty == kl) s_d[k] = (float)a[KB][KB];
       }
       __syncthreads();
@@ -432,26 +427,35 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
       // beta = 2 / |v|^2 with |v|^2 = 2 (|x|^2 + |x0| |x|); 0 when x = 0 (then v = 0)
       const double beta = nn > 0.0 ? 1.0 / fma(fabs(x0), sq, nn) : 0.0;
       if (tid == 0) s_e[k] = (float)alpha;
-      if (tx == (r0 & 15)) {  // A v = A x - alpha (column k+1)
+      // v = x - alpha e_{k+1}: A v = A x - alpha (column k+1), corrected in
+      // the lanes holding column k+1; entry k+1 of v in the lanes holding it
+      if (tx == (r0 & 15)) {
+        if (kl == 15) {
 #pragma unroll
-        for (int r = KB; r < BS; ++r) pr[r] = fma(-alpha, kl == 15 ? a[r][KB1] : a[r][KB], pr[r]);
+          for (int r = KB; r < BS; ++r) pr[r] = fma(-alpha, a[r][KB1], pr[r]);
+          xc[KB1] -= alpha;
+        } else {
+#pragma unroll
+          for (int r = KB; r < BS; ++r) pr[r] = fma(-alpha, a[r][KB], pr[r]);
+          xc[KB] -= alpha;
+        }
+      }
+      if (ty == (r0 & 15)) {
+        if (kl == 15) xr[KB1] -= alpha;
+        else xr[KB] -= alpha;
       }
 #pragma unroll
       for (int r = KB; r < BS; ++r) pr[r] = row16_sum(pr[r]);
-      {  // lane tx writes p of row ty + 16 tx
-        double pv = 0.0;
+      if (tx == 0) {  // p of this thread's rows (zero on rows <= k)
+        sp[ty + 16 * KB] = ty > kl ? beta * pr[KB] : 0.0;
 #pragma unroll
-        for (int r = KB; r < BS; ++r) pv = tx == r ? pr[r] : pv;
-        const int i = ty + 16 * tx;
-        if (tx >= KB && tx < BS) sp[i] = i > k ? beta * pv : 0.0;
+        for (int r = KB + 1; r < BS; ++r) sp[ty + 16 * r] = beta * pr[r];
       }
       __syncthreads();
-      double pc[BS], vc[BS];
+      double pc[BS];
+      const double* vc = xc;
 #pragma unroll
-      for (int c = KB; c < BS; ++c) {
-        pc[c] = sp[tx + 16 * c];
-        vc[c] = tx + 16 * c == r0 ? x0 - alpha : xc[c];
-      }
+      for (int c = KB; c < BS; ++c) pc[c] = sp[tx + 16 * c];
       double vp = 0.0;
 #pragma unroll
       for (int c = KB; c < BS; ++c) vp = fma(vc[c], pc[c], vp);
@@ -461,9 +465,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void sp
       for (int c = KB; c < BS; ++c) wc[c] = fma(-kk, vc[c], pc[c]);
 #pragma unroll
       for (int r = KB; r < BS; ++r) {
-        const int i = ty + 16 * r;
-        const double vr = i == r0 ? x0 - alpha : xr[r];
-        const double wr = fma(-kk, vr, sp[i]);
+        const double vr = xr[r];
+        const double wr = fma(-kk, vr, sp[ty + 16 * r]);
 #pragma unroll
         for (int c = KB; c < BS; ++c) a[r][c] = fma(-vr, wc[c], fma(-wr, vc[c], a[r][c]));
       }
