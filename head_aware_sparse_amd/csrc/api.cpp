@@ -176,7 +176,8 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
                   expect <= 0.7 * has::kFusedSelCand) ? 1 : 0;
   }
   // prefiltered scoring units: about 2048 over the worst-case item count,
-  // between 1024 and 16384 tokens
+  // between 1024 and 16384 tokens (a shared-index step without labels sizes
+  // them to whole rounds of the resident scoring workgroups at launch)
   g.ct_tip = clampi(pow2_floor((long long)g.T * n_idx / 2048), 1024, 16384);
   g.nch_tip = (g.T + g.ct_tip - 1) / g.ct_tip;
   g.bm_words = (g.T + 31) / 32;

@@ -2345,6 +2345,29 @@ hipError_t launch_tip_v(const Geo& g, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Scoring workgroups of the in-unit tau mode resident per CU (the occupancy
+// query, once per element type and row width).
+template <typename E, int V>
+int tip_resident_per_cu() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, tip_kernel<E, V, 3>, NT, 0) != hipSuccess) b = 0;
+    return b;
+  }();
+  return n;
+}
+template <typename E>
+int tip_resident_per_cu(const Geo& g) {
+  switch (g.R * (int)sizeof(E) / 16) {
+    case 1: return tip_resident_per_cu<E, 1>();
+    case 2: return tip_resident_per_cu<E, 2>();
+    case 4: return tip_resident_per_cu<E, 4>();
+    case 8: return tip_resident_per_cu<E, 8>();
+    case 16: return tip_resident_per_cu<E, 16>();
+    default: return 0;
+  }
+}
+
 // Prefiltered scoring with a tau launch when every query head selects its
 // own tokens: the hg heads of a KV group share each unit (bf16 caches).
 template <int V>
@@ -2499,6 +2522,9 @@ constexpr long long kSideStreamRows = 1LL << 20;
 // which each unit derives tau itself instead of a separate launch.
 constexpr long long kTauInlineUnits = 512;
 constexpr long long kTauInlineUnitsMax = 4096;
+// Tokens per prefiltered scoring unit: the bounds of the sizes chosen.
+constexpr long long kTipUnitMinTokens = 1024;
+constexpr long long kTipUnitMaxTokens = 16384;
 // Output elements per call from which the merge moves 4 per thread in
 // 16-byte vectors; below, one per thread keeps more threads in flight.
 constexpr long long kMergeVecOutputs = 1LL << 18;
@@ -2550,6 +2576,22 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
   // per-query-head selection: a KV group's hg heads share the sampling and
   // scoring units (bf16 caches, steps with a tau launch)
   const int hg = 1 << g.kv_shift;
+  // A shared-index step without labels scores every index item, so its
+  // scoring units can fill whole rounds of the resident scoring workgroups:
+  // the fewest rounds that keep a unit within 16384 tokens (one round for 32
+  // items of 131072 tokens), which also derives tau in the fewest units.
+  if (g.prefilter && g.clsa && g.labels == nullptr) {
+    const int per_cu = g.bf16 ? tip_resident_per_cu<uint16_t>(g) : tip_resident_per_cu<float>(g);
+    const long long slots = (long long)(g.grid / 8) * per_cu;  // g.grid: 8 workgroups per CU
+    if (slots > 0) {
+      const long long cap = kTipUnitMaxTokens;
+      const long long rounds = std::max(1LL, (n_idx_items * g.T + slots * cap - 1) / (slots * cap));
+      const long long per_item = std::max(1LL, (rounds * slots + n_idx_items - 1) / n_idx_items);
+      const long long ct = ((g.T + per_item - 1) / per_item + 63) / 64 * 64;
+      g.ct_tip = (int)std::min(std::max(ct, (long long)kTipUnitMinTokens), cap);
+      g.nch_tip = (g.T + g.ct_tip - 1) / g.ct_tip;
+    }
+  }
   // tau inside the scoring units: always up to kTauInlineUnits units; up to
   // kTauInlineUnitsMax (with the ring issued first) when no heads share units
   const long long units_tip = n_idx_items * g.nch_tip;
