@@ -14,8 +14,9 @@
 //   spectrum  per query head: the symmetric S = L^T G_Q L (fp64 matrix
 //             cores), which is similar to C_h = G_Q G_K; Householder
 //             tridiagonalisation of S in fp64, the matrix in registers.
-//   bisect    eigenvalues of the tridiagonal by Sturm-count bisection (one
-//             thread per eigenvalue), sigma = sqrt(max(lambda, 0)) and ER.
+//   bisect    eigenvalues of the tridiagonal by Sturm counts (a shared
+//             first round, then trisection by a pair of threads per
+//             eigenvalue), sigma = sqrt(max(lambda, 0)) and ER.
 //   finalize  group mean of ER, global rank with ties to the lower index,
 //             labels.
 #include <type_traits>
@@ -515,31 +516,40 @@ __device__ __forceinline__ int sturm_count(const float4* d4, const float4* e4, f
   return cnt;
 }
 
-// One thread per eigenvalue j (ascending) in Gershgorin's interval, padded.
-// A first round is shared: thread t counts at the t-th of D equally spaced
-// interior points, and eigenvalue j starts between the last point whose count
-// is <= j and the first whose count is above it.  Then bisection until the
+// Two threads per eigenvalue j (ascending), in Gershgorin's interval,
+// padded.  A first round is shared: thread t counts at the t-th of 2D equally
+// spaced interior points, and eigenvalue j starts between the last point whose
+// count is <= j and the first whose count is above it.  Then trisection: each
+// thread of the pair counts at one of the bracket's two interior thirds, the
+// pair swaps counts and both keep the third that holds eigenvalue j (the
+// same floating-point steps in both, so their brackets stay equal), until the
 // bracket's image under sqrt(max(., 0)) -- the singular value it brackets --
 // is 2^-19 of sqrt(the interval's magnitude) wide: what the ER needs, with
 // exact zero eigenvalues (rank-deficient projections) driven to 2^-38 of the
 // magnitude.  lambda is the bracket's midpoint; sigma = sqrt(max(lambda, 0))
 // and the head's ER follow.
 template <int D>
-__global__ __launch_bounds__(D) void bisect_kernel(LGeo g) {
+__global__ __launch_bounds__(2 * D) void bisect_kernel(LGeo g) {
+  constexpr int NTB = 2 * D, NWB = NTB / 64;
   __shared__ float4 s_d4[D / 4], s_e4[D / 4];
-  __shared__ float s_lo[D / 64], s_hi[D / 64], s_x[D];
-  __shared__ int s_cnt[D];
-  __shared__ double s_sum[D / 64];
+  __shared__ float s_lo[NWB], s_hi[NWB], s_x[NTB];
+  __shared__ int s_cnt[NTB];
+  __shared__ double s_sum[NWB];
   float* s_d = reinterpret_cast<float*>(s_d4);
   float* s_e2 = reinterpret_cast<float*>(s_e4);
-  const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = tid >> 1, part = tid & 1;
   const int head = blockIdx.x;
   const float* tri = g.tri + (size_t)head * 2 * D;
-  const float dj = tri[j], ej = tri[D + j];
-  const float ejm = j > 0 ? tri[D + j - 1] : 0.f;
-  s_d[j] = dj;
-  s_e2[j] = ejm * ejm;
-  float lo = dj - fabsf(ej) - fabsf(ejm), hi = dj + fabsf(ej) + fabsf(ejm);
+  float lo = INFINITY, hi = -INFINITY;
+  if (tid < D) {
+    const float dj = tri[tid], ej = tri[D + tid];
+    const float ejm = tid > 0 ? tri[D + tid - 1] : 0.f;
+    s_d[tid] = dj;
+    s_e2[tid] = ejm * ejm;
+    lo = dj - fabsf(ej) - fabsf(ejm);
+    hi = dj + fabsf(ej) + fabsf(ejm);
+  }
   for (int o = 32; o >= 1; o >>= 1) {
     lo = fminf(lo, __shfl_xor(lo, o));
     hi = fmaxf(hi, __shfl_xor(hi, o));
@@ -549,48 +559,57 @@ __global__ __launch_bounds__(D) void bisect_kernel(LGeo g) {
     s_hi[wave] = hi;
   }
   __syncthreads();
-  for (int w = 0; w < D / 64; ++w) {
+  for (int w = 0; w < NWB; ++w) {
     lo = fminf(lo, s_lo[w]);
     hi = fmaxf(hi, s_hi[w]);
   }
   const float pad = 1e-6f * fmaxf(fabsf(lo), fabsf(hi)) + 1e-30f;
   float a = lo - pad, b = hi + pad;
   const float tol_s = 0x1p-19f * sqrtf(fmaxf(fabsf(a), fabsf(b)));
-  const float xt = a + (b - a) * ((float)(j + 1) / (float)(D + 1));
-  s_x[j] = xt;
-  s_cnt[j] = sturm_count<D>(s_d4, s_e4, xt);
+  const float xt = a + (b - a) * ((float)(tid + 1) / (float)(NTB + 1));
+  s_x[tid] = xt;
+  s_cnt[tid] = sturm_count<D>(s_d4, s_e4, xt);
   __syncthreads();
-  int t0 = 0, t1 = D;  // the first point whose count is above j
+  int t0 = 0, t1 = NTB;  // the first point whose count is above j
   while (t0 < t1) {
     const int m = (t0 + t1) >> 1;
     if (s_cnt[m] > j) t1 = m;
     else t0 = m + 1;
   }
-  if (t0 < D) b = s_x[t0];
+  if (t0 < NTB) b = s_x[t0];
   if (t0 > 0) a = s_x[t0 - 1];
   for (int it = 0; it < 64; ++it) {
     if (!(sqrtf(fmaxf(b, 0.f)) - sqrtf(fmaxf(a, 0.f)) > tol_s)) break;
-    const float mid = 0.5f * (a + b);
-    if (!(mid > a && mid < b)) break;
-    if (sturm_count<D>(s_d4, s_e4, mid) > j) b = mid;
-    else a = mid;
+    const float w3 = (b - a) * (1.f / 3.f);
+    const float x1 = a + w3, x2 = b - w3;
+    if (!(x1 > a && x2 > x1 && b > x2)) break;
+    const int mine = sturm_count<D>(s_d4, s_e4, part ? x2 : x1);
+    const int other = __shfl_xor(mine, 1);
+    const int c1 = part ? other : mine, c2 = part ? mine : other;
+    if (c1 > j) b = x1;
+    else if (c2 > j) {
+      a = x1;
+      b = x2;
+    } else {
+      a = x2;
+    }
   }
   const double lam = fmax(0.5 * ((double)a + (double)b), 0.0);
-  const double sigma = sqrt(lam);
+  const double sigma = part ? 0.0 : sqrt(lam);  // one thread of the pair counts
   double tot = wave_sum_d(sigma);
   if (lane == 0) s_sum[wave] = tot;
   __syncthreads();
   tot = 0.0;
-  for (int w = 0; w < D / 64; ++w) tot += s_sum[w];
+  for (int w = 0; w < NWB; ++w) tot += s_sum[w];
   __syncthreads();
   const double p = tot > 0.0 ? sigma / tot : 0.0;
   double hterm = p > 0.0 ? -p * log(p) : 0.0;
   hterm = wave_sum_d(hterm);
   if (lane == 0) s_sum[wave] = hterm;
   __syncthreads();
-  if (j == 0) {
+  if (tid == 0) {
     double H = 0.0;
-    for (int w = 0; w < D / 64; ++w) H += s_sum[w];
+    for (int w = 0; w < NWB; ++w) H += s_sum[w];
     g.er_head[head] = (float)exp(H);
   }
 }
@@ -677,8 +696,8 @@ hipError_t launch_label(const LabelArgs& a, hipStream_t s) {
   }
   {
     KTimer t("bisect", s);
-    if (a.d == 128) bisect_kernel<128><<<n_heads, 128, 0, s>>>(g);
-    else bisect_kernel<64><<<n_heads, 64, 0, s>>>(g);
+    if (a.d == 128) bisect_kernel<128><<<n_heads, 256, 0, s>>>(g);
+    else bisect_kernel<64><<<n_heads, 128, 0, s>>>(g);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
