@@ -524,10 +524,13 @@ __device__ __forceinline__ int sturm_count(const float4* d4, const float4* e4, f
 // pair swaps counts and both keep the third that holds eigenvalue j (the
 // same floating-point steps in both, so their brackets stay equal), until the
 // bracket's image under sqrt(max(., 0)) -- the singular value it brackets --
-// is 2^-19 of sqrt(the interval's magnitude) wide: what the ER needs, with
-// exact zero eigenvalues (rank-deficient projections) driven to 2^-38 of the
-// magnitude.  lambda is the bracket's midpoint; sigma = sqrt(max(lambda, 0))
-// and the head's ER follow.
+// is 2^-19 of sqrt(the interval's magnitude) wide, what the ER needs.  A
+// bracket that still reaches 0 or below (an exact zero eigenvalue: a
+// rank-deficient projection) goes on until its upper end is 2^-48 of the
+// magnitude, so that each zero's singular value stays below 2^-24 of its
+// square root: even 127 zeros beside one nonzero singular value move the ER
+// by about 1e-4.  lambda is the bracket's midpoint; sigma = sqrt(max(lambda,
+// 0)) and the head's ER follow.
 template <int D>
 __global__ __launch_bounds__(2 * D) void bisect_kernel(LGeo g) {
   constexpr int NTB = 2 * D, NWB = NTB / 64;
@@ -566,6 +569,7 @@ __global__ __launch_bounds__(2 * D) void bisect_kernel(LGeo g) {
   const float pad = 1e-6f * fmaxf(fabsf(lo), fabsf(hi)) + 1e-30f;
   float a = lo - pad, b = hi + pad;
   const float tol_s = 0x1p-19f * sqrtf(fmaxf(fabsf(a), fabsf(b)));
+  const float tol_z = 0x1p-48f * fmaxf(fabsf(a), fabsf(b));
   const float xt = a + (b - a) * ((float)(tid + 1) / (float)(NTB + 1));
   s_x[tid] = xt;
   s_cnt[tid] = sturm_count<D>(s_d4, s_e4, xt);
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(2 * D) void bisect_kernel(LGeo g) {
   if (t0 < NTB) b = s_x[t0];
   if (t0 > 0) a = s_x[t0 - 1];
   for (int it = 0; it < 64; ++it) {
-    if (!(sqrtf(fmaxf(b, 0.f)) - sqrtf(fmaxf(a, 0.f)) > tol_s)) break;
+    if (a > 0.f ? !(sqrtf(b) - sqrtf(a) > tol_s) : !(b > tol_z)) break;
     const float w3 = (b - a) * (1.f / 3.f);
     const float x1 = a + w3, x2 = b - w3;
     if (!(x1 > a && x2 > x1 && b > x2)) break;

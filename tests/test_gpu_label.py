@@ -90,6 +90,48 @@ def test_rank_deficient_key_projection():
     _check(got, ref, 2)
 
 
+def _flat_weights(d, dm, ranks, key_zero, scale):
+    """W_Q rows i < r of head h are scale[h] times distinct unit vectors of
+    d_model (so W_Q W_Q^T = scale^2 diag(1 x r, 0)); W_K of a group is the
+    first d unit vectors times 3 (W_K W_K^T = 9 I), or zero."""
+    G = len(ranks) // len(key_zero)
+    wq = np.zeros((1, len(ranks) * d, dm), dtype=np.float32)
+    wk = np.zeros((1, len(key_zero) * d, dm), dtype=np.float32)
+    for h, r in enumerate(ranks):
+        for i in range(r):
+            wq[0, h * d + i, (7 * i + h) % dm] = scale[h]
+    for gk, z in enumerate(key_zero):
+        if not z:
+            for i in range(d):
+                wk[0, gk * d + i, (5 * i + 3 * gk) % dm] = 3.0
+    assert G * len(key_zero) == len(ranks)
+    return wq, wk
+
+
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+def test_flat_and_empty_spectra(bf16):
+    """Closed forms (AoH Metodología §2): r equal singular values give ER = r
+    exactly -- the tridiagonal then carries r repeated eigenvalues and d - r
+    exact zeros, every one bisected; a head whose query projection is zero,
+    and every head of a group whose key projection is zero, have no
+    spectrum: ER = exp(0) = 1.  The rank-1 head puts 127 zeros beside one
+    singular value, where the zeros' residual singular values weigh most."""
+    d, dm = 128, 512
+    ranks = [1, 7, 64, 128, 5, 5, 5, 5, 0, 3, 16, 2]
+    scale = [1.0, 1.0, 1.0, 1.0, 1.0, 2.0, 0.5, 1.0, 1.0, 2.0, 1.0, 4.0]
+    key_zero = [False, True, False]
+    cfg = R.get_config("c1", n_q_heads=12, n_kv_heads=3, d_model=dm, d_head=d, kv_dtype="bf16" if bf16 else "f32")
+    wq, wk = _flat_weights(d, dm, ranks, key_zero, scale)
+    w = (R._to_storage(wq, bf16), R._to_storage(wk, bf16))
+    print(f"case label flat spectra bf16={bf16}", flush=True)
+    got, ref = _run(cfg, k=1, w=w)
+    _check(got, ref, 1)
+    want = np.array([max(r, 1) if not key_zero[h // 4] else 1 for h, r in enumerate(ranks)], dtype=np.float64)
+    np.testing.assert_allclose(ref[0][0], want, rtol=1e-9)
+    np.testing.assert_allclose(got[0][0], want, rtol=ER_RTOL)
+    assert got[2][0].tolist() == [0, 1, 0]
+
+
 @pytest.mark.parametrize("over", [
     dict(kv_dtype="f32"),                           # fp32 weights, d 128
     dict(d_head=64, n_dom=8),                       # bf16 weights, d 64
