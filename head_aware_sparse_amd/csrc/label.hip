@@ -10,9 +10,11 @@
 //   gram      G = W W^T for every query and key head (matrix cores, bf16 or
 //             fp32 in, fp32 accumulate).  Reads every weight once: the
 //             HBM-bound step.
-//   cholesky  per key head, in fp64 LDS: G_K = L L^T.
+//   cholesky  per key head, in fp64 with the matrix in registers:
+//             G_K = L L^T.
 //   spectrum  per query head: the symmetric S = L^T G_Q L (fp64 matrix
-//             cores), which is similar to C_h = G_Q G_K; Householder
+//             cores, L's zero blocks skipped, the lower triangle only),
+//             which is similar to C_h = G_Q G_K; Householder
 //             tridiagonalisation of S in fp64, the matrix in registers.
 //   bisect    eigenvalues of the tridiagonal by Sturm counts (a shared
 //             first round, then trisection by a pair of threads per
