@@ -1759,9 +1759,9 @@ __global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
 //   S[qv][row] = Q[qv][:] . K[row][:]       (bf16 MFMA 32x32x16, fp32 sums)
 //   P = softmax over the unit's rows per qv (fp32, in LDS)
 //   O[qv][d]   = sum_row P[qv][row] V[row][d]
-// P V also runs on bf16 MFMA: P = P_hi + P_lo with both halves rounded to
-// bf16, so the product keeps about 16 bits of P (V is bf16 already) and
-// accumulates in fp32.  One unit = (group, sequence, chunk of kClsaRows =
+// P V also runs on bf16 MFMA: P = P_hi + P_lo, P_hi the upper 16 bits of P
+// and P_lo those of the exact remainder P - P_hi, so the product keeps P to a
+// relative error below 2^-14 (V is bf16 already) and accumulates in fp32.  One unit = (group, sequence, chunk of kClsaRows =
 // 128 selected rows); its K and V rows are gathered into LDS once, and P
 // reuses the K tile's LDS once S is computed.  Wave w owns row block w for S
 // and channel block w for O.  MFMA 32x32: A element (lane%32, k-slice
@@ -1776,12 +1776,6 @@ constexpr int kPPad = kClsaRows + 4;   // floats per P row (16-byte aligned rows
 constexpr int kClsaTileBytes = kClsaRows * kClsaPad * 2;  // one K or V tile in LDS
 constexpr int kClsaQBytes = 32 * kClsaPad * 2;            // the query tile
 constexpr int kClsaLdsBytes = 2 * kClsaTileBytes + kClsaQBytes;
-
-// bf16 bits of x rounded to nearest even (x finite)
-__device__ __forceinline__ unsigned short bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
 
 // The attention of one unit over its nrows gathered rows, whose cache
 // positions rows(r) gives (r < nrows; values in [0, T)), into the chunk
@@ -1917,7 +1911,8 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
     }
   }
   __syncthreads();
-  // O = P V for channel block `wave`, P split into bf16 hi + lo
+  // O = P V for channel block `wave`, P split into bf16 hi + lo: a pair of
+  // values packs the upper halves of two words in one byte permute
   f32x16_t o;
 #pragma unroll
   for (int r = 0; r < 16; ++r) o[r] = 0.f;
@@ -1928,17 +1923,22 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
       const float4 p0 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks]);
       const float4 p1 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks + 4]);
       const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      u16x8_t hi, lo, vv;
+      constexpr uint32_t kUpperHalves = 0x07060302u;  // bytes 2-3 of the second operand, then of the first
+      uint32_t hw[4], lw[4];
+      u16x8_t vv;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const unsigned short h = bf16_rne(pv[i]);
-        hi[i] = h;
-        lo[i] = bf16_rne(pv[i] - __uint_as_float((uint32_t)h << 16));
-        vv[i] = s_v[k0 + ks + i][dcol];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = __float_as_uint(pv[2 * i]), c = __float_as_uint(pv[2 * i + 1]);
+        hw[i] = __builtin_amdgcn_perm(c, a, kUpperHalves);
+        const float la = pv[2 * i] - __uint_as_float(a & 0xFFFF0000u);
+        const float lc = pv[2 * i + 1] - __uint_as_float(c & 0xFFFF0000u);
+        lw[i] = __builtin_amdgcn_perm(__float_as_uint(lc), __float_as_uint(la), kUpperHalves);
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vv[i] = s_v[k0 + ks + i][dcol];
       const bf16x8_t vb8 = __builtin_bit_cast(bf16x8_t, vv);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, hi), vb8, o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lo), vb8, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, hw), vb8, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lw), vb8, o, 0, 0, 0);
     }
   }
   // partials: acc for (layer, head) = qv, channel block `wave`
@@ -2153,12 +2153,13 @@ __global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
       // candidates -> LDS when they fit, counted by their first digit
       const uint4* c4 = reinterpret_cast<const uint4*>(gc);
       const int n4 = (int)(count + 1) / 2;
-      for (int i0 = tid; i0 < n4; i0 += 4 * BT) {
-        uint4 r[4];
+      constexpr int kLd = 8;  // 16-byte loads in flight per thread: up to 4096 candidates in one round
+      for (int i0 = tid; i0 < n4; i0 += kLd * BT) {
+        uint4 r[kLd];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = i0 + q * BT < n4 ? c4[i0 + q * BT] : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < kLd; ++q) r[q] = i0 + q * BT < n4 ? c4[i0 + q * BT] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kLd; ++q) {
           const int i = i0 + q * BT;
           if (i < n4) {
             if (in_lds) s_c[2 * i] = make_uint2(r[q].x, r[q].y);
