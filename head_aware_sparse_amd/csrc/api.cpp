@@ -142,15 +142,12 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
   // the matrix cores pay off once several layers' queries share each
   // gathered row; a single layer's G heads go faster on the vector ALUs
   g.clsa_mfma = clsa && g.bf16 && g.d == 128 && g.Lq >= 2 && g.Lq * g.G <= 32;
-  g.cf = g.clsa_mfma ? has::kClsaRows : clampi(pow2_floor((long long)g.n_fac * n_att / 2048), 128, has::kMaxChunkRows);
-  g.nch_f = (g.n_fac + g.cf - 1) / g.cf;
   g.s_end = g.n_sink < g.T ? g.n_sink : g.T;
   g.w_start = (g.T - g.window) > g.s_end ? (g.T - g.window) : g.s_end;
   g.n_srows = g.s_end + (g.T - g.w_start);
   g.cs = clampi(pow2_floor((long long)g.n_srows * n_att / 2048), 128, has::kMaxChunkRows);
   g.nch_s = (g.n_srows + g.cs - 1) / g.cs;
   g.cs = (g.n_srows + g.nch_s - 1) / g.nch_s;  // equal chunks (no short tail)
-  g.nparts = g.nch_f > g.nch_s ? g.nch_f : g.nch_s;
   // Prefiltered selection: a sample of kSampleTokens scores places a key
   // threshold expected to pass about 1.25 n_fac tokens plus 4 standard
   // deviations of the sampled count; used when that fits the kCandFast
@@ -175,6 +172,13 @@ Layout make_layout(const has_decode_dims* d, bool clsa) {
     g.fuse_sel = (g.clsa_mfma && g.prefilter && g.T <= has::kShortMaxT && g.n_fac < 65536 &&
                   expect <= 0.7 * has::kFusedSelCand) ? 1 : 0;
   }
+  // retrieval chunks: the shared-index units' LDS tiles (kFusedRows when they
+  // also select), else about 2048 units over the worst-case item count
+  g.cf = g.fuse_sel ? has::kFusedRows
+       : g.clsa_mfma ? has::kClsaRows
+                     : clampi(pow2_floor((long long)g.n_fac * n_att / 2048), 128, has::kMaxChunkRows);
+  g.nch_f = (g.n_fac + g.cf - 1) / g.cf;
+  g.nparts = g.nch_f > g.nch_s ? g.nch_f : g.nch_s;
   // prefiltered scoring units: about 2048 over the worst-case item count,
   // between 1024 and 16384 tokens (a shared-index step without labels sizes
   // them to whole rounds of the resident scoring workgroups at launch)

@@ -862,6 +862,13 @@ __device__ void key_range(const Src& src, uint32_t* s_res, uint32_t& lo, uint32_
 
 constexpr int kRankMax = 256;  // bin size resolved by direct ranking
 
+// 1 when the (key, token) pair a comes before b in the order (key desc, token
+// asc), else 0.  Bitwise, so both halves load as one LDS read and the
+// comparisons of a ranking loop stay free of branches and their waits.
+__device__ __forceinline__ uint32_t before(uint2 a, uint2 b) {
+  return (uint32_t)(a.x > b.x) | ((uint32_t)(a.x == b.x) & (uint32_t)(a.y < b.y));
+}
+
 // The element of rank need-1 (0-based) in the order (key desc, token asc)
 // among the elements whose key satisfies ((key - lo) >> sh) == pre; there
 // are at most kRankMax of them.  Each counts the members ordered before it.
@@ -883,7 +890,7 @@ __device__ void rank_in_bin(const Src& src, uint32_t lo, int sh, uint32_t pre, u
 #pragma unroll 8
     for (int j = 0; j < m; ++j) {
       const uint2 o = s_list[j];
-      r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+      r += before(o, me);
     }
     if (r == need - 1) {
       s_res[0] = me.x;
@@ -1259,7 +1266,7 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(Geo g) {
 #pragma unroll 8
           for (int j = 0; j < m; ++j) {
             const uint2 o = s_list[j];
-            r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+            r += before(o, me);
           }
           if (direct && r < need) mark(me.y);
           if (r == need - 1) {
@@ -1761,35 +1768,40 @@ __global__ __launch_bounds__(NT) void merge_kernel(Geo g) {
 //   O[qv][d]   = sum_row P[qv][row] V[row][d]
 // P V also runs on bf16 MFMA: P = P_hi + P_lo, P_hi the upper 16 bits of P
 // and P_lo those of the exact remainder P - P_hi, so the product keeps P to a
-// relative error below 2^-14 (V is bf16 already) and accumulates in fp32.  One unit = (group, sequence, chunk of kClsaRows =
-// 128 selected rows); its K and V rows are gathered into LDS once, and P
+// relative error below 2^-14 (V is bf16 already) and accumulates in fp32.
+// One unit = (group, sequence, chunk of ROWS selected rows) run by ROWS * 2
+// threads: 128 rows and four waves, or 256 rows and eight waves (the units
+// that also select); its K and V rows are gathered into LDS once, and P
 // reuses the K tile's LDS once S is computed.  Wave w owns row block w for S
-// and channel block w for O.  MFMA 32x32: A element (lane%32, k-slice
-// lane/32), B element (k-slice lane/32, lane%32), result (8*(r/4) +
+// and, for O, channel block w % 4 over row part w / 4 (with eight waves the
+// two parts are summed through LDS).  MFMA 32x32: A element (lane%32,
+// k-slice lane/32), B element (k-slice lane/32, lane%32), result (8*(r/4) +
 // 4*(lane/32) + r%4, lane%32) in register r.  Layers labelled streaming for
 // the group are computed and discarded.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-constexpr int kClsaPad = 136;          // bf16 elements per K/V/Q LDS row (128 + 16 B of padding)
-constexpr int kPPad = kClsaRows + 4;   // floats per P row (16-byte aligned rows)
-constexpr int kClsaTileBytes = kClsaRows * kClsaPad * 2;  // one K or V tile in LDS
-constexpr int kClsaQBytes = 32 * kClsaPad * 2;            // the query tile
-constexpr int kClsaLdsBytes = 2 * kClsaTileBytes + kClsaQBytes;
+constexpr int kClsaPad = 136;  // bf16 elements per K/V/Q LDS row (128 + 16 B of padding)
+// LDS of a unit of ROWS rows: the K and V tiles, then the query tile
+template <int ROWS>
+constexpr int clsa_lds_bytes() { return 2 * ROWS * kClsaPad * 2 + 32 * kClsaPad * 2; }
+constexpr int kClsaLdsBytes = clsa_lds_bytes<kClsaRows>();
+constexpr int kFusedLdsBytes = clsa_lds_bytes<kFusedRows>();
 
 // The attention of one unit over its nrows gathered rows, whose cache
 // positions rows(r) gives (r < nrows; values in [0, T)), into the chunk
-// partials.  qreg holds this thread's two 16-byte pieces of the query tile
-// (see clsa_load_q), already loaded.  lds: kClsaLdsBytes, 16-byte aligned;
-// s_ml/s_lab small LDS arrays.  The caller synchronises before the call when
-// lds was in other use.
-__device__ __forceinline__ void clsa_load_q(const Geo& g, int b, int gi, uint4 (&qreg)[2]) {
+// partials.  qreg holds this thread's 16-byte pieces of the query tile (see
+// clsa_load_q), already loaded.  lds: clsa_lds_bytes<ROWS>(), 16-byte
+// aligned; s_ml/s_lab small LDS arrays.  The caller synchronises before the
+// call when lds was in other use.
+template <int BT>
+__device__ __forceinline__ void clsa_load_q(const Geo& g, int b, int gi, uint4 (&qreg)[32 * 16 / BT]) {
   constexpr int D = 128;
   const int QV = g.Lq * g.G;
-  static_assert(32 * 16 == 2 * NT, "two query elements per thread");
+  static_assert((32 * 16) % BT == 0, "whole query elements per thread");
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = threadIdx.x + i * NT, qv = min(e >> 4, QV - 1), part = e & 15;
+  for (int i = 0; i < 32 * 16 / BT; ++i) {
+    const int e = threadIdx.x + i * BT, qv = min(e >> 4, QV - 1), part = e & 15;
     const int n = qv / g.G, h = qv - n * g.G;
     qreg[i] = ld16((const uint16_t*)g.q + (((size_t)n * g.B + b) * g.Hq + (size_t)gi * g.G + h) * D + part * 8);
   }
@@ -1798,18 +1810,26 @@ __device__ __forceinline__ void clsa_load_q(const Geo& g, int b, int gi, uint4 (
 // Q_FIRST: the query tile goes to LDS before the row loads are issued (its
 // registers are then free during the gather; the query loads completed
 // earlier); otherwise after them, so its loads overlap theirs.
-template <bool Q_FIRST, class Rows>
+template <int ROWS, int BT, bool Q_FIRST, class Rows>
 __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, int chunk, int nrows, Rows rows,
-                                                 const uint4 (&qreg)[2], unsigned char* lds, float (*s_ml)[2],
-                                                 uint8_t* s_lab) {
+                                                 const uint4 (&qreg)[32 * 16 / BT], unsigned char* lds,
+                                                 float (*s_ml)[2], uint8_t* s_lab) {
   constexpr int D = 128;
-  constexpr int ROWS = kClsaRows;
+  constexpr int NWV = BT / 64;         // waves
+  constexpr int QPT = 32 * 16 / BT;    // query tile elements per thread
+  constexpr int PP = ROWS + 4;         // floats per P row (16-byte aligned rows)
+  constexpr int TILE = ROWS * kClsaPad * 2;  // one K or V tile in LDS
+  constexpr int NPART = NWV / 4;       // row parts of P V (four channel blocks)
+  constexpr int LPQ = BT / 32;         // softmax lanes per query vector
   constexpr float kScale = 0.08838834764831845f * 1.4426950408889634f;
-  static_assert(32 * kPPad * sizeof(float) <= kClsaTileBytes, "P fits the K tile");
+  static_assert(ROWS == 32 * NWV && (NPART == 1 || NPART == 2), "a 32-row block of S per wave");
+  static_assert(ROWS == 16 * LPQ, "16 softmax rows per lane");
+  static_assert(32 * PP * sizeof(float) + (NPART - 1) * 4 * 16 * 64 * sizeof(float) <= TILE,
+                "P (and the second row part of O) fit the K tile");
   uint16_t (*s_k)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(lds);
-  float (*s_p)[kPPad] = reinterpret_cast<float (*)[kPPad]>(lds);
-  uint16_t (*s_v)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(lds + kClsaTileBytes);
-  uint16_t (*s_q)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(lds + 2 * kClsaTileBytes);
+  float (*s_p)[PP] = reinterpret_cast<float (*)[PP]>(lds);
+  uint16_t (*s_v)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(lds + TILE);
+  uint16_t (*s_q)[kClsaPad] = reinterpret_cast<uint16_t (*)[kClsaPad]>(lds + 2 * TILE);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int QV = g.Lq * g.G;
   const size_t kvs = (size_t)b * g.Hkv + gi;
@@ -1818,11 +1838,11 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
   // every K and V element of the tile (16 bytes per element e = row * 16 +
   // part) is loaded unconditionally (rows past the end read the last valid
   // one, then store zeros), so the loads issue as one group
-  static_assert(ROWS * 16 == 8 * NT, "eight tile elements per thread");
+  static_assert(ROWS * 16 == 8 * BT, "eight tile elements per thread");
   auto store_q = [&]() {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + i * NT;
+    for (int i = 0; i < QPT; ++i) {
+      const int e = tid + i * BT;
       *reinterpret_cast<uint4*>(&s_q[e >> 4][(e & 15) * 8]) = (e >> 4) < QV ? qreg[i] : make_uint4(0, 0, 0, 0);
     }
   };
@@ -1839,8 +1859,8 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
   for (int u = 0; u < 8; ++u) {
     // positions come from the selection and lie in [0, T); the clamp only
     // keeps a corrupted index from reading another row of the slice
-    const int r = min((tid + u * NT) >> 4, nrows - 1);
-    off[u] = min(max(rows(r), 0), g.T - 1) * (D * 2) + ((tid + u * NT) & 15) * 16;
+    const int r = min((tid + u * BT) >> 4, nrows - 1);
+    off[u] = min(max(rows(r), 0), g.T - 1) * (D * 2) + ((tid + u * BT) & 15) * 16;
   }
   uint4 rk[8], rv[8];
 #pragma unroll
@@ -1852,7 +1872,7 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
   if constexpr (!Q_FIRST) store_q();
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int e = tid + u * NT, r = e >> 4;
+    const int e = tid + u * BT, r = e >> 4;
     const bool live = r < nrows;
     *reinterpret_cast<uint4*>(&s_k[r][(e & 15) * 8]) = live ? rk[u] : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(&s_v[r][(e & 15) * 8]) = live ? rv[u] : make_uint4(0, 0, 0, 0);
@@ -1879,9 +1899,9 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
     }
   }
   __syncthreads();
-  // softmax: 8 consecutive lanes per query vector, 16 rows each
+  // softmax: LPQ consecutive lanes per query vector, 16 rows each
   {
-    const int qv = tid >> 3, seg = tid & 7;
+    const int qv = tid / LPQ, seg = tid % LPQ;
     float4* pr = reinterpret_cast<float4*>(&s_p[qv][seg * 16]);
     float z[16];
 #pragma unroll
@@ -1895,14 +1915,14 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
     float m = z[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) m = fmaxf(m, z[i]);
-    m = group_max<8>(m);
+    m = group_max<LPQ>(m);
     float l = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       z[i] = exp2f(z[i] - m);
       l += z[i];
     }
-    l = group_sum<8>(l);
+    l = group_sum<LPQ>(l);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = make_float4(z[4 * i], z[4 * i + 1], z[4 * i + 2], z[4 * i + 3]);
     if (seg == 0) {
@@ -1911,15 +1931,19 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
     }
   }
   __syncthreads();
-  // O = P V for channel block `wave`, P split into bf16 hi + lo: a pair of
-  // values packs the upper halves of two words in one byte permute
+  // O = P V for channel block cb over row part rp, P split into bf16 hi +
+  // lo: a pair of values packs the upper halves of two words in one byte
+  // permute
+  const int cb = wave & 3, rp = wave >> 2;
+  const int dcol = cb * 32 + (lane & 31);
   f32x16_t o;
 #pragma unroll
   for (int r = 0; r < 16; ++r) o[r] = 0.f;
   {
-    const int dcol = wave * 32 + (lane & 31), ks = (lane >> 5) * 8;
+    constexpr int RW = ROWS / NPART;
+    const int ks = (lane >> 5) * 8;
 #pragma unroll 2
-    for (int k0 = 0; k0 < ROWS; k0 += 16) {
+    for (int k0 = rp * RW; k0 < rp * RW + RW; k0 += 16) {
       const float4 p0 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks]);
       const float4 p1 = *reinterpret_cast<const float4*>(&s_p[lane & 31][k0 + ks + 4]);
       const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -1941,9 +1965,21 @@ __device__ __forceinline__ void clsa_attend_unit(const Geo& g, int b, int gi, in
       o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, lw), vb8, o, 0, 0, 0);
     }
   }
-  // partials: acc for (layer, head) = qv, channel block `wave`
-  {
-    const int dcol = wave * 32 + (lane & 31);
+  if constexpr (NPART == 2) {
+    // the second row part's sums through the K tile's LDS behind P
+    float* s_o = reinterpret_cast<float*>(lds + 32 * PP * sizeof(float));
+    if (rp == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_o[(cb * 16 + r) * 64 + lane] = o[r];
+    }
+    __syncthreads();
+    if (rp == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] += s_o[(cb * 16 + r) * 64 + lane];
+    }
+  }
+  // partials: acc for (layer, head) = qv, channel block cb
+  if (rp == 0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qv = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -1978,9 +2014,10 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
     const int32_t* ix = g.idx + iitem * g.n_fac + (size_t)chunk * g.cf;
     const int nrows = min(g.cf, g.n_fac - chunk * g.cf);
     __syncthreads();
-    uint4 qreg[2];
-    clsa_load_q(g, b, gi, qreg);
-    clsa_attend_unit<false>(g, b, gi, chunk, nrows, [&](int r) { return ix[r]; }, qreg, s_lds, s_ml, s_lab);
+    uint4 qreg[32 * 16 / NT];
+    clsa_load_q<NT>(g, b, gi, qreg);
+    clsa_attend_unit<kClsaRows, NT, false>(g, b, gi, chunk, nrows, [&](int r) { return ix[r]; }, qreg, s_lds, s_ml,
+                                           s_lab);
   }
 }
 
@@ -2020,11 +2057,13 @@ struct SelSrcT {
 };
 
 // Selection fused into the shared-index attention (prefiltered path, T <=
-// kShortMaxT): every unit (sequence, group, chunk) finds its item's exact
-// top-n_fac cut from the candidates itself -- the item's units repeat the
-// same deterministic work side by side instead of waiting for one final
-// workgroup -- then takes the selected tokens whose ascending rank falls in
-// its chunk, writes those idx_out entries, and attends over them.
+// kShortMaxT): every unit (sequence, group, chunk of kFusedRows rows; eight
+// waves and almost all of a CU's LDS, so a CU runs one copy of the
+// selection) finds its item's exact top-n_fac cut from the candidates
+// itself -- the item's units repeat the same deterministic work side by
+// side instead of waiting for one final workgroup -- then takes the
+// selected tokens whose ascending rank falls in its chunk, writes those
+// idx_out entries, and attends over them.
 //   1. candidates -> LDS (from global memory when more than fit), counted
 //      in 2048 bins of (key - tau) >> sh as in the final kernel;
 //   2. the bin holding the n_fac-th candidate; its members (<= kRankMax)
@@ -2040,10 +2079,10 @@ constexpr int kSelBitmapWords = kShortMaxT / 32;                      // 4096
 constexpr int kSelHistBytes = kHistBins * 4;                          // 8 KB: histogram, later u16 prefixes
 constexpr int kSelListBytes = kRankMax * 8;                           // 2 KB
 constexpr int kSelCandOfs = kSelHistBytes + kSelListBytes + kSelBitmapWords * 4;
-constexpr int kSelCandLds = (kClsaLdsBytes - kSelCandOfs) / 8;        // candidates held in LDS
+constexpr int kSelCandLds = (kFusedLdsBytes - kSelCandOfs) / 8;       // candidates held in LDS
 static_assert(kSelBitmapWords * 2 <= kSelHistBytes, "u16 prefixes fit the histogram");
 static_assert(kSelCandLds == kFusedSelCand, "the host sizes the fused selection with this capacity");
-static_assert(kClsaRows <= NT, "one thread per row of a unit");
+static_assert(kFusedRows <= kFusedThreads && kFusedRows * 2 == kFusedThreads, "one thread per row of a unit");
 
 // The bit position of the k-th set bit (0-based, k < popcount) of x.
 __device__ __forceinline__ int nth_set_bit(uint32_t x, int k) {
@@ -2063,13 +2102,14 @@ __device__ __forceinline__ int nth_set_bit(uint32_t x, int k) {
   return pos;
 }
 
-__global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
-  constexpr int BT = NT;
-  __shared__ __attribute__((aligned(16))) unsigned char s_lds[kClsaLdsBytes];
+__global__ __launch_bounds__(kFusedThreads, 1) void select_attn_clsa_kernel(Geo g) {
+  constexpr int BT = kFusedThreads;
+  constexpr int NWV = BT / 64;
+  __shared__ __attribute__((aligned(16))) unsigned char s_lds[kFusedLdsBytes];
   __shared__ float s_ml[32][2];
   __shared__ uint8_t s_lab[32];
-  __shared__ int s_rows[kClsaRows];
-  __shared__ int s_w[NWAVE];
+  __shared__ int s_rows[kFusedRows];
+  __shared__ int s_w[NWV];
   __shared__ uint32_t s_res[2];
   __shared__ int s_m;
   uint32_t* s_hist = reinterpret_cast<uint32_t*>(s_lds);
@@ -2081,7 +2121,7 @@ __global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the bitmap always spans kShortMaxT tokens (the words past T stay 0), so
   // the prefix scan below has a fixed shape
-  constexpr int nrow64 = kSelBitmapWords / (64 * NWAVE);  // 64-word rows per wave
+  constexpr int nrow64 = kSelBitmapWords / (64 * NWV);  // 64-word rows per wave
   constexpr int nwords = kSelBitmapWords;
   const int J = g.Hkv * g.B * g.nch_f;
   for (int j = blockIdx.x; j < J; j += gridDim.x) {
@@ -2093,8 +2133,8 @@ __global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
     const int nrows = min(g.cf, g.n_fac - r0);
     int32_t* ox = g.idx_out ? g.idx_out + ((size_t)b * g.Hkv + gi) * g.n_fac : nullptr;
     __syncthreads();
-    uint4 qreg[2];
-    clsa_load_q(g, b, gi, qreg);  // in flight during the selection
+    uint4 qreg[32 * 16 / BT];
+    clsa_load_q<BT>(g, b, gi, qreg);  // in flight during the selection
     const uint32_t count = g.info[(size_t)item * 4 + 2];
     const uint2 th = g.tau[item];
     for (int w = tid; w < nwords; w += BT) s_bm[w] = 0u;
@@ -2137,7 +2177,7 @@ __global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
 #pragma unroll 8
         for (int q = 0; q < m; ++q) {
           const uint2 o = s_list[q];
-          r += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1u : 0u;
+          r += before(o, me);
         }
         if (r < need) mark(me.y);
       }
@@ -2200,7 +2240,7 @@ __global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
     }
     __syncthreads();
     // exclusive prefix counts of the bitmap words: each wave a contiguous
-    // quarter, lane L on word L of each 64-word row; the rows' scans are
+    // share, lane L on word L of each 64-word row; the rows' scans are
     // independent, then carried through
     {
       const uint32_t* wb = s_bm + wave * nrow64 * 64;
@@ -2239,7 +2279,8 @@ __global__ __launch_bounds__(NT, 2) void select_attn_clsa_kernel(Geo g) {
       if (ox) ox[rank] = t;
     }
     __syncthreads();
-    clsa_attend_unit<true>(g, b, gi, chunk, nrows, [&](int r) { return s_rows[r]; }, qreg, s_lds, s_ml, s_lab);
+    clsa_attend_unit<kFusedRows, BT, true>(g, b, gi, chunk, nrows, [&](int r) { return s_rows[r]; }, qreg, s_lds,
+                                           s_ml, s_lab);
   }
 }
 
@@ -2680,7 +2721,7 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
       const int grid_c = clampi((long long)g.Hkv * g.B * g.nch_f, 1, g.grid);
       if (g.fuse_sel) {
         KTimer ts("select_attend", s);
-        select_attn_clsa_kernel<<<grid_c, NT, 0, s>>>(g);
+        select_attn_clsa_kernel<<<grid_c, kFusedThreads, 0, s>>>(g);
       } else {
         attn_clsa_mfma_kernel<<<grid_c, NT, 0, s>>>(g);
       }

@@ -18,7 +18,9 @@ constexpr int kSampleTokens = 4096;  // tokens scored per item to place the pref
 constexpr int kPrefilterMaxT = 524288;  // token bitmap of the prefiltered path fits the final kernel's LDS
 constexpr int kShortMaxT = 131072;      // up to here the final kernel's token bitmap has an LDS array of its own
 constexpr int kSelMaxLong = 8192;       // beyond kShortMaxT: n_fac the final kernel compacts beside its bitmap
-constexpr int kFusedSelCand = 6464;     // candidates the selection fused into the shared-index attention holds in LDS
+constexpr int kFusedSelCand = 15168;    // candidates the selection fused into the shared-index attention holds in LDS
+constexpr int kFusedRows = 256;         // rows per unit of that fused kernel (eight waves, one unit per CU)
+constexpr int kFusedThreads = 512;
 
 // One decode call, with the workspace carved.  Passed by value to kernels.
 struct Geo {

@@ -6,8 +6,9 @@ vectors, up to 131072 tokens) every matrix-core attention unit of a
 itself.  These cases drive each way a unit can read them: from LDS (the
 common case), from global memory (more candidates than its LDS holds), or by
 rescoring the whole item (the sample misleads, or the candidates overflow
-their slots); and the unfused path of short contexts (general selection,
-then the attention units).  Index sets are compared exactly with the
+their slots); and the unfused paths, for short contexts (general
+selection) and for more expected candidates than the units hold (the final
+kernel's selection), each followed by the attention units.  Index sets are compared exactly with the
 oracle's top-n (ties to the lower token) where scores tie exactly, else with
 the 1e-5 tie band; outputs with |d| <= 2e-3 + 1e-2 |ref|."""
 import numpy as np
@@ -62,16 +63,17 @@ def test_fused_path_taken_for_the_c3_shape():
 
 
 def test_candidates_beyond_lds_read_from_global_memory():
-    """8000 tokens of one group share the top score exactly, so about a
-    quarter of the sample sits on it, the candidate threshold lands on it and
-    all 8000 pass: more than a unit's LDS holds (6464).  The cut falls inside
-    the tie: the lowest-index tied tokens are selected."""
+    """15500 of the 32768 tokens of one group share the top score exactly, so
+    about half of the sample sits on it, the candidate threshold lands on it
+    and all 15500 pass: more than a unit's LDS holds (15168), fewer than the
+    16384 candidate slots.  The cut falls inside the tie: the lowest-index
+    tied tokens are selected."""
     cfg = _cfg()
     print("case clsa fused: candidates from global memory", flush=True)
     case = U.DeviceCase(cfg)
     b, g, G = 0, 2, cfg.group
     rng = np.random.default_rng(21)
-    pos = np.sort(rng.choice(np.arange(1, cfg.ctx_len), size=8000, replace=False))
+    pos = np.sort(rng.choice(np.arange(1, cfg.ctx_len), size=15500, replace=False))
     qbar = U.f64(case.hi.q[0, b, g * G:(g + 1) * G], cfg).mean(axis=0)
     dom = np.concatenate([case.hi.i_dom[0, g], case.hi.i_dom[0, g] + cfg.d_head // 2])
     vals = np.where(qbar[dom] >= 0, 64.0, -64.0).astype(np.float32)
@@ -84,7 +86,7 @@ def test_candidates_beyond_lds_read_from_global_memory():
     out, idx, _ = U.run_clsa(case)
     ref, ridx, scores = _oracle(cfg, case, b, g)
     tied = np.sum(scores == scores[pos[0]])
-    assert tied >= 8000 and np.sum(scores > scores[pos[0]]) < cfg.n_fac
+    assert tied >= 15500 and np.sum(scores > scores[pos[0]]) < cfg.n_fac
     assert (idx[b, g] == ridx).all()
     for n in range(cfg.n_layers):
         U.check_out(out[n, b, g * G:(g + 1) * G], ref[n], f"global-candidates out n{n}")
@@ -152,3 +154,21 @@ def test_short_context_unfused_path():
         U.check_index_set(idx[b, g], scores, cfg.n_fac, f"short idx b{b} g{g}")
         for n in range(cfg.n_layers):
             U.check_out(out[n, b, g * G:(g + 1) * G], ref[n], f"short out n{n} b{b} g{g}")
+
+
+def test_expected_candidates_beyond_lds_unfused_path():
+    """About 11100 expected candidates (32768 tokens, n_fac 8000) are more
+    than the fused units may count on holding in LDS (70% of 15168), so the
+    final kernel selects each item once and the 128-row matrix-core units
+    read its index (a ragged last chunk of 64 rows)."""
+    cfg = _cfg(n_fac=8000)
+    print("case clsa unfused prefiltered selection", flush=True)
+    assert H.sparse_selection_path(U.dims_of(cfg)) == 1
+    case = U.DeviceCase(cfg)
+    out, idx, _ = U.run_clsa(case)
+    G = cfg.group
+    for (b, g) in [(0, 3), (1, 6)]:
+        ref, _, scores = _oracle(cfg, case, b, g)
+        U.check_index_set(idx[b, g], scores, cfg.n_fac, f"unfused idx b{b} g{g}")
+        for n in range(cfg.n_layers):
+            U.check_out(out[n, b, g * G:(g + 1) * G], ref[n], f"unfused out n{n} b{b} g{g}")
