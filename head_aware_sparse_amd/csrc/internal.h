@@ -9,7 +9,7 @@ namespace has {
 
 constexpr int kHistBins = 2048;      // first radix digit: key bits 31..21
 constexpr int kCandLds = 8192;       // candidates held in LDS by the threshold pass
-constexpr int kMaxChunkRows = 512;   // attention rows per work unit
+constexpr int kMaxChunkRows = 1024;  // attention rows per work unit
 constexpr int kClsaRows = 128;       // rows per layer-fused shared-index unit (staged in LDS)
 constexpr int kMaxTipChunks = 1024;  // score chunks per item
 constexpr int kMaxPairs = 8192;      // (layer, KV group) pairs per call
