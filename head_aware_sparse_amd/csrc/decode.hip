@@ -1142,9 +1142,10 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(Geo g) {
   __shared__ int s_m;
   // !LONG: the prefix counts (u16) reuse the histogram, free by then
   static_assert(kHistBins * sizeof(uint32_t) >= kShortMaxT / 32 * sizeof(uint16_t), "u16 prefixes in s_hist");
-  // bitmap words per thread for the prefix counts: a multiple of 4 (16-byte
-  // reads), so the bitmap spans BT * per words
-  const int per = ((g.bm_words + BT - 1) / BT + 3) & ~3;
+  // bitmap words per thread for the prefix counts, so the bitmap spans BT *
+  // per words; for LONG a multiple of 4, which keeps the prefix counts
+  // placed behind it 16-byte aligned
+  const int per = LONG ? ((g.bm_words + BT - 1) / BT + 3) & ~3 : (g.bm_words + BT - 1) / BT;
   constexpr int kSelWords = kSelMaxLong;  // n_fac on this path, a multiple of 4 words
   constexpr int kPerMax = (kPrefilterMaxT / 32 / BT + 3) & ~3;
   static_assert(kCandFast * sizeof(uint2) >= (kSelWords + BT * kPerMax) * sizeof(uint32_t) +
@@ -1174,7 +1175,7 @@ __global__ __launch_bounds__(kFinalThreads) void final_kernel(Geo g) {
     // conflict-free; a first pass sums the quarters for the wave offsets.
     auto prefix = [&](const uint32_t* bm, uint16_t* pre) {
       const int lane = tid & 63, wave = tid >> 6;
-      const int qw = BT * per / BW;  // a multiple of 64 (per is a multiple of 4)
+      const int qw = BT * per / BW;  // a multiple of 64 (BT / BW = 64)
       const uint32_t* wb = bm + wave * qw;
       uint16_t* wp = pre + wave * qw;
       uint32_t tot = 0;
