@@ -225,6 +225,45 @@ def test_prefilter_fallback_too_few_candidates(T):
     U.check_out(out[l, 0, g * cfg.group:(g + 1) * cfg.group], ref, "fallback out")
 
 
+@pytest.mark.parametrize("T,n_fac", [(32768, 2048), (262144, 256)], ids=["T32k", "T256k"])
+def test_cut_above_sampled_maximum(T, n_fac):
+    """More than n_fac tokens outside the sample get their keys scaled up 40x
+    (tokens whose score then exceeds every sampled one), so the n_fac-th
+    score lies above the sampled maximum, in the candidates' clamped top
+    first-digit bin, while the candidate count stays within its slots: the
+    final selection must resolve that bin exactly (with the token bitmap in
+    its own LDS array, and beyond 131072 tokens in the candidate buffer)."""
+    import numpy as np
+    cfg = R.get_config("c1", ctx_len=T, n_fac=n_fac, batch=1)
+    print(f"case cut above sampled max T={T} n_fac={n_fac}", flush=True)
+    hi = R.HostInputs(cfg, with_weights=False)
+    sampled = np.concatenate([np.arange(16) + (sb * (T - 16)) // 255 for sb in range(256)])
+    (l, g) = R.planted_groups(cfg)[0]
+    G = cfg.group
+    case = U.DeviceCase(cfg, hi=hi)
+    assert H.sparse_selection_path(case.dims) == 1
+    from oracle import fasa
+    q64 = U.f64(hi.q[l, 0, g * G:(g + 1) * G], cfg)
+    s0 = fasa.tip_scores(q64, U.f64(hi.rows("k", l, 0, g), cfg), hi.i_dom[l, g])
+    smax = s0[sampled].max()
+    outside = np.setdiff1d(np.flatnonzero(s0 > smax / 30.0), sampled)
+    assert outside.size > n_fac + 100
+    lift = np.random.default_rng(5).choice(outside, n_fac + 100, replace=False)
+    kk = case.k[l, 0, g].float()
+    kk[torch.from_numpy(lift).cuda()] *= 40.0
+    case.k[l, 0, g] = kk.to(case.k.dtype)
+    H.kdom_pack(case.kd_dims, case.k, case.i_dom, case.k_dom)
+    torch.cuda.synchronize()
+    out, idx, _ = case.run()
+    k_host = case.k[l, 0, g].view(torch.int16).cpu().numpy().view(np.uint16)
+    scores = fasa.tip_scores(q64, U.f64(k_host, cfg), hi.i_dom[l, g])
+    assert np.sort(scores)[-n_fac] > scores[sampled].max(), "the cut must lie above every sampled score"
+    U.check_index_set(idx[l, 0, g], scores, cfg.n_fac, "cut above sampled max idx")
+    ref, _ = U.oracle_item_custom(cfg, hi.q[l, 0, g * G:(g + 1) * G], k_host, hi.rows("v", l, 0, g),
+                                  hi.i_dom[l, g], True)
+    U.check_out(out[l, 0, g * G:(g + 1) * G], ref, "cut above sampled max out")
+
+
 @pytest.mark.parametrize("shared_q,levels,T", [(True, 1, 32768), (False, 2, 32768), (False, 2, 262144)],
                          ids=["coarse-ties", "fine-ties", "fine-ties-256k"])
 def test_tied_scores_select_exactly(shared_q, levels, T):
