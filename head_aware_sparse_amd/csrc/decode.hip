@@ -987,6 +987,59 @@ __device__ void exact_threshold(const Src& src, uint32_t need, uint32_t* s_hist,
   }
 }
 
+// Elements for the selection fused into the attention: (key, token) pairs
+// through a generic pointer (LDS, or global memory when an item's
+// candidates do not fit there), or an item's whole score row.  One type for
+// the three cases, so the threshold helpers (and their LDS) are instantiated
+// once; four reads in flight per thread.
+template <int BT = NT>
+struct SelSrcT {
+  const uint2* pairs;  // null: the score row sc
+  const float* sc;
+  int n;
+  template <class F>
+  __device__ __forceinline__ void for_each(F f) const {
+    int i = threadIdx.x;
+    if (pairs) {
+      for (; i + 3 * BT < n; i += 4 * BT) {
+        const uint2 a = pairs[i], b = pairs[i + BT], c = pairs[i + 2 * BT], d = pairs[i + 3 * BT];
+        f(a.x, a.y);
+        f(b.x, b.y);
+        f(c.x, c.y);
+        f(d.x, d.y);
+      }
+      for (; i < n; i += BT) f(pairs[i].x, pairs[i].y);
+    } else {
+      for (; i + 3 * BT < n; i += 4 * BT) {
+        const float a = sc[i], b = sc[i + BT], c = sc[i + 2 * BT], d = sc[i + 3 * BT];
+        f(f2key(a), (uint32_t)i);
+        f(f2key(b), (uint32_t)(i + BT));
+        f(f2key(c), (uint32_t)(i + 2 * BT));
+        f(f2key(d), (uint32_t)(i + 3 * BT));
+      }
+      for (; i < n; i += BT) f(f2key(sc[i]), (uint32_t)i);
+    }
+  }
+};
+
+// The bit position of the k-th set bit (0-based, k < popcount) of x.
+__device__ __forceinline__ int nth_set_bit(uint32_t x, int k) {
+  int pos = 0;
+#pragma unroll
+  for (int half = 16; half >= 1; half >>= 1) {
+    const uint32_t low = x & ((1u << half) - 1u);
+    const int c = __popc(low);
+    if (k >= c) {
+      k -= c;
+      x >>= half;
+      pos += half;
+    } else {
+      x = low;
+    }
+  }
+  return pos;
+}
+
 // sample: TIP keys of kSampleTokens tokens per index item, in 64 V evenly
 // spread blocks of 64 / V tokens (V 16-byte pieces per key row: 256 blocks of
 // 16 for bf16 d 128); one unit = (item, 256 of the tokens), each wave scoring
@@ -1500,7 +1553,178 @@ __global__ __launch_bounds__(NT) void select_c_kernel(Geo g) {
 // query heads share every loaded row: lanes of a row (LPR of them, 16 bytes
 // each) form the dot products, then p = exp2(z - m) per head, then P.V.
 // Output: per head acc[d] = sum p v, m (log2 domain), l = sum p.
-template <typename E, int D, int G>
+// LDS of the selection inside an attention unit: the histogram (later the u16
+// prefix counts), the member list, a token bitmap of kShortMaxT bits and up
+// to kUnitSelCand candidates (more are read from global memory again).
+constexpr int kUnitSelCand = 4096;
+constexpr int kUnitSelCandOfs = kHistBins * 4 + kRankMax * 8 + kShortMaxT / 32 * 4;
+constexpr int kUnitSelBytes = kUnitSelCandOfs + kUnitSelCand * 8;
+
+// The exact top-n_fac cut of index item `item` from its candidates, by one
+// attention unit (NT threads) for itself -- FASA §2.B.1, the same selection
+// as final_kernel, repeated by every unit of the item side by side instead
+// of one workgroup per item in a launch of its own -- and the cache
+// positions of the selected tokens of ascending rank r0 .. r0 + nrows - 1
+// into rows (LDS), with those idx_out entries (ox, or null).  Candidates are
+// read from global memory (the item's units share them through the L2):
+// they are counted in 2048 bins of (key - tau) >> sh, the members of the bin
+// holding the n_fac-th are ranked directly (at most kRankMax, below the
+// clamped top bin), else the general radix threshold; selected tokens are
+// marked in a token bitmap, whose words' exclusive prefix counts give each
+// rank's word and bit.  Fewer than n_fac candidates or an overflow: the unit
+// rescores the item in full (every unit writes the same score row).
+// lds: kUnitSelBytes, 16-byte aligned; s_qd: R floats of LDS (rescoring).
+template <typename E>
+__device__ void unit_select_rows(const Geo& g, int item, int r0, int nrows, int* rows, int32_t* ox,
+                                 unsigned char* lds, float* s_qd) {
+  __shared__ int s_w[NWAVE];
+  __shared__ uint32_t s_res[2];
+  __shared__ int s_m;
+  uint32_t* s_hist = reinterpret_cast<uint32_t*>(lds);
+  uint16_t* s_pre = reinterpret_cast<uint16_t*>(lds);
+  uint2* s_list = reinterpret_cast<uint2*>(lds + kHistBins * 4);
+  uint32_t* s_bm = reinterpret_cast<uint32_t*>(lds + kHistBins * 4 + kRankMax * 8);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // bitmap words per wave: whole 64-word rows covering bm_words (<= kShortMaxT / 32)
+  const int qw = (g.bm_words + NT - 1) / NT * 64;
+  const int nwords = NWAVE * qw;
+  const uint32_t count = g.info[(size_t)item * 4 + 2];
+  const uint2 th = g.tau[item];
+  for (int w = tid; w < nwords; w += NT) s_bm[w] = 0u;
+  for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+  if (tid == 0) s_m = 0;
+  auto mark = [&](uint32_t t) { atomicOr(&s_bm[t >> 5], 1u << (t & 31)); };
+  auto cut_general = [&](const SelSrcT<NT>& src) {
+    uint32_t kstar, tstar;
+    exact_threshold<NT>(src, (uint32_t)g.n_fac, s_hist, s_w, s_res, kstar, tstar);
+    src.for_each([&](uint32_t k, uint32_t t) {
+      if (k > kstar || (k == kstar && t <= tstar)) mark(t);
+    });
+  };
+  const uint2* gc = g.cand + (size_t)item * g.cand_cap;
+  if (count >= (uint32_t)g.n_fac && count <= (uint32_t)g.cand_cap) {
+    const uint32_t tau = th.x;
+    const uint32_t span = th.y > tau ? th.y - tau : 0u;
+    const int bits = span ? 32 - __clz(span) : 0;
+    const int sh = bits > 11 ? bits - 11 : 0;
+    __syncthreads();
+    // candidates -> LDS when they fit, counted by their first digit
+    uint2* s_c = reinterpret_cast<uint2*>(lds + kUnitSelCandOfs);
+    const bool in_lds = count <= (uint32_t)kUnitSelCand;
+    const uint4* c4 = reinterpret_cast<const uint4*>(gc);
+    const int n4 = (int)(count + 1) / 2;
+    constexpr int kLd = 4;  // 16-byte loads in flight per thread
+    for (int i0 = tid; i0 < n4; i0 += kLd * NT) {
+      uint4 r[kLd];
+#pragma unroll
+      for (int q = 0; q < kLd; ++q) r[q] = i0 + q * NT < n4 ? c4[i0 + q * NT] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < kLd; ++q) {
+        const int i = i0 + q * NT;
+        if (i < n4) {
+          if (in_lds) s_c[2 * i] = make_uint2(r[q].x, r[q].y);
+          atomicAdd(&s_hist[min((r[q].x - tau) >> sh, (uint32_t)kHistBins - 1u)], 1u);
+          if (2 * i + 1 < (int)count) {
+            if (in_lds) s_c[2 * i + 1] = make_uint2(r[q].z, r[q].w);
+            atomicAdd(&s_hist[min((r[q].z - tau) >> sh, (uint32_t)kHistBins - 1u)], 1u);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    int bin;
+    uint32_t above;
+    find_bin_top<NT>(s_hist, kHistBins, (uint32_t)g.n_fac, s_w, s_res, bin, above);
+    const uint32_t members = s_hist[bin];
+    __syncthreads();
+    const SelSrcT<NT> gsrc{gc, nullptr, (int)count};
+    // everything above bin ub is selected; its members are ranked
+    auto cut_binned = [&](const auto& src, uint32_t ub) {
+      src.for_each([&](uint32_t k, uint32_t t) {
+        const uint32_t d = min((k - tau) >> sh, (uint32_t)kHistBins - 1u);
+        if (d > ub) mark(t);
+        const bool mem = d == ub;
+        const uint64_t bal = __ballot(mem);
+        if (bal) {  // one reservation per wave, by its first active lane
+          const int leader = __builtin_amdgcn_readfirstlane(lane);
+          int base = 0;
+          if (lane == leader) base = atomicAdd(&s_m, __popcll(bal));
+          base = __builtin_amdgcn_readfirstlane(base);
+          if (mem) s_list[base + mbcnt(bal)] = make_uint2(k, t);
+        }
+      });
+      __syncthreads();
+      const uint32_t need = (uint32_t)g.n_fac - above;
+      const int m = s_m;
+      for (int i = tid; i < m; i += NT) {
+        const uint2 me = s_list[i];
+        uint32_t rk = 0;
+#pragma unroll 8
+        for (int q = 0; q < m; ++q) rk += before(s_list[q], me);
+        if (rk < need) mark(me.y);
+      }
+    };
+    if (bin < kHistBins - 1 && members <= (uint32_t)kRankMax) {
+      if (in_lds)
+        cut_binned(LdsPairsT<NT>{s_c, (int)count}, (uint32_t)bin);
+      else
+        cut_binned(gsrc, (uint32_t)bin);
+    } else {
+      cut_general(gsrc);
+    }
+  } else {
+    // rescoring: the item's full score row (the same values from every unit)
+    __syncthreads();
+    const size_t slice = group_query_dom<E>(g, item, s_qd);
+    __syncthreads();
+    const E* kd = (const E*)g.kdom + slice * (size_t)g.tstride * g.R;
+    float* sc = g.scores + (size_t)item * g.Ts;
+    for (int t = tid; t < g.T; t += NT) sc[t] = score_one<E>(kd + (size_t)t * g.R, s_qd, g.R);
+    __threadfence();
+    __syncthreads();
+    cut_general(SelSrcT<NT>{nullptr, sc, g.T});
+  }
+  __syncthreads();
+  // exclusive prefix counts of the bitmap words (u16: < n_fac < 2^16): wave w
+  // scans words [w qw, (w + 1) qw), lane L on word L of each 64-word row
+  {
+    const uint32_t* wb = s_bm + wave * qw;
+    uint32_t tot = 0;
+    for (int k = lane; k < qw; k += 64) tot += (uint32_t)__popc(wb[k]);
+    tot = wave_reduce_u(tot, [](uint32_t x, uint32_t y) { return x + y; });
+    if (lane == 0) s_w[wave] = (int)tot;
+    __syncthreads();  // the histogram (aliased by the prefixes) is free since the cut
+    uint32_t carry = 0;
+    for (int w = 0; w < wave; ++w) carry += (uint32_t)s_w[w];
+    uint16_t* wp = s_pre + wave * qw;
+    for (int k0 = 0; k0 < qw; k0 += 64) {
+      const uint32_t x = (uint32_t)__popc(wb[k0 + lane]);
+      const uint32_t inc = wave_incl_scan_u(x);
+      wp[k0 + lane] = (uint16_t)(carry + inc - x);
+      carry += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    }
+  }
+  __syncthreads();
+  // rank r0 + r: the last word whose prefix count is at most it, then the
+  // set bit of that order inside the word
+  for (int r = tid; r < nrows; r += NT) {
+    const uint32_t rank = (uint32_t)(r0 + r);
+    int lo = 0, hi = nwords - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((uint32_t)s_pre[mid] <= rank) lo = mid;
+      else hi = mid - 1;
+    }
+    const int t = lo * 32 + nth_set_bit(s_bm[lo], (int)(rank - s_pre[lo]));
+    rows[r] = min(max(t, 0), g.T - 1);
+    if (ox) ox[rank] = t;
+  }
+}
+
+// SEL: the prefiltered path's selection runs in the FAC units themselves
+// (unit_select_rows), with no final-selection launch before; its LDS shares
+// the space of the logits and row sums, which are used only after it.
+template <typename E, int D, int G, bool SEL = false>
 __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
   constexpr int CPL = Vec<E>::N;
   constexpr int LPR = D / CPL;
@@ -1508,10 +1732,14 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
   constexpr int RPB = RPW * NWAVE;
   constexpr float kScale = (D == 128 ? 0.08838834764831845f : 0.125f) * 1.4426950408889634f;
   constexpr int AU = 4;  // row groups (16 B per lane each) in flight per wave
-  __shared__ float s_z[G][kMaxChunkRows];
+  constexpr int kZBytes = G * kMaxChunkRows * 4;
+  constexpr int kUBytes = kZBytes + NWAVE * G * D * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_u[SEL && kUnitSelBytes > kUBytes ? kUnitSelBytes : kUBytes];
+  float (*s_z)[kMaxChunkRows] = reinterpret_cast<float (*)[kMaxChunkRows]>(s_u);
+  float (*s_red)[G][D] = reinterpret_cast<float (*)[G][D]>(s_u + kZBytes);
   __shared__ int s_rows[kMaxChunkRows];
-  __shared__ float s_red[NWAVE][G][D];
   __shared__ float s_ml[G][2];
+  __shared__ float s_qd[SEL ? kMaxR : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane % LPR, rsub = lane / LPR;
   // sgrp > 1 (per-head selection): a streaming unit serves the sgrp = G
@@ -1540,11 +1768,16 @@ __global__ __launch_bounds__(NT) void attn_kernel(Geo g) {
     int nrows;
     if (fac) {
       const int iitem = g.idx_bmajor ? b * g.Hkv + gi : (g.clsa ? gi * g.B + b : pa * g.B + b);
-      const int32_t* ix = g.idx + (size_t)iitem * g.n_fac + (size_t)chunk * g.cf;
       nrows = min(g.cf, g.n_fac - chunk * g.cf);
-      // indices come from select_c and are always in [0, T); the clamp only
-      // keeps a corrupted workspace from turning into out-of-range reads
-      for (int r = tid; r < nrows; r += NT) s_rows[r] = min(max(ix[r], 0), g.T - 1);
+      if constexpr (SEL) {
+        int32_t* ox = g.idx_out ? g.idx_out + (((size_t)lq * g.B + b) * g.Hkv + gi) * g.n_fac : nullptr;
+        unit_select_rows<E>(g, iitem, chunk * g.cf, nrows, s_rows, ox, s_u, s_qd);
+      } else {
+        const int32_t* ix = g.idx + (size_t)iitem * g.n_fac + (size_t)chunk * g.cf;
+        // indices come from select_c and are always in [0, T); the clamp only
+        // keeps a corrupted workspace from turning into out-of-range reads
+        for (int r = tid; r < nrows; r += NT) s_rows[r] = min(max(ix[r], 0), g.T - 1);
+      }
     } else {
       nrows = min(g.cs, g.n_srows - chunk * g.cs);
       for (int r = tid; r < nrows; r += NT) {
@@ -2022,41 +2255,6 @@ __global__ __launch_bounds__(NT) void attn_clsa_mfma_kernel(Geo g) {
   }
 }
 
-// Elements for the selection fused into the attention: (key, token) pairs
-// through a generic pointer (LDS, or global memory when an item's
-// candidates do not fit there), or an item's whole score row.  One type for
-// the three cases, so the threshold helpers (and their LDS) are instantiated
-// once; four reads in flight per thread.
-template <int BT = NT>
-struct SelSrcT {
-  const uint2* pairs;  // null: the score row sc
-  const float* sc;
-  int n;
-  template <class F>
-  __device__ __forceinline__ void for_each(F f) const {
-    int i = threadIdx.x;
-    if (pairs) {
-      for (; i + 3 * BT < n; i += 4 * BT) {
-        const uint2 a = pairs[i], b = pairs[i + BT], c = pairs[i + 2 * BT], d = pairs[i + 3 * BT];
-        f(a.x, a.y);
-        f(b.x, b.y);
-        f(c.x, c.y);
-        f(d.x, d.y);
-      }
-      for (; i < n; i += BT) f(pairs[i].x, pairs[i].y);
-    } else {
-      for (; i + 3 * BT < n; i += 4 * BT) {
-        const float a = sc[i], b = sc[i + BT], c = sc[i + 2 * BT], d = sc[i + 3 * BT];
-        f(f2key(a), (uint32_t)i);
-        f(f2key(b), (uint32_t)(i + BT));
-        f(f2key(c), (uint32_t)(i + 2 * BT));
-        f(f2key(d), (uint32_t)(i + 3 * BT));
-      }
-      for (; i < n; i += BT) f(f2key(sc[i]), (uint32_t)i);
-    }
-  }
-};
-
 // Selection fused into the shared-index attention (prefiltered path, T <=
 // kShortMaxT): every unit (sequence, group, chunk of kFusedRows rows; eight
 // waves and almost all of a CU's LDS, so a CU runs one copy of the
@@ -2084,24 +2282,6 @@ constexpr int kSelCandLds = (kFusedLdsBytes - kSelCandOfs) / 8;       // candida
 static_assert(kSelBitmapWords * 2 <= kSelHistBytes, "u16 prefixes fit the histogram");
 static_assert(kSelCandLds == kFusedSelCand, "the host sizes the fused selection with this capacity");
 static_assert(kFusedRows <= kFusedThreads && kFusedRows * 2 == kFusedThreads, "one thread per row of a unit");
-
-// The bit position of the k-th set bit (0-based, k < popcount) of x.
-__device__ __forceinline__ int nth_set_bit(uint32_t x, int k) {
-  int pos = 0;
-#pragma unroll
-  for (int half = 16; half >= 1; half >>= 1) {
-    const uint32_t low = x & ((1u << half) - 1u);
-    const int c = __popc(low);
-    if (k >= c) {
-      k -= c;
-      x >>= half;
-      pos += half;
-    } else {
-      x = low;
-    }
-  }
-  return pos;
-}
 
 __global__ __launch_bounds__(kFusedThreads, 1) void select_attn_clsa_kernel(Geo g) {
   constexpr int BT = kFusedThreads;
@@ -2356,22 +2536,23 @@ __global__ __launch_bounds__(NT) void kdom_pack_kernel(Geo g, E* __restrict__ kd
   }
 }
 
-template <typename E, int D>
+template <typename E, int D, bool SEL>
 hipError_t launch_attn_g(const Geo& g, int grid, hipStream_t s) {
   switch (g.G * g.sgrp) {
-    case 1: attn_kernel<E, D, 1><<<grid, NT, 0, s>>>(g); break;
-    case 2: attn_kernel<E, D, 2><<<grid, NT, 0, s>>>(g); break;
-    case 4: attn_kernel<E, D, 4><<<grid, NT, 0, s>>>(g); break;
-    case 8: attn_kernel<E, D, 8><<<grid, NT, 0, s>>>(g); break;
+    case 1: attn_kernel<E, D, 1, SEL><<<grid, NT, 0, s>>>(g); break;
+    case 2: attn_kernel<E, D, 2, SEL><<<grid, NT, 0, s>>>(g); break;
+    case 4: attn_kernel<E, D, 4, SEL><<<grid, NT, 0, s>>>(g); break;
+    case 8: attn_kernel<E, D, 8, SEL><<<grid, NT, 0, s>>>(g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool SEL = false>
 hipError_t launch_attn(const Geo& g, int grid, hipStream_t s) {
   if (g.bf16)
-    return g.d == 128 ? launch_attn_g<uint16_t, 128>(g, grid, s) : launch_attn_g<uint16_t, 64>(g, grid, s);
-  return g.d == 128 ? launch_attn_g<float, 128>(g, grid, s) : launch_attn_g<float, 64>(g, grid, s);
+    return g.d == 128 ? launch_attn_g<uint16_t, 128, SEL>(g, grid, s) : launch_attn_g<uint16_t, 64, SEL>(g, grid, s);
+  return g.d == 128 ? launch_attn_g<float, 128, SEL>(g, grid, s) : launch_attn_g<float, 64, SEL>(g, grid, s);
 }
 
 template <typename E, int MODE>
@@ -2558,6 +2739,11 @@ hipError_t launch_kv_append(const Geo& g, int pos0, int n_new, const void* k_new
   return hipGetLastError();
 }
 
+// Attention units per call up to which the FAC units select for themselves
+// (no final-selection launch): about one round of the selecting kernel's
+// resident workgroups, two per CU; larger steps repeat the selection in too
+// many units.
+constexpr long long kSelAttnMaxUnits = 512;
 // Streaming rows per call (over all (layer, sequence, group) items) from which
 // the streaming attention runs on the side stream.
 constexpr long long kSideStreamRows = 1LL << 20;
@@ -2614,6 +2800,12 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
     if (e != hipSuccess) return e;
     if ((e = hipEventRecord(ss.join, ss.side)) != hipSuccess) return e;
   }
+  // Small prefiltered steps (no side stream, T <= kShortMaxT, one index per
+  // KV group, device cache): the FAC units select for themselves, so the
+  // final-selection launch is saved.
+  const bool sel_attn = g.prefilter && !side && !g.clsa && g.kv_shift == 0 && !g.split && !g.select_only &&
+                        g.T <= kShortMaxT &&
+                        n_att_items * (long long)(g.nch_f + g.nch_s) <= kSelAttnMaxUnits;
   const int grid_tip = clampi(n_idx_items * g.nch_t, 1, g.grid);
   const int grid_item = clampi(n_idx_items, 1, g.grid);
   // per-query-head selection: a KV group's hg heads share the sampling and
@@ -2674,7 +2866,7 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
         e = g.bf16 ? launch_tip_v<uint16_t, 1>(g, grid_tip_pf, s) : launch_tip_v<float, 1>(g, grid_tip_pf, s);
     }
     if (e != hipSuccess) return e;
-    if (!g.fuse_sel) {
+    if (!g.fuse_sel && !sel_attn) {
       KTimer t("select_final", s);
       if (g.T <= kShortMaxT) {
         if (g.bf16) final_kernel<uint16_t, false><<<grid_item, kFinalThreads, 0, s>>>(g);
@@ -2734,7 +2926,7 @@ hipError_t launch_decode(const Geo& g0, const StreamSet& ss) {
       }
     } else {
       const long long units = n_att_items * (long long)(g.nch_f + (with_stream ? g.nch_s : 0));
-      e = launch_attn(g, clampi(units, 1, g.grid), s);
+      e = sel_attn ? launch_attn<true>(g, clampi(units, 1, g.grid), s) : launch_attn(g, clampi(units, 1, g.grid), s);
     }
   }
   if (e != hipSuccess) return e;

@@ -57,6 +57,34 @@ def test_c2_batch16_32k_all_items():
     _check_items(case, _all_items(cfg), "c2")
 
 
+def _launch_names(case):
+    """The library's timed launches of one decode call."""
+    H.timing_enable(True)
+    try:
+        H.timing_collect()
+        case.run()
+        return H.timing_collect()
+    finally:
+        H.timing_enable(False)
+
+
+def test_small_steps_select_in_attention_units():
+    """A prefiltered step of at most 512 attention units without the side
+    stream (one c1 layer) has no final-selection launch: each FAC unit finds
+    its item's cut itself; a larger one (c2, 3200 units) keeps the launch.
+    With n_fac 3500 the expected 5200 candidates exceed the 4096 a unit
+    holds in LDS, so the units' cut passes read them from global memory:
+    every item against the oracle."""
+    cfg = R.get_config("c1", n_fac=3500)
+    print(f"case selection in attention units {cfg}", flush=True)
+    case = U.DeviceCase(cfg)
+    names = _launch_names(case)
+    assert "select_final" not in names and {"sample", "tip_score", "attention_fac", "merge"} <= set(names), names
+    _check_items(case, _all_items(cfg), "c1 n_fac 3500")
+    big = U.DeviceCase(R.get_config("c2", n_layers=1, batch=16))
+    assert "select_final" in _launch_names(big)
+
+
 @pytest.mark.parametrize("over", [
     dict(ctx_len=5000, n_fac=777, window=300, n_sink=3),            # ragged chunks everywhere
     dict(ctx_len=3000, n_fac=3000, window=100),                     # every token selected
