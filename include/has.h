@@ -163,7 +163,9 @@ size_t sparse_decode_workspace(const has_decode_dims* dims);
 /* Which of the two exact selection paths ([FASA] §2.B.1 top-N_fac, the same
  * set either way) sparse_decode_step takes for these dims; host only, no HIP
  * call.  1: prefiltered (a sampled key threshold; TIP writes only the tokens
- * at or above it, the final kernel ranks them).  0: general (TIP writes every
+ * at or above it, and the final kernel ranks them, or on steps of at most 512
+ * attention units without the side stream the attention units themselves).
+ * 0: general (TIP writes every
  * score, an exact radix threshold follows).  -1: invalid dims, the reason in
  * has_last_error().  The prefiltered path needs 8192 <= ctx_len <= 524288
  * and its 16384 candidate slots to hold the expected candidates with room to
