@@ -1549,10 +1549,6 @@ __global__ __launch_bounds__(NT) void select_c_kernel(Geo g) {
 }
 
 // ------------------------------------------------------------------ attention
-// One unit = (attention item, chunk of <= kMaxChunkRows rows).  The group's G
-// query heads share every loaded row: lanes of a row (LPR of them, 16 bytes
-// each) form the dot products, then p = exp2(z - m) per head, then P.V.
-// Output: per head acc[d] = sum p v, m (log2 domain), l = sum p.
 // LDS of the selection inside an attention unit: the histogram (later the u16
 // prefix counts), the member list, a token bitmap of kShortMaxT bits and up
 // to kUnitSelCand candidates (more are read from global memory again).
@@ -1565,9 +1561,10 @@ constexpr int kUnitSelBytes = kUnitSelCandOfs + kUnitSelCand * 8;
 // as final_kernel, repeated by every unit of the item side by side instead
 // of one workgroup per item in a launch of its own -- and the cache
 // positions of the selected tokens of ascending rank r0 .. r0 + nrows - 1
-// into rows (LDS), with those idx_out entries (ox, or null).  Candidates are
-// read from global memory (the item's units share them through the L2):
-// they are counted in 2048 bins of (key - tau) >> sh, the members of the bin
+// into rows (LDS), with those idx_out entries (ox, or null).  The item's
+// units read its candidates through the L2, each staging up to kUnitSelCand
+// in LDS (more are read from global memory again for the cut) while counting
+// them in 2048 bins of (key - tau) >> sh; the members of the bin
 // holding the n_fac-th are ranked directly (at most kRankMax, below the
 // clamped top bin), else the general radix threshold; selected tokens are
 // marked in a token bitmap, whose words' exclusive prefix counts give each
@@ -1721,6 +1718,10 @@ __device__ void unit_select_rows(const Geo& g, int item, int r0, int nrows, int*
   }
 }
 
+// One unit = (attention item, chunk of <= kMaxChunkRows rows).  The group's G
+// query heads share every loaded row: lanes of a row (LPR of them, 16 bytes
+// each) form the dot products, then p = exp2(z - m) per head, then P.V.
+// Output: per head acc[d] = sum p v, m (log2 domain), l = sum p.
 // SEL: the prefiltered path's selection runs in the FAC units themselves
 // (unit_select_rows), with no final-selection launch before; its LDS shares
 // the space of the logits and row sums, which are used only after it.
