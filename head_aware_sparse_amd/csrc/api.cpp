@@ -96,6 +96,11 @@ has_status check_dims(const has_decode_dims* d, bool clsa, bool uses_stream = tr
       return fail(HAS_ERR_INVALID_ARG, "bad rope_layout");
   }
   if (d->kv_dtype != HAS_F32 && d->kv_dtype != HAS_BF16) return fail(HAS_ERR_INVALID_ARG, "bad kv_dtype");
+  // the scoring kernels hold a dominant-key row in at most 16 lanes of 16
+  // bytes: 2 n_dom channels of at most 256 bytes (always so for bf16)
+  if (uses_dom && 2 * d->n_dom * esize(d->kv_dtype) > 256)
+    return fail(HAS_ERR_UNSUPPORTED, "n_dom %d: 2 n_dom fp32 channels exceed the 256-byte dominant-key row (n_dom <= 32)",
+                d->n_dom);
   if ((long long)d->n_layers * d->n_kv_heads > has::kMaxPairs)
     return fail(HAS_ERR_UNSUPPORTED, "n_layers * n_kv_heads above %d", has::kMaxPairs);
   (void)clsa;

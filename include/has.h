@@ -105,7 +105,9 @@ has_status aoh_label(int n_layers, int n_q_heads, int n_kv_heads, int d_model, i
  * cache of ctx_len tokens at positions 0..ctx_len-1 (the current token
  * included); queries are for position ctx_len-1.
  *   n_q_heads % n_kv_heads == 0, G = n_q_heads / n_kv_heads in {1,2,4,8}
- *   d_head in {64, 128}; 1 <= n_dom <= d_head/2
+ *   d_head in {64, 128}; 1 <= n_dom <= d_head/2, and n_dom <= 32 for fp32
+ *   caches (the dominant-key row holds at most 256 bytes; else
+ *   HAS_ERR_UNSUPPORTED)
  *   1 <= n_fac <= ctx_len; n_sink >= 0, window >= 0, n_sink + window >= 1
  *   ctx_len <= 4194304; n_layers * n_kv_heads <= 8192
  */

@@ -50,6 +50,7 @@ def _decode(d, ws_bytes=1 << 40, **ptrs):
     (dict(n_sink=0, window=0), 1), (dict(window=-1), 1), (dict(n_dom=0), 1), (dict(n_dom=65), 1),
     (dict(kv_dtype=5), 1), (dict(rope_layout=3), 1), (dict(n_layers=2000, n_kv_heads=8, n_q_heads=8), 2),
     (dict(ctx_len=1 << 23, n_fac=10), 2), (dict(batch=0), 1),
+    (dict(kv_dtype=H.HAS_F32, n_dom=33), 2),  # fp32 dominant-key rows above 256 bytes
 ])
 def test_bad_dims_rejected(over, status):
     assert _decode(_dims(**over)) == status

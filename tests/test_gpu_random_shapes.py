@@ -1,0 +1,55 @@
+"""GPU parity of sparse_decode_step on seeded random shapes.
+
+Each case draws its layers, batch, group size, KV heads, head size, cache
+dtype, context length (8192..48000, so the prefiltered selection applies and
+most lengths are ragged), n_fac, dominant-chunk count (at most 32 for fp32
+caches, the library's limit), sink, window and the
+number of retrieval pairs, then compares four (layer, sequence, group) items
+with the fp64 oracle: index sets under the 1e-5 tie band, outputs within
+2e-3 + 1e-2 |ref|, -1 index rows for streaming groups."""
+import numpy as np
+import pytest
+
+from synth import recipe as R
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    bf16 = bool(rng.random() < 0.75)
+    T = int(rng.integers(8192, 48000))
+    L = int(rng.integers(1, 3))
+    sink = int(rng.integers(0, 8))
+    n_dom_max = d // 2 if bf16 else min(d // 2, 32)  # fp32: at most 256 bytes of dominant channels
+    cfg = R.get_config("c1", n_layers=L, batch=int(rng.integers(1, 4)), n_q_heads=G * hkv, n_kv_heads=hkv,
+                       d_head=d, ctx_len=T, n_fac=int(rng.integers(1, min(T, 6000))), n_sink=sink,
+                       window=int(rng.integers(0 if sink else 1, 3000)), n_dom=int(rng.integers(1, n_dom_max + 1)),
+                       kv_dtype="bf16" if bf16 else "f32", n_retrieval=int(rng.integers(0, L * hkv + 1)),
+                       d_model=max(256, G * hkv * d // 4))
+    return cfg, rng
+
+
+@pytest.mark.parametrize("seed", list(range(100, 124)))
+def test_random_shape(seed):
+    cfg, rng = _draw(seed)
+    print(f"case random seed {seed}: {cfg}", flush=True)
+    case = U.DeviceCase(cfg)
+    out, idx, _ = case.run()
+    L, B, hkv, G = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.group
+    items = [(int(rng.integers(0, L)), int(rng.integers(0, B)), int(rng.integers(0, hkv))) for _ in range(3)]
+    ret = [(l, g) for l in range(L) for g in range(hkv) if case.labels_np[l, g]]
+    if ret:
+        l, g = ret[int(rng.integers(0, len(ret)))]
+        items.append((l, int(rng.integers(0, B)), g))
+    for (l, b, g) in items:
+        ref, _, scores = U.oracle_item(cfg, case.hi, case.labels_np, l, b, g)
+        U.check_out(out[l, b, g * G:(g + 1) * G], ref, f"seed {seed} out l{l} b{b} g{g}")
+        if case.labels_np[l, g]:
+            U.check_index_set(idx[l, b, g], scores, cfg.n_fac, f"seed {seed} idx l{l} b{b} g{g}")
+        else:
+            assert (idx[l, b, g] == -1).all(), f"seed {seed} streaming idx l{l} b{b} g{g}"
