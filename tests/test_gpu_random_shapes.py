@@ -1,6 +1,7 @@
-"""GPU parity of sparse_decode_step on seeded random shapes.
+"""GPU parity on seeded random shapes: sparse_decode_step (prefiltered
+contexts, and short contexts on the general selection) and shared_index_decode.
 
-Each case draws its layers, batch, group size, KV heads, head size, cache
+Each prefiltered case draws its layers, batch, group size, KV heads, head size, cache
 dtype, context length (8192..48000, so the prefiltered selection applies and
 most lengths are ragged), n_fac, dominant-chunk count (at most 32 for fp32
 caches, the library's limit), sink, window and the
@@ -53,3 +54,59 @@ def test_random_shape(seed):
             U.check_index_set(idx[l, b, g], scores, cfg.n_fac, f"seed {seed} idx l{l} b{b} g{g}")
         else:
             assert (idx[l, b, g] == -1).all(), f"seed {seed} streaming idx l{l} b{b} g{g}"
+
+
+def _draw_kind(seed, kind):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    bf16 = bool(rng.random() < 0.7)
+    T = int(rng.integers(1, 8192)) if kind == "short" else int(rng.integers(2000, 60000))
+    sink = int(rng.integers(0, 8))
+    over = dict(n_q_heads=G * hkv, n_kv_heads=hkv, d_head=d, ctx_len=T, n_fac=int(rng.integers(1, min(T, 9000) + 1)),
+                n_sink=sink, window=int(rng.integers(0 if sink else 1, 3000)),
+                n_dom=int(rng.integers(1, (d // 2 if bf16 else min(d // 2, 32)) + 1)), kv_dtype="bf16" if bf16 else "f32")
+    return over, rng
+
+
+@pytest.mark.parametrize("seed", list(range(200, 208)))
+def test_random_shape_short_context(seed):
+    """Contexts below 8192 tokens: the general selection (every score
+    written, exact radix threshold)."""
+    over, rng = _draw_kind(seed, "short")
+    L, B = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    cfg = R.get_config("c1", n_layers=L, batch=B, n_retrieval=int(rng.integers(0, L * over["n_kv_heads"] + 1)),
+                       d_model=256, **over)
+    print(f"case random short seed {seed}: {cfg}", flush=True)
+    case = U.DeviceCase(cfg)
+    out, idx, _ = case.run()
+    G, hkv = cfg.group, cfg.n_kv_heads
+    for _ in range(4):
+        l, b, g = int(rng.integers(0, L)), int(rng.integers(0, B)), int(rng.integers(0, hkv))
+        ref, _, scores = U.oracle_item(cfg, case.hi, case.labels_np, l, b, g)
+        U.check_out(out[l, b, g * G:(g + 1) * G], ref, f"seed {seed} out l{l} b{b} g{g}")
+        if case.labels_np[l, g]:
+            U.check_index_set(idx[l, b, g], scores, cfg.n_fac, f"seed {seed} idx l{l} b{b} g{g}")
+        else:
+            assert (idx[l, b, g] == -1).all()
+
+
+@pytest.mark.parametrize("seed", list(range(300, 308)))
+def test_random_shape_shared_index(seed):
+    """The shared-index mode: 1..8 layers over one cache (at most 32 query
+    vectors per group), with or without per-layer labels."""
+    over, rng = _draw_kind(seed, "clsa")
+    G, hkv = over["n_q_heads"] // over["n_kv_heads"], over["n_kv_heads"]
+    N = int(rng.integers(1, min(8, 32 // G) + 1))
+    cfg = R.get_config("c3", n_layers=N, batch=int(rng.integers(1, 3)), **over)
+    lab = None if rng.random() < 0.5 else rng.integers(0, 2, size=(N, hkv)).astype(np.uint8)
+    print(f"case random shared-index seed {seed}: {cfg} labels {lab is not None}", flush=True)
+    case = U.DeviceCase(cfg)
+    out, idx, _ = U.run_clsa(case, labels=lab)
+    for _ in range(3):
+        b, g = int(rng.integers(0, cfg.batch)), int(rng.integers(0, hkv))
+        ref, _, scores = U.oracle_clsa_item(cfg, case.hi, b, g, labels=lab)
+        for n in range(N):
+            U.check_out(out[n, b, g * G:(g + 1) * G], ref[n], f"seed {seed} out n{n} b{b} g{g}")
+        U.check_index_set(idx[b, g], scores, cfg.n_fac, f"seed {seed} idx b{b} g{g}")
