@@ -9,15 +9,24 @@
 // + recent window); the CLSA article, "Cómo funciona CLSA" (one index reused
 // by every layer sharing the cache).
 //
-// Launch sequence (all on the caller's stream, no host synchronisation):
-//   plan      labels -> work lists; clears histograms and counters
-//   tip       scores s_t (fp32) + per-item histogram of the top 11 key bits
-//   select_bin per item: the first-digit bin that holds the n_fac-th score
-//   select_a  per chunk: count above that bin, collect the bin's candidates
-//   select_b  per item: exact threshold (key*, token*) by radix refinement
-//   select_c  per chunk: ordered compaction -> ascending token indices
-//   attn      per (item, chunk of rows): scores, softmax partial, P.V
-//   merge     log-sum-exp merge of the chunk partials -> out
+// Launch sequences (all on the caller's stream, no host synchronisation;
+// launch_decode picks one per call):
+//   prefiltered (8192 <= T <= 524288 and the expected candidates fit):
+//     plan      labels -> work lists, counters (inside the sampling launch
+//               when no side stream is used)
+//     [side stream: attn over streaming groups, when they attend to >= 2^20 rows]
+//     sample    TIP keys of 4096 evenly spread tokens per item
+//     tau       per item: the candidate threshold (inside TIP on smaller steps)
+//     tip       scores; only tokens at or above tau are written as candidates
+//     final     per item: the exact top-n_fac cut among the candidates,
+//               ascending indices (inside the FAC units on small steps, and
+//               inside the shared-index attention units)
+//     attn      per (item, chunk of rows): logits, softmax partial, P.V
+//     merge     log-sum-exp merge of the chunk partials -> out
+//   general (other lengths, or too many expected candidates): plan, tip
+//     (every score + a first-digit histogram), select_bin, select_a,
+//     select_b, select_c (exact radix threshold, ordered compaction), attn,
+//     merge.
 // Work is split into units (item x chunk) processed by a persistent grid;
 // unit counts depend on the labels and are read from device memory.
 #include "internal.h"
