@@ -188,3 +188,25 @@ def test_c4_32_layers_bf16():
     got = (erh.cpu().numpy(), erg.cpu().numpy(), lab.cpu().numpy())
     _check(got, (r_erh, r_erg, r_lab), cfg.n_retrieval)
     assert (got[2] == R.planted_labels(cfg)).all()
+
+
+@pytest.mark.parametrize("seed", list(range(500, 510)))
+def test_random_shapes(seed):
+    """Seeded random shapes: 1-8 layers, group sizes 1-8, 1-8 KV heads, d_head
+    64 or 128, d_model from d_head (square, ill-conditioned Gram matrices) to
+    2048, bf16 or fp32 weights, any number of planted heads, the top-k or the
+    threshold rule."""
+    rng = np.random.default_rng(seed)
+    G, hkv, d = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 4, 8])), int(rng.choice([64, 128]))
+    L = int(rng.integers(1, 9))
+    dm = int(rng.choice([d, max(d, 128), int(rng.integers(max(d, 128) // 64, 33)) * 64]))
+    cfg = R.get_config("c1", n_layers=L, n_q_heads=G * hkv, n_kv_heads=hkv, d_head=d, d_model=dm,
+                       kv_dtype="bf16" if rng.random() < 0.6 else "f32", n_retrieval=int(rng.integers(0, L * hkv + 1)))
+    print(f"case label random seed {seed}: {cfg}", flush=True)
+    if rng.random() < 0.3:
+        got, ref = _run(cfg, threshold=float(rng.uniform(5, 60)))
+        _check(got, ref, None)
+    else:
+        k = int(rng.integers(0, L * hkv + 1))
+        got, ref = _run(cfg, k=k)
+        _check(got, ref, k)
