@@ -1,7 +1,8 @@
 """Graph capture: a decode step captured into a HIP graph (through torch's
 graph API, on the caller's capturing stream) replays to exactly the eager
 results, several times, with eager work and synchronisations between the
-replays.  Covered: a small step (one stream), a step that forks the
+replays.  Covered: a small step (one stream), one whose attention units
+select for themselves, a step that forks the
 streaming attention onto the library's side stream and joins it back, and
 the shared-index step.  The library records no memset or copy on the
 stream, so everything it enqueues is kernels and event waits."""
@@ -66,6 +67,14 @@ def _decode_case(case):
 def test_small_step_graph_replays():
     cfg = R.get_config("c1", ctx_len=20000, batch=2, n_layers=2)
     print("case graph small step", flush=True)
+    _decode_case(U.DeviceCase(cfg))
+
+
+def test_selecting_attention_step_graph_replays():
+    # one layer, batch 1: 200 attention units, so the FAC units find their
+    # item's cut themselves (no final-selection launch)
+    cfg = R.get_config("c1", ctx_len=20000, batch=1, n_layers=1)
+    print("case graph selecting attention units", flush=True)
     _decode_case(U.DeviceCase(cfg))
 
 
