@@ -228,6 +228,11 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the full-attention comparison")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-label", action="store_true")
+    ap.add_argument("--labels-out", default=None,
+                    help="save the headline config's labeller outputs (labels, ERs, I_dom) to this .npz")
+    ap.add_argument("--labels-in", default=None,
+                    help="take the headline config's labels from this .npz (written by --labels-out) "
+                         "instead of running the labeller")
     ap.add_argument("--cpu-sample", default="24,72", help="retrieval,streaming items timed on the CPU")
     ap.add_argument("--cpu-reps", type=int, default=4, help="oracle calls timed per sampled item")
     ap.add_argument("--extra-configs", default="c3,c2,c1",
@@ -332,7 +337,14 @@ def run_config(args, cfg_name, headline=True):
     # labels: the offline AoH labeller on the model weights (timed separately)
     label_info = None
     labels_np = hi.labels
-    if cfg.d_model and not args.no_label:
+    if headline and args.labels_in:
+        rec = H.load_labels(args.labels_in, cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.n_dom)
+        if not np.array_equal(rec["i_dom"], hi.i_dom):
+            raise SystemExit(f"{args.labels_in}: its I_dom is not this workload's (the cache is packed with the seeded one)")
+        labels_np = rec["labels"]
+        label_info = {"loaded_from": args.labels_in, "n_retrieval": int(labels_np.sum())}
+        log(f"labels loaded from {args.labels_in}")
+    elif cfg.d_model and not args.no_label:
         wq = sdev.to_device(hi.w_q, "cuda", cfg.bf16)
         wk = sdev.to_device(hi.w_k, "cuda", cfg.bf16)
         lab_d = torch.empty((cfg.n_layers, cfg.n_kv_heads), dtype=torch.uint8, device="cuda")
@@ -365,6 +377,9 @@ def run_config(args, cfg_name, headline=True):
             "labels_match_planted": bool((labels_np == hi.labels).all()),
             "n_retrieval": int(labels_np.sum()),
         }
+        if headline and args.labels_out:
+            H.save_labels(args.labels_out, labels_np, erh, erg, hi.i_dom)
+            label_info["saved_to"] = args.labels_out
         del wq, wk
         log(f"labeller {label_info}")
     labels = torch.from_numpy(np.ascontiguousarray(labels_np)).cuda()

@@ -35,3 +35,4 @@ from .binding import (  # noqa: F401
     timing_collect,
     timing_enable,
 )
+from .labels_io import load_labels, save_labels  # noqa: F401,E402
