@@ -275,6 +275,11 @@ def main():
                 "step_hbm_GBps", "step_hbm_frac", "tokens_scored_per_s", "kernels_ms", "replicas",
                 "dense_attention", "cpu_baseline") if k in r}
             log(f"{name}: {r['ms_per_step']:.4f} ms/step, {r['step_hbm_frac']:.3f} of peak")
+    # provenance: the library sources this run's libhas.so was built from
+    # (the kernel sources also key the counter records under profiles/)
+    res["source_sha256"] = {
+        f: hashlib.sha256(open(os.path.join(ROOT, "head_aware_sparse_amd", "csrc", f), "rb").read()).hexdigest()[:16]
+        for f in ("decode.hip", "label.hip", "api.cpp")}
     print(json.dumps(res), flush=True)
 
 
